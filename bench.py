@@ -1,0 +1,298 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+A step is one serving step over a shared paged KV cache, the workload that
+touches every stage of the path: the fused RoPE + paged cache write for all
+new tokens, chunked prefill of 8 requests (512 new tokens each on 0-2048
+cached tokens) and decode of 128 sequences (context log-uniform in
+[16, 32768]) with its merge pass; 12 query / 2 kv heads, head_dim 128,
+bf16, 16-token blocks, RoPE base 10000, pool pre-fragmented (seed 1004).
+Inputs are synthetic and already resident in HBM when timing starts.
+
+value = percent of the step's serial roofline time reached:
+    100 * (F / 2.5 PFLOP/s + B / 8 TB/s) / measured step time
+with F the chunked-prefill flops (4 * D per unmasked query-key pair) and B the
+write and decode algorithmic bytes.  The line also carries the roofline of
+the dominant kernel (the paged decode), the oracle timed on the host cores
+and the per-stage figures, plus the contiguous long prefill (T 16384) and the
+uniform-context decode (64 sequences, U[128, 4096]) measured on their own.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attention TFLOP/s + paged-decode KV GB/s on 1 MI355X (% of roofline)"
+PEAK_BF16_FLOPS = 2.5e15
+PEAK_HBM = 8.0e12
+HQ, HKV, D, BS = 12, 2, 128, 16
+ELT = 2  # bf16 bytes
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+
+def prefill_pairs_causal(cached, new):
+    """Unmasked (query, key) pairs of a chunk of `new` rows on `cached` keys."""
+    return int(new) * int(cached) + int(new) * (int(new) + 1) // 2
+
+
+def chunk_flops(case):
+    pairs = sum(prefill_pairs_causal(c, case.chunk) for c in case.cached)
+    return 4 * D * HQ * pairs
+
+
+def decode_bytes(lengths, num_blocks_used=None):
+    """K and V read once per kv head, plus q, o, the used block-table entries
+    and the context lengths."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    kv = int(lengths.sum()) * HKV * D * ELT * 2
+    qo = len(lengths) * HQ * D * ELT * 2
+    bt = int(((lengths + BS - 1) // BS).sum()) * 4
+    return kv + qo + bt + len(lengths) * 4
+
+
+def write_bytes(n_tokens):
+    """q read + written, k and v read, rotated k and v written, positions and
+    slots read."""
+    return n_tokens * (HQ * D * ELT * 2 + HKV * D * ELT * 2 * 2 + 8)
+
+
+# ----------------------------------------------------------------------------- timing helpers
+
+class EventTimer:
+    """Accumulates GPU time between event pairs on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def stop(self, e0):
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e1.record()
+        self.pairs.append((e0, e1))
+
+    def mean_ms(self):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--only", choices=["mixed", "prefill", "decode"], default=None,
+                    help="run one workload only (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(multi-GPU sharding is a design note, not implemented)"}))
+        sys.exit(2)
+
+    import torch
+    import transformer_attention_05_amd as mi
+    from transformer_attention_05_amd.step import MixedStep
+    from workloads import assign_blocks, build_decode_pool, decode_case, mixed_case, prefill_case, scatter_to_pool
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    mi.load()
+    dev = "cuda"
+    out = {}
+
+    # ------------------------------------------------------------------ the step (mixed)
+    if args.only in (None, "mixed"):
+        log("bench: building the mixed step (seed 1004)")
+        case = mixed_case(1004)
+        step = MixedStep(case, assign_blocks, dev, scatter=scatter_to_pool)
+        n_new = case.q_new.shape[0]
+        F = chunk_flops(case)
+        B_dec = decode_bytes(case.dec_lengths)
+        B_wr = write_bytes(n_new)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            step.run()
+        torch.cuda.synchronize()
+        t_wr, t_pre, t_dec = EventTimer(torch), EventTimer(torch), EventTimer(torch)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            e = t_wr.start(); step.write(); t_wr.stop(e)
+            e = t_pre.start(); step.prefill(); t_pre.stop(e)
+            e = t_dec.start(); step.decode(); t_dec.stop(e)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / args.steps
+        ms_wr, ms_pre, ms_dec = t_wr.mean_ms(), t_pre.mean_ms(), t_dec.mean_ms()
+        t_roof = F / PEAK_BF16_FLOPS + (B_dec + B_wr) / PEAK_HBM
+        out["mixed"] = dict(wall_s=wall, ms_write=ms_wr, ms_prefill=ms_pre, ms_decode=ms_dec, F=F, B_dec=B_dec,
+                            B_wr=B_wr, t_roof=t_roof, n_new=n_new, part=mi.attn_decode_paged_auto_partition(
+                                len(case.dec_lengths), HKV, int(case.dec_lengths.max())),
+                            dec_tokens=int(case.dec_lengths.sum()), pool_blocks=case.num_blocks)
+        log(f"bench: mixed step wall {wall * 1e3:.3f} ms | write {ms_wr:.3f} prefill {ms_pre:.3f} "
+            f"decode {ms_dec:.3f} ms")
+        del step
+
+    # ------------------------------------------------------------------ contiguous long prefill
+    if not args.no_components and args.only in (None, "prefill"):
+        log("bench: contiguous prefill T 16384")
+        q, k, v = prefill_case(1003, 1, 16384, HQ, HKV, D, torch.bfloat16)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        o = torch.empty_like(qd)
+        for _ in range(max(2, args.warmup)):
+            mi.attn_prefill(qd, kd, vd, o=o)
+        torch.cuda.synchronize()
+        tp = EventTimer(torch)
+        for _ in range(max(5, args.steps // 2)):
+            e = tp.start(); mi.attn_prefill(qd, kd, vd, o=o); tp.stop(e)
+        torch.cuda.synchronize()
+        fl = 4 * D * HQ * 16384 * 16385 // 2
+        out["prefill_c4"] = dict(ms=tp.mean_ms(), flops=fl)
+        log(f"bench: prefill C4 {tp.mean_ms():.3f} ms  {fl / tp.mean_ms() / 1e9:.1f} TFLOP/s")
+        del qd, kd, vd, o
+
+    # ------------------------------------------------------------------ uniform decode
+    if not args.no_components and args.only in (None, "decode"):
+        log("bench: decode 64 seqs ctx U[128, 4096] (3 rotating pool copies)")
+        dc = decode_case(1002, 64, 128, 4096)
+        pools = [build_decode_pool(dc, dev) for _ in range(3)]
+        qd = dc.q.to(dev)
+        bt = torch.from_numpy(dc.block_tables).to(dev)
+        cl = torch.from_numpy(dc.lengths.astype(np.int32)).to(dev)
+        mx = int(dc.lengths.max())
+        ws = torch.empty(max(256, mi.attn_decode_paged_workspace_size(64, HQ, HKV, D, mx)), dtype=torch.uint8,
+                         device=dev)
+        o = torch.empty_like(qd)
+        for i in range(max(3, args.warmup)):
+            mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws)
+        torch.cuda.synchronize()
+        td = EventTimer(torch)
+        n = max(9, args.steps)
+        for i in range(n):
+            e = td.start(); mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws); td.stop(e)
+        torch.cuda.synchronize()
+        by = decode_bytes(dc.lengths)
+        out["decode_c3"] = dict(ms=td.mean_ms(), bytes=by, part=mi.attn_decode_paged_auto_partition(64, HKV, mx))
+        log(f"bench: decode C3 {td.mean_ms() * 1e3:.1f} us  {by / td.mean_ms() / 1e6:.0f} GB/s")
+        del pools
+
+    # ------------------------------------------------------------------ CPU baseline (oracle)
+    cpu = None
+    if not args.no_cpu_baseline and "mixed" in out:
+        cpu = cpu_baseline(case, out["mixed"])
+
+    emit(args, out, cpu)
+
+
+def cpu_baseline(case, m):
+    """The oracle on the whole mixed step (a few seconds of host work)."""
+    import oracle
+    from workloads import to_f64
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:
+        threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+        threadpool_limits(threads)
+        blas = [f"{i.get('internal_api')}:{i.get('num_threads')}" for i in threadpool_info()]
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        blas, used = [], threads
+    log(f"bench: oracle on the host ({threads} cores visible, BLAS {blas})")
+    t0 = time.perf_counter()
+    pos = case.positions
+    q_rot = oracle.round_bf16(oracle.rope(to_f64(case.q_new), pos, case.rope_base))
+    k_rot = oracle.round_bf16(oracle.rope(to_f64(case.k_new), pos, case.rope_base))
+    v_new = to_f64(case.v_new)
+    R, C = len(case.cached), case.chunk
+    qs, ks, vs = [], [], []
+    for r in range(R):
+        sl = slice(r * C, (r + 1) * C)
+        qs.append(q_rot[sl])
+        ks.append(np.concatenate([to_f64(case.k_old[r]), k_rot[sl]]))
+        vs.append(np.concatenate([to_f64(case.v_old[r]), v_new[sl]]))
+    oracle.chunked_prefill(qs, ks, vs)
+    dk, dv = [], []
+    for s in range(len(case.dec_lengths)):
+        n = R * C + s
+        dk.append(np.concatenate([to_f64(case.k_old[R + s]), k_rot[n:n + 1]]))
+        dv.append(np.concatenate([to_f64(case.v_old[R + s]), v_new[n:n + 1]]))
+    oracle.decode(q_rot[R * C:], dk, dv)
+    t = time.perf_counter() - t0
+    return dict(value=round(100.0 * m["t_roof"] / t, 6), unit="% of roofline", cores=int(used),
+                kind="oracle", seconds_per_step=round(t, 3),
+                sample="the whole mixed step (RoPE on all 4224 new tokens, 8 chunked prefills, 128 decodes), "
+                       "fp64 NumPy, once")
+
+
+def emit(args, out, cpu):
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    comps = {}
+    if "mixed" in out:
+        m = out["mixed"]
+        step_s = m["wall_s"]
+        res["value"] = round(100.0 * m["t_roof"] / step_s, 3)
+        res["unit"] = "% of roofline"
+        res["ms_per_step"] = round(step_s * 1e3, 4)
+        res["config"] = {"workload": "mixed serving step: fused RoPE+paged KV write (4224 tokens), chunked "
+                                     "prefill 8x512 new on 0-2048 cached, decode 128 seqs ctx log-U[16,32768]; "
+                                     "Hq 12 / Hkv 2, D 128, bf16, block 16, fragmented pool, seed 1004",
+                         "new_tokens": m["n_new"], "decode_context_tokens": m["dec_tokens"],
+                         "pool_blocks": m["pool_blocks"], "decode_partition": m["part"],
+                         "parallelism": "single GPU"}
+        dec_s = m["ms_decode"] / 1e3
+        gbps = m["B_dec"] / dec_s / 1e9
+        res["roofline"] = {"kernel": "paged decode (decode_partition_kernel + decode_merge_kernel)",
+                           "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                           "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": None,
+                           "algorithmic_bytes_per_launch": m["B_dec"], "avg_launch_us": round(m["ms_decode"] * 1e3, 2)}
+        comps["step_write"] = {"us": round(m["ms_write"] * 1e3, 2), "GB/s": round(m["B_wr"] / (m["ms_write"] / 1e3) / 1e9, 1)}
+        comps["step_chunked_prefill"] = {"us": round(m["ms_prefill"] * 1e3, 2),
+                                         "TFLOP/s": round(m["F"] / (m["ms_prefill"] / 1e3) / 1e12, 1),
+                                         "frac_of_bf16_peak": round(m["F"] / (m["ms_prefill"] / 1e3) / PEAK_BF16_FLOPS, 4)}
+        comps["step_decode"] = {"us": round(m["ms_decode"] * 1e3, 2), "GB/s": round(gbps, 1),
+                                "frac_of_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4)}
+        comps["step_roofline_us"] = round(m["t_roof"] * 1e6, 2)
+    if "prefill_c4" in out:
+        p = out["prefill_c4"]
+        tf = p["flops"] / (p["ms"] / 1e3) / 1e12
+        comps["prefill_T16384"] = {"us": round(p["ms"] * 1e3, 1), "TFLOP/s": round(tf, 1),
+                                   "frac_of_bf16_peak": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)}
+    if "decode_c3" in out:
+        d = out["decode_c3"]
+        gb = d["bytes"] / (d["ms"] / 1e3) / 1e9
+        comps["decode_64seq_U128_4096"] = {"us": round(d["ms"] * 1e3, 2), "GB/s": round(gb, 1),
+                                           "frac_of_hbm_peak": round(gb * 1e9 / PEAK_HBM, 4), "partition": d["part"]}
+    res["components"] = comps
+    if "value" not in res:
+        res["value"] = None
+        res["unit"] = "% of roofline"
+        res["ms_per_step"] = None
+        res["config"] = {"workload": f"partial run ({args.only})"}
+    res["cpu_baseline"] = cpu
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

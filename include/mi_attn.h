@@ -1,0 +1,224 @@
+/*
+ * mi_attn.h -- C ABI of an MI355X (gfx950) attention library: exact
+ * scaled-dot-product attention computed FlashAttention-style, a paged-KV
+ * decode with split-KV partitions and a merge pass, a fused RoPE + paged
+ * KV-cache write, and the host-side block pool that hands out cache blocks.
+ *
+ * Source of the operations: the tutorial "Fast Attention Kernels and
+ * Operator Fusion" (Machine Learning Mastery).  Section names below refer to
+ * it.
+ *
+ * General conventions
+ *   - Every pointer named *device* is device memory owned by the caller; the
+ *     library never allocates, frees or keeps device memory.  Pool functions
+ *     take host memory only.
+ *   - Every launch function validates all arguments first.  On any error it
+ *     returns a negative attn_status, records a message for attn_last_error()
+ *     and makes no HIP call at all: nothing is launched or changed.
+ *   - Launch functions enqueue on `stream` (NULL = the default stream) and
+ *     return without synchronising.  They do not allocate and do not read
+ *     device memory on the host, so a caller may capture them in a HIP graph
+ *     (replay needs the same addresses and shapes).
+ *   - Tensors are token-major with the head dimension contiguous.  Strides
+ *     are in elements.  Device pointers must be 16-byte aligned and every
+ *     stride a multiple of 8 elements (bf16) or 4 elements (f32).
+ *   - Supported: head_dim 64 or 128; dtype F32 or BF16 (paged kernels: BF16);
+ *     block_size 16; num_q_heads a multiple of num_kv_heads.  Anything else
+ *     returns ATTN_E_UNSUPPORTED.
+ *   - Paged cache layout (one pool per tensor):
+ *       k_cache [num_blocks][num_kv_heads][16][head_dim]   (token-major)
+ *       v_cache [num_blocks][num_kv_heads][head_dim][16]   (token-minor)
+ *     Storing a value block token-minor lets the PV contraction read 4 or 8
+ *     consecutive tokens of one channel with one load.
+ */
+#ifndef MI_ATTN_H
+#define MI_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define ATTN_API __attribute__((visibility("default")))
+#else
+#define ATTN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* attn_stream_t; /* same handle as hipStream_t */
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_E_INVALID = -1,     /* null pointer, bad size, misaligned pointer or stride */
+  ATTN_E_UNSUPPORTED = -2, /* valid in principle, not supported by these kernels */
+  ATTN_E_NOMEM = -3,       /* pool exhausted or workspace too small */
+  ATTN_E_STATE = -4,       /* double free, refcount misuse */
+  ATTN_E_DEVICE = -5       /* a HIP call failed */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Text of the last error on the calling thread ("" if none).  Valid until
+ * that thread's next call into the library. */
+ATTN_API const char* attn_last_error(void);
+
+/* -------------------------------------------------------------------------
+ * attn_prefill -- contiguous attention  O = softmax(Q K^T * scale + M) V.
+ *
+ * Defined by the attention equation of §FlashAttention-Style Kernels (an
+ * additive mask M; d is the head dimension) and computed the way the same
+ * section describes FlashAttention: per tile of queries, score blocks are
+ * formed against tiles of keys, the running softmax statistics (row max and
+ * row sum) are updated and the output is accumulated on chip; the Tq x Tk
+ * score matrix never reaches device memory.
+ *
+ *   q   device [batch][seqlen_q][num_q_heads][head_dim]   (strides q_strides)
+ *   k,v device [batch][seqlen_k][num_kv_heads][head_dim]  (k_strides, v_strides)
+ *   o   device, same shape as q, written                  (o_strides)
+ *   lse device float [batch][num_q_heads][seqlen_q], written if non-NULL:
+ *       natural-log sum of exp of the scaled, masked scores of each row.
+ *   *_strides[3]: element strides of the batch, token and head dimensions.
+ *   Query head h reads key/value head h / (num_q_heads / num_kv_heads).
+ *   scale: 0 means 1/sqrt(head_dim).
+ *   causal: non-zero masks key j for query i unless j <= i + seqlen_k - seqlen_q
+ *     (bottom-right aligned); requires seqlen_k >= seqlen_q.
+ *   A query row that sees no key (only possible when seqlen_k == 0) gets O = 0.
+ *   q, k, v, o must not overlap o.
+ * ---------------------------------------------------------------------- */
+ATTN_API int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                 int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                 const int64_t q_strides[3], const int64_t k_strides[3],
+                 const int64_t v_strides[3], const int64_t o_strides[3],
+                 float scale, int32_t causal, attn_dtype dtype, attn_stream_t stream);
+
+/* -------------------------------------------------------------------------
+ * attn_prefill_paged -- prefill of new query chunks over a paged KV cache.
+ *
+ * The same computation as attn_prefill, with keys and values read through
+ * a block table as §Paged Attention Kernels describes: logical token t of
+ * sequence s lives in physical block block_table[s][t / 16] at offset t % 16;
+ * K[t+1] is not assumed to follow K[t].
+ *
+ *   q            device bf16 [total_q][num_q_heads][head_dim], sequences packed
+ *   k_cache,
+ *   v_cache      device bf16 paged pools (layout in the header comment)
+ *   block_table  device int32 [num_seqs][max_blocks_per_seq]; entries past a
+ *                sequence's last block are never read
+ *   cu_seqlens_q device int32 [num_seqs + 1]; sequence s owns q rows
+ *                cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 (at most max_seqlen_q)
+ *   context_lens device int32 [num_seqs]; keys of sequence s, the new tokens
+ *                included (they must already be in the cache); must be >= the
+ *                sequence's query count
+ *   o            device bf16, same shape as q, written
+ *   Chunk row i of sequence s sits at position context_lens[s] - n_s + i and,
+ *   when causal, sees keys 0 .. that position.
+ * ---------------------------------------------------------------------- */
+ATTN_API int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                       void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks,
+                       float scale, int32_t causal, attn_dtype dtype, attn_stream_t stream);
+
+/* -------------------------------------------------------------------------
+ * attn_decode_paged -- one query token per sequence over its paged cache.
+ *
+ * §FlashAttention-Style Kernels: decode has one new query per request and is
+ * dominated by reading the growing KV cache; §Paged Attention Kernels: the
+ * kernel follows the block table.  Each sequence's context is cut into
+ * partitions of `partition_size` tokens.  One pass computes, per partition,
+ * the partition's running max m, sum l and unnormalised output; a merge pass
+ * combines the partitions exactly (each rescaled by exp(m_p - max_p m_p)).
+ * A sequence with one partition is finished by the first pass.
+ *
+ *   q            device bf16 [num_seqs][num_q_heads][head_dim]
+ *   block_table  device int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens device int32 [num_seqs], 1 .. max_context_len (the new
+ *                token included)
+ *   o            device bf16 [num_seqs][num_q_heads][head_dim], written
+ *   partition_size: 0 = automatic, else a multiple of 128.
+ *   workspace    device scratch of at least
+ *                attn_decode_paged_workspace_size(...) bytes (same arguments)
+ * ---------------------------------------------------------------------- */
+ATTN_API size_t attn_decode_paged_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_context_len,
+                                        int32_t partition_size);
+ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* context_lens, void* o,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                      int32_t max_blocks_per_seq, int32_t max_context_len,
+                      int32_t partition_size, float scale, attn_dtype dtype,
+                      void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+/* Partition size that attn_decode_paged uses when partition_size is 0. */
+ATTN_API int32_t attn_decode_paged_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                         int32_t max_context_len);
+
+/* -------------------------------------------------------------------------
+ * attn_kv_cache_write_rope -- fused rotary embedding + paged cache write.
+ *
+ * §Operator Fusion lists two fusions this kernel performs in one pass:
+ * applying rotary position embeddings to queries and keys, and updating the
+ * KV cache while transforming keys and values.  For token n with position
+ * positions[n]: each pair (x[i], x[i + D/2]), i < D/2, of every query and key
+ * head is rotated by angle positions[n] * rope_base^(-2i/D) (angle and its
+ * sine and cosine in double precision); the rotated key and the unchanged
+ * value are stored in slot slot_mapping[n] (block slot / 16, offset slot % 16);
+ * slot -1 skips the cache write for that token.  Rotated queries overwrite q.
+ *
+ *   q            device [num_tokens][num_q_heads][head_dim], may be NULL
+ *   k, v         device [num_tokens][num_kv_heads][head_dim]
+ *   positions    device int32 [num_tokens], >= 0
+ *   slot_mapping device int32 [num_tokens], -1 or 0 .. num_blocks*16-1
+ *   rope_base    0 = no rotation (plain copy)
+ *   dtype        BF16 or F32 (q, k, v and the caches share it)
+ * ---------------------------------------------------------------------- */
+ATTN_API int attn_kv_cache_write_rope(void* q, const void* k, const void* v, const int32_t* positions,
+                             const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                             int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             float rope_base, attn_dtype dtype, attn_stream_t stream);
+
+/* -------------------------------------------------------------------------
+ * Block pool (host only).  §Paged Attention Kernels: fixed-size blocks are
+ * allocated on demand, returned to a pool when a request ends and may be
+ * shared by sequences with a common prefix; a block table maps a sequence's
+ * logical blocks to physical ones.  The pool is a LIFO free list with a
+ * reference count per block.  Not thread-safe: callers serialise access.
+ * ---------------------------------------------------------------------- */
+typedef struct attn_pool attn_pool;
+
+/* num_blocks >= 1, block_size >= 1.  Fresh pools hand out ids 0, 1, 2, ... */
+ATTN_API int attn_pool_create(int32_t num_blocks, int32_t block_size, attn_pool** out);
+ATTN_API void attn_pool_destroy(attn_pool* pool);
+/* Take n blocks (refcount 1) into out_ids[n].  All or nothing: NOMEM leaves
+ * the pool unchanged. */
+ATTN_API int attn_pool_alloc(attn_pool* pool, int32_t n, int32_t* out_ids);
+/* Drop one reference of each id; a block whose count reaches 0 returns to the
+ * free list (pushed in argument order).  Every id is checked first
+ * (range, and enough references for repeated ids): on error nothing changes. */
+ATTN_API int attn_pool_free(attn_pool* pool, const int32_t* ids, int32_t n);
+/* Add one reference to each (allocated) id, for prefix sharing. */
+ATTN_API int attn_pool_retain(attn_pool* pool, const int32_t* ids, int32_t n);
+ATTN_API int32_t attn_pool_num_free(const attn_pool* pool);
+ATTN_API int32_t attn_pool_num_blocks(const attn_pool* pool);
+/* Reference count of id (0 = free), or ATTN_E_INVALID. */
+ATTN_API int attn_pool_refcount(const attn_pool* pool, int32_t id);
+
+/* Grow a sequence from cur_len to cur_len + n_new tokens.  Blocks the new
+ * length needs beyond ceil(cur_len / block_size) are allocated (all or
+ * nothing) and appended to block_table_row (host, max_blocks entries); the
+ * slot of each new token, block_table_row[t / bs] * bs + t % bs, is written to
+ * slot_mapping_out[n_new] (may be NULL). */
+ATTN_API int attn_seq_reserve(attn_pool* pool, int32_t* block_table_row, int32_t max_blocks,
+                     int32_t cur_len, int32_t n_new, int32_t* slot_mapping_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MI_ATTN_H */

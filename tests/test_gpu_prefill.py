@@ -1,0 +1,154 @@
+"""Parity of the contiguous prefill kernel (attn_prefill) with the fp64
+oracle, on the same seeded host inputs."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_05_amd as mi
+from tests.gpu_util import DEV, check, f64, say
+from workloads import prefill_case, rng, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def run(q, k, v, causal=True, want_lse=False, scale=0.0):
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=DEV) if want_lse else None
+    o = mi.attn_prefill(qd, kd, vd, lse=lse, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return (o.cpu(), lse.cpu() if want_lse else None)
+
+
+def test_c1_single_head_f32():
+    """Single head, T 64, D 64, fp32, causal, scale 1/8 (seed 1000)."""
+    say("case: C1 f32 T64 D64")
+    q, k, v = prefill_case(1000, 1, 64, 1, 1, 64, torch.float32)
+    o, lse = run(q, k, v, want_lse=True)
+    ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=True, scale=0.125)
+    check(f64(o), ref, torch.float32, "C1 O")
+    np.testing.assert_allclose(f64(lse), ref_lse, rtol=0, atol=1e-5)
+
+
+def test_c2_qwen_shape_bf16():
+    """T 2048, 12 query / 2 kv heads, D 128, bf16, causal (seed 1001)."""
+    say("case: C2 bf16 T2048 Hq12 Hkv2 D128")
+    q, k, v = prefill_case(1001, 1, 2048, 12, 2, 128, torch.bfloat16)
+    o, lse = run(q, k, v, want_lse=True)
+    ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=True)
+    check(f64(o), ref, torch.bfloat16, "C2 O")
+    np.testing.assert_allclose(f64(lse), ref_lse, rtol=0, atol=1e-3)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_tutorial_sdpa_shape(dtype):
+    """(B, H, T, D) = (2, 16, 512, 64), causal: the tutorial's SDPA example,
+    passed in its own head-major layout through strides."""
+    say(f"case: tutorial shape {dtype}")
+    g = rng(7)
+    shape = (2, 16, 512, 64)   # (B, H, T, D)
+    q, k, v = (torch.from_numpy(g.standard_normal(shape, dtype=np.float32)).to(dtype) for _ in range(3))
+    qd, kd, vd = (t.to(DEV).transpose(1, 2) for t in (q, k, v))   # [B, T, H, D] views
+    o = mi.attn_prefill(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.attention(to_f64(q.transpose(1, 2)), to_f64(k.transpose(1, 2)), to_f64(v.transpose(1, 2)))
+    check(f64(o), ref, dtype, "tutorial")
+
+
+CASES = [
+    # (tq, tk, hq, hkv, d, causal)
+    (1, 1, 1, 1, 64, True),
+    (15, 15, 2, 1, 64, True),
+    (16, 16, 6, 1, 128, True),
+    (17, 17, 12, 2, 128, True),
+    (63, 63, 4, 2, 64, True),
+    (65, 65, 6, 6, 128, True),
+    (127, 127, 12, 2, 128, True),
+    (129, 129, 12, 2, 128, True),
+    (300, 300, 2, 2, 64, False),
+    (1000, 1000, 12, 2, 128, True),
+    (37, 101, 12, 2, 128, True),     # bottom-right causal, tq < tk
+    (130, 400, 6, 3, 64, True),
+    (200, 77, 4, 1, 128, False),     # tk < tq, non-causal
+]
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("case", CASES, ids=[f"tq{c[0]}_tk{c[1]}_h{c[2]}x{c[3]}_d{c[4]}_{'c' if c[5] else 'nc'}" for c in CASES])
+def test_ragged_shapes(case, dtype):
+    tq, tk, hq, hkv, d, causal = case
+    say(f"case: ragged {case} {dtype}")
+    q, k, v = prefill_case(2000 + CASES.index(case), 2, tq, hq, hkv, d, dtype, seqlen_k=tk)
+    o, lse = run(q, k, v, causal=causal, want_lse=True)
+    ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=causal)
+    check(f64(o), ref, dtype, f"ragged {case}")
+    np.testing.assert_allclose(f64(lse), ref_lse, rtol=0, atol=1e-3 if dtype == torch.bfloat16 else 1e-5)
+
+
+def test_explicit_scale():
+    q, k, v = prefill_case(3, 1, 100, 4, 2, 64, torch.float32)
+    o, _ = run(q, k, v, scale=0.3)
+    ref, _ = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=True, scale=0.3)
+    check(f64(o), ref, torch.float32, "scale 0.3")
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+
+def test_identity_v_gives_probabilities_f32():
+    """V = I (T = D = 64): O is the probability matrix itself.  Rows sum to 1,
+    entries above the diagonal are exactly 0, and P equals the oracle's."""
+    say("case: V = I")
+    q, k, _ = prefill_case(1000, 1, 64, 1, 1, 64, torch.float32)
+    v = torch.eye(64, dtype=torch.float32)[None, :, None, :]
+    o, _ = run(q, k, v)
+    p = f64(o)[0, :, 0, :]
+    np.testing.assert_allclose(p.sum(-1), 1.0, rtol=0, atol=1e-5)
+    assert np.all(np.triu(p, 1) == 0.0)
+    _, _, ref_p = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=True, return_probs=True)
+    np.testing.assert_allclose(p, ref_p[0, 0], rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_constant_v_and_first_row(dtype):
+    say(f"case: constant V {dtype}")
+    q, k, v = prefill_case(11, 1, 333, 12, 2, 128, dtype)
+    c = v[:, :1].clone()
+    vc = c.expand_as(v).contiguous()
+    o, _ = run(q, k, vc)
+    want = f64(c).repeat(6, axis=2)     # head h reads kv head h // 6
+    if dtype == torch.bfloat16:
+        # rows are convex combinations of one bf16 vector: exact up to output rounding
+        assert np.array_equal(f64(o), np.broadcast_to(want, o.shape))
+    else:
+        np.testing.assert_allclose(f64(o), np.broadcast_to(want, o.shape), rtol=0, atol=1e-5)
+    o2, _ = run(q, k, v)
+    # first causal row is V[0] exactly
+    np.testing.assert_array_equal(f64(o2)[:, 0], f64(v)[:, 0].repeat(6, axis=1))
+
+
+def test_gqa_equals_repeated_heads():
+    q, k, v = prefill_case(12, 1, 200, 12, 2, 128, torch.bfloat16)
+    o1, _ = run(q, k, v)
+    o2, _ = run(q, k.repeat_interleave(6, dim=2), v.repeat_interleave(6, dim=2))
+    assert torch.equal(o1, o2)
+
+
+def test_c4_long_prefill_sampled_rows():
+    """T 16384, 12/2 heads, D 128, bf16, causal (seed 1003), the benchmark's
+    launch: sampled rows against the oracle, computed one row at a time."""
+    say("case: C4 T16384 sampled rows")
+    q, k, v = prefill_case(1003, 1, 16384, 12, 2, 128, torch.bfloat16)
+    o, lse = run(q, k, v, want_lse=True)
+    g = rng(99)
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 129, 8191, 8192, 16255, 16256, 16383],
+                                     g.integers(0, 16384, 36)]))
+    ref, ref_lse = oracle.attention_rows(to_f64(q[0]), to_f64(k[0]), to_f64(v[0]), rows, chunk=16)
+    check(f64(o)[0, rows], ref, torch.bfloat16, "C4 rows")
+    np.testing.assert_allclose(f64(lse)[0][:, rows].T, ref_lse, rtol=0, atol=1e-3)
+    # every row finite; first row exact
+    assert torch.isfinite(o).all()
+    np.testing.assert_array_equal(f64(o)[0, 0], f64(v)[0, 0].repeat(6, axis=0))

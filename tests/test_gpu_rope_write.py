@@ -1,0 +1,103 @@
+"""Fused RoPE + paged KV-cache write (attn_kv_cache_write_rope) against the
+oracle: slot indexing and values bit-exact, rotation within tolerance."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_05_amd as mi
+from tests.gpu_util import DEV, check, f64, say
+from workloads import BLOCK_SIZE, normal, rng, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+SENTINEL = -1  # int16 0xFFFF: a NaN bit pattern in bf16
+
+
+def setup(seed, n, hq, hkv, d, nb, dtype):
+    g = rng(seed)
+    q = normal(g, (n, hq, d), dtype)
+    k = normal(g, (n, hkv, d), dtype)
+    v = normal(g, (n, hkv, d), dtype)
+    pos = g.integers(0, 32768, n).astype(np.int32)
+    slots = g.permutation(nb * BLOCK_SIZE)[:n].astype(np.int32)
+    slots[::7] = -1
+    return q, k, v, pos, slots
+
+
+def caches(nb, hkv, d, dtype):
+    if dtype == torch.bfloat16:
+        kc = torch.full((nb, hkv, BLOCK_SIZE, d), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        vc = torch.full((nb, hkv, d, BLOCK_SIZE), SENTINEL, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    else:
+        kc = torch.full((nb, hkv, BLOCK_SIZE, d), -7.0, dtype=torch.float32, device=DEV)
+        vc = torch.full((nb, hkv, d, BLOCK_SIZE), -7.0, dtype=torch.float32, device=DEV)
+    return kc, vc
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_plain_copy_is_bit_exact(dtype):
+    say(f"case: cache write copy {dtype}")
+    n, hq, hkv, d, nb = 300, 12, 2, 128, 40
+    q, k, v, pos, slots = setup(60, n, hq, hkv, d, nb, dtype)
+    kc, vc = caches(nb, hkv, d, dtype)
+    kc0, vc0 = kc.clone(), vc.clone()
+    qd = q.to(DEV)
+    mi.attn_kv_cache_write_rope(qd, k.to(DEV), v.to(DEV), torch.from_numpy(pos).to(DEV),
+                                torch.from_numpy(slots).to(DEV), kc, vc, rope_base=0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(qd.cpu(), q)      # no rotation: q untouched
+    ek, ev = oracle.kv_cache_write_expected(f64(kc0), f64(vc0), to_f64(k), to_f64(v), pos, slots,
+                                            rope_base=0.0, bf16=False)
+    if dtype == torch.bfloat16:
+        # compare raw bits, so untouched sentinel slots (NaN patterns) are checked too
+        written = ~np.isnan(ek)
+        assert np.array_equal(f64(kc)[written], ek[written])
+        assert np.array_equal(f64(vc)[~np.isnan(ev)], ev[~np.isnan(ev)])
+        untouched_k = kc.view(torch.int16).cpu().numpy()[~written]
+        assert np.all(untouched_k == SENTINEL)
+        assert np.all(vc.view(torch.int16).cpu().numpy()[np.isnan(ev)] == SENTINEL)
+    else:
+        assert np.array_equal(f64(kc), ek) and np.array_equal(f64(vc), ev)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_rope_write(dtype):
+    say(f"case: rope write {dtype}")
+    n, hq, hkv, d, nb = 500, 12, 2, 128, 64
+    q, k, v, pos, slots = setup(61, n, hq, hkv, d, nb, dtype)
+    kc, vc = caches(nb, hkv, d, dtype)
+    kc0, vc0 = kc.clone(), vc.clone()
+    qd = q.to(DEV)
+    mi.attn_kv_cache_write_rope(qd, k.to(DEV), v.to(DEV), torch.from_numpy(pos).to(DEV),
+                                torch.from_numpy(slots).to(DEV), kc, vc, rope_base=10000.0)
+    torch.cuda.synchronize()
+    bf = dtype == torch.bfloat16
+    q_ref = oracle.rope(to_f64(q), pos, 10000.0)
+    if bf:
+        q_ref = oracle.round_bf16(q_ref)
+    check(f64(qd), q_ref, dtype, "q rotated")
+    ek, ev = oracle.kv_cache_write_expected(f64(kc0), f64(vc0), to_f64(k), to_f64(v), pos, slots,
+                                            rope_base=10000.0, bf16=bf)
+    written = ~np.isnan(ek) if bf else ek != -7.0
+    # the set of written slots is exact
+    got_written = ~np.isnan(f64(kc)) if bf else f64(kc) != -7.0
+    assert np.array_equal(got_written, written)
+    check(f64(kc)[written], ek[written], dtype, "k rotated in cache")
+    # values are copied bit-exactly
+    vw = ~np.isnan(ev) if bf else ev != -7.0
+    assert np.array_equal(f64(vc)[vw], ev[vw])
+
+
+def test_rope_position_zero_is_identity():
+    n, hq, hkv, d, nb = 32, 12, 2, 64, 4
+    q, k, v, _, slots = setup(62, n, hq, hkv, d, nb, torch.bfloat16)
+    pos = np.zeros(n, dtype=np.int32)
+    kc, vc = caches(nb, hkv, d, torch.bfloat16)
+    qd = q.to(DEV)
+    mi.attn_kv_cache_write_rope(qd, k.to(DEV), v.to(DEV), torch.from_numpy(pos).to(DEV),
+                                torch.from_numpy(slots).to(DEV), kc, vc, rope_base=10000.0)
+    torch.cuda.synchronize()
+    assert torch.equal(qd.cpu(), q)

@@ -1,0 +1,277 @@
+"""Python binding of libmi_attn, the MI355X (gfx950) attention library.
+
+Argument marshalling only: every function here checks that tensors are on
+the GPU, takes their device pointers, sizes and the current HIP stream, and
+calls the C ABI of the same name (declared in include/mi_attn.h).  There is
+no CPU or PyTorch fallback; if the shared library is missing, every call
+raises.  PyTorch supplies device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+__all__ = [
+    "AttnError",
+    "Pool",
+    "attn_decode_paged",
+    "attn_decode_paged_auto_partition",
+    "attn_decode_paged_workspace_size",
+    "attn_kv_cache_write_rope",
+    "attn_last_error",
+    "attn_prefill",
+    "attn_prefill_paged",
+    "lib_path",
+    "load",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libmi_attn.so"
+BLOCK_SIZE = 16
+
+ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_NOMEM, ATTN_E_STATE, ATTN_E_DEVICE = 0, -1, -2, -3, -4, -5
+ATTN_F32, ATTN_BF16 = 0, 1
+
+_c_i32 = ctypes.c_int32
+_c_i64p = ctypes.POINTER(ctypes.c_int64)
+_c_i32p = ctypes.POINTER(ctypes.c_int32)
+_vp = ctypes.c_void_p
+
+_SIGNATURES = {
+    "attn_last_error": (ctypes.c_char_p, []),
+    "attn_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                    _c_i64p, _c_i64p, _c_i64p, _c_i64p, ctypes.c_float, _c_i32, ctypes.c_int, _vp]),
+    "attn_prefill_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float, _c_i32,
+                                          ctypes.c_int, _vp]),
+    "attn_decode_paged_workspace_size": (ctypes.c_size_t, [_c_i32] * 6),
+    "attn_decode_paged_auto_partition": (_c_i32, [_c_i32] * 3),
+    "attn_decode_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                         _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp,
+                                         ctypes.c_size_t, _vp]),
+    "attn_kv_cache_write_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp]),
+    "attn_pool_create": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_vp)]),
+    "attn_pool_destroy": (None, [_vp]),
+    "attn_pool_alloc": (ctypes.c_int, [_vp, _c_i32, _c_i32p]),
+    "attn_pool_free": (ctypes.c_int, [_vp, _c_i32p, _c_i32]),
+    "attn_pool_retain": (ctypes.c_int, [_vp, _c_i32p, _c_i32]),
+    "attn_pool_num_free": (_c_i32, [_vp]),
+    "attn_pool_num_blocks": (_c_i32, [_vp]),
+    "attn_pool_refcount": (ctypes.c_int, [_vp, _c_i32]),
+    "attn_seq_reserve": (ctypes.c_int, [_vp, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p]),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"[status {status}] {msg}")
+        self.status = status
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def load() -> ctypes.CDLL:
+    """Load the in-tree shared library (built by transformer_attention_05_amd.build)."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with `python -m transformer_attention_05_amd.build`")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def attn_last_error() -> str:
+    return load().attn_last_error().decode()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    return 99  # rejected by the library as unsupported
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (no CPU path exists)")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _i64x3(vals):
+    return (ctypes.c_int64 * 3)(*[int(x) for x in vals])
+
+
+def _bth_strides(t: torch.Tensor, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [batch, tokens, heads, head_dim]")
+    if t.stride(3) != 1:
+        raise ValueError(f"{name}: head_dim must be contiguous")
+    return _i64x3(t.stride()[:3])
+
+
+# ----------------------------------------------------------------------------- kernels
+
+def attn_prefill(q, k, v, o=None, lse=None, causal=True, scale=0.0):
+    """Contiguous attention on [B, T, H, D] tensors (any batch/token/head strides)."""
+    if o is None:
+        o = torch.empty_like(q)
+    b, tq, hq, d = q.shape
+    _, tk, hkv, _ = k.shape
+    st = load().attn_prefill(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(lse, "lse") if lse is not None else None,
+        b, tq, tk, hq, hkv, d,
+        _bth_strides(q, "q"), _bth_strides(k, "k"), _bth_strides(v, "v"), _bth_strides(o, "o"),
+        float(scale), 1 if causal else 0, _dtype_code(q), _stream(q))
+    _check(st)
+    return o
+
+
+def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, context_lens, max_seqlen_q,
+                       o=None, causal=True, scale=0.0):
+    """Chunked prefill of packed queries q [total_q, Hq, D] over the paged caches."""
+    if o is None:
+        o = torch.empty_like(q)
+    total_q, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    st = load().attn_prefill_paged(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(context_lens, "context_lens"),
+        _dev(o, "o"), context_lens.shape[0], total_q, int(max_seqlen_q), hq, hkv, d, bs, nb,
+        float(scale), 1 if causal else 0, _dtype_code(q), _stream(q))
+    _check(st)
+    return o
+
+
+def attn_decode_paged_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                     partition_size=0) -> int:
+    return int(load().attn_decode_paged_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                       max_context_len, partition_size))
+
+
+def attn_decode_paged_auto_partition(num_seqs, num_kv_heads, max_context_len) -> int:
+    return int(load().attn_decode_paged_auto_partition(num_seqs, num_kv_heads, max_context_len))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_context_len, o=None,
+                      partition_size=0, scale=0.0, workspace=None):
+    """Decode: q [S, Hq, D], one query per sequence, over the paged caches.
+
+    ``workspace`` is a uint8 GPU tensor of at least
+    attn_decode_paged_workspace_size(...) bytes; allocated here if None."""
+    if o is None:
+        o = torch.empty_like(q)
+    s, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    need = attn_decode_paged_workspace_size(s, hq, hkv, d, int(max_context_len), int(partition_size))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().attn_decode_paged(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        _dev(context_lens, "context_lens"), _dev(o, "o"), s, hq, hkv, d, bs, nb, block_table.shape[1],
+        int(max_context_len), int(partition_size), float(scale), _dtype_code(q), ws_ptr, ws_bytes, _stream(q))
+    _check(st)
+    return o
+
+
+def attn_kv_cache_write_rope(q, k, v, positions, slot_mapping, k_cache, v_cache, rope_base=10000.0):
+    """Rotate q (in place, may be None) and k; write rotated k and v into their slots."""
+    n, hkv, d = k.shape
+    hq = q.shape[1] if q is not None else hkv
+    nb = k_cache.shape[0]
+    bs = k_cache.shape[2]
+    st = load().attn_kv_cache_write_rope(
+        _dev(q, "q") if q is not None else None, _dev(k, "k"), _dev(v, "v"), _dev(positions, "positions"),
+        _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        n, hq, hkv, d, bs, nb, float(rope_base), _dtype_code(k), _stream(k))
+    _check(st)
+
+
+# ----------------------------------------------------------------------------- host pool
+
+def _i32_array(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return a, a.ctypes.data_as(_c_i32p)
+
+
+class Pool:
+    """Host block pool (LIFO free list with reference counts)."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE):
+        self._lib = load()
+        h = _vp()
+        _check(self._lib.attn_pool_create(int(num_blocks), int(block_size), ctypes.byref(h)))
+        self._h = h
+        self.block_size = block_size
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.attn_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def alloc(self, n: int) -> np.ndarray:
+        out = np.zeros(max(int(n), 0), dtype=np.int32)
+        _check(self._lib.attn_pool_alloc(self._h, int(n), out.ctypes.data_as(_c_i32p)))
+        return out
+
+    def free(self, ids):
+        a, p = _i32_array(ids)
+        _check(self._lib.attn_pool_free(self._h, p, a.size))
+
+    def retain(self, ids):
+        a, p = _i32_array(ids)
+        _check(self._lib.attn_pool_retain(self._h, p, a.size))
+
+    @property
+    def num_free(self) -> int:
+        return int(self._lib.attn_pool_num_free(self._h))
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self._lib.attn_pool_num_blocks(self._h))
+
+    def refcount(self, block_id: int) -> int:
+        r = self._lib.attn_pool_refcount(self._h, int(block_id))
+        if r < 0:
+            _check(r)
+        return int(r)
+
+    def seq_reserve(self, row: np.ndarray, cur_len: int, n_new: int) -> np.ndarray:
+        """Grow a sequence in place: ``row`` is its int32 block-table row."""
+        if row.dtype != np.int32 or not row.flags["C_CONTIGUOUS"]:
+            raise ValueError("row must be a contiguous int32 array (it is updated in place)")
+        slots = np.zeros(max(int(n_new), 0), dtype=np.int32)
+        _check(self._lib.attn_seq_reserve(self._h, row.ctypes.data_as(_c_i32p), row.size, int(cur_len), int(n_new),
+                                          slots.ctypes.data_as(_c_i32p)))
+        return slots

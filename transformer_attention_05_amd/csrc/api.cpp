@@ -1,0 +1,290 @@
+// C ABI entry points: argument validation, launch geometry and launch.
+//
+// Every entry point validates all of its arguments before the first HIP call
+// ("Fast Attention Kernels and Operator Fusion" notes that hard-wired
+// attention backends fail when they do not support the inputs, and that a
+// serving engine validates its backend at initialisation and raises; here an
+// unsupported or malformed call returns a status and launches nothing).
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kernels.h"
+#include "mi_attn.h"
+#include "status.h"
+
+using namespace mi_attn;
+
+namespace mi_attn {
+char* error_buffer() {
+  static thread_local char buf[512];
+  return buf;
+}
+}  // namespace mi_attn
+
+extern "C" const char* attn_last_error(void) { return error_buffer(); }
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_head_dim(int32_t d, const char* fn) {
+  if (d != 64 && d != 128) return fail(ATTN_E_UNSUPPORTED, "%s: head_dim %d (supported: 64, 128)", fn, d);
+  return ATTN_OK;
+}
+
+int check_heads(int32_t hq, int32_t hkv, const char* fn) {
+  if (hq < 1 || hkv < 1) return fail(ATTN_E_INVALID, "%s: head counts must be >= 1 (got %d, %d)", fn, hq, hkv);
+  if (hq % hkv != 0)
+    return fail(ATTN_E_INVALID, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", fn, hq, hkv);
+  return ATTN_OK;
+}
+
+int check_scale(float scale, int32_t d, float* scale_log2, const char* fn) {
+  if (!std::isfinite(scale) || scale < 0.f)
+    return fail(ATTN_E_INVALID, "%s: scale must be finite and >= 0 (0 = 1/sqrt(head_dim))", fn);
+  const double sc = scale == 0.f ? 1.0 / std::sqrt((double)d) : (double)scale;
+  *scale_log2 = (float)(sc * 1.4426950408889634);
+  return ATTN_OK;
+}
+
+int launched(hipError_t e, const char* fn) {
+  if (e != hipSuccess) return fail(ATTN_E_DEVICE, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            const int64_t q_strides[3], const int64_t k_strides[3],
+                            const int64_t v_strides[3], const int64_t o_strides[3],
+                            float scale, int32_t causal, attn_dtype dtype, attn_stream_t stream) {
+  static const char* fn = "attn_prefill";
+  if (!q || !k || !v || !o) return fail(ATTN_E_INVALID, "%s: q, k, v and o must be non-NULL", fn);
+  if (!q_strides || !k_strides || !v_strides || !o_strides)
+    return fail(ATTN_E_INVALID, "%s: stride arrays must be non-NULL", fn);
+  if (batch < 0 || seqlen_q < 0 || seqlen_k < 0) return fail(ATTN_E_INVALID, "%s: negative size", fn);
+  int st;
+  if ((st = check_heads(num_q_heads, num_kv_heads, fn)) != ATTN_OK) return st;
+  if ((st = check_head_dim(head_dim, fn)) != ATTN_OK) return st;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  if (causal && seqlen_k < seqlen_q)
+    return fail(ATTN_E_INVALID, "%s: causal needs seqlen_k >= seqlen_q (%d < %d)", fn, seqlen_k, seqlen_q);
+  float scale_log2;
+  if ((st = check_scale(scale, head_dim, &scale_log2, fn)) != ATTN_OK) return st;
+  const int64_t mult = dtype == ATTN_BF16 ? 8 : 4;
+  const void* ptrs[] = {q, k, v, o};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return fail(ATTN_E_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (lse && !aligned(lse, 4)) return fail(ATTN_E_INVALID, "%s: lse must be 4-byte aligned", fn);
+  const int64_t* strides[] = {q_strides, k_strides, v_strides, o_strides};
+  for (const int64_t* sa : strides)
+    for (int i = 0; i < 3; ++i)
+      if (sa[i] < 0 || sa[i] % mult != 0)
+        return fail(ATTN_E_INVALID, "%s: strides must be >= 0 and multiples of %lld elements", fn, (long long)mult);
+  if (batch == 0 || seqlen_q == 0) return ok();
+
+  PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.qs_b = q_strides[0]; a.qs_t = q_strides[1]; a.qs_h = q_strides[2];
+  a.ks_b = k_strides[0]; a.ks_t = k_strides[1]; a.ks_h = k_strides[2];
+  a.vs_b = v_strides[0]; a.vs_t = v_strides[1]; a.vs_h = v_strides[2];
+  a.os_b = o_strides[0]; a.os_t = o_strides[1]; a.os_h = o_strides[2];
+  a.batch = batch; a.tq = seqlen_q; a.tk = seqlen_k;
+  a.hq = num_q_heads; a.hkv = num_kv_heads; a.group = num_q_heads / num_kv_heads;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = scale_log2;
+  const int bm = dtype == ATTN_BF16 ? kPrefillBlockM : kPrefillF32BlockM;
+  a.num_m_tiles = ceil_div(seqlen_q, bm);
+  const int64_t nwg = (int64_t)a.num_m_tiles * num_q_heads * batch;
+  if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
+  a.num_wg = (uint32_t)nwg;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16) return launched(launch_prefill_bf16(a, head_dim, false, s), fn);
+  return launched(launch_prefill_f32(a, head_dim, s), fn);
+}
+
+// ---------------------------------------------------------------------------
+extern "C" int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                  void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks,
+                                  float scale, int32_t causal, attn_dtype dtype, attn_stream_t stream) {
+  static const char* fn = "attn_prefill_paged";
+  if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !context_lens || !o)
+    return fail(ATTN_E_INVALID, "%s: pointer arguments must be non-NULL", fn);
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(ATTN_E_INVALID, "%s: bad size", fn);
+  if (max_seqlen_q > total_q) return fail(ATTN_E_INVALID, "%s: max_seqlen_q > total_q", fn);
+  int st;
+  if ((st = check_heads(num_q_heads, num_kv_heads, fn)) != ATTN_OK) return st;
+  if ((st = check_head_dim(head_dim, fn)) != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "%s: paged kernels take bf16 only", fn);
+  if (block_size != kBlockSizeHost) return fail(ATTN_E_UNSUPPORTED, "%s: block_size %d (supported: 16)", fn, block_size);
+  float scale_log2;
+  if ((st = check_scale(scale, head_dim, &scale_log2, fn)) != ATTN_OK) return st;
+  const void* ptrs[] = {q, k_cache, v_cache, o};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return fail(ATTN_E_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!aligned(block_table, 4) || !aligned(cu_seqlens_q, 4) || !aligned(context_lens, 4))
+    return fail(ATTN_E_INVALID, "%s: int32 arrays must be 4-byte aligned", fn);
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
+
+  PrefillArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.o = o; a.lse = nullptr;
+  a.batch = num_seqs;
+  a.hq = num_q_heads; a.hkv = num_kv_heads; a.group = num_q_heads / num_kv_heads;
+  a.causal = causal ? 1 : 0;
+  a.scale_log2 = scale_log2;
+  a.num_m_tiles = ceil_div(max_seqlen_q, kPrefillBlockM);
+  const int64_t nwg = (int64_t)a.num_m_tiles * num_q_heads * num_seqs;
+  if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
+  a.num_wg = (uint32_t)nwg;
+  a.block_table = block_table; a.bt_stride = max_blocks_per_seq;
+  a.cu_seqlens_q = cu_seqlens_q; a.context_lens = context_lens;
+  a.num_blocks = num_blocks;
+  a.total_q = total_q;
+  return launched(launch_prefill_bf16(a, head_dim, true, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
+extern "C" int32_t attn_decode_paged_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
+                                                    int32_t max_context_len) {
+  // Largest power-of-two partition (128 .. 1024 tokens) that still yields
+  // about 2048 partition workgroups if every sequence were as long as the
+  // longest: enough to fill 256 CUs several times over.
+  int32_t p = 1024;
+  const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+  const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
+  while (p > 128 && units * ((ctx + p - 1) / p) < 2048) p /= 2;
+  return p;
+}
+
+namespace {
+struct DecodeGeom {
+  int32_t part, max_parts;
+  size_t o_bytes, ml_bytes;
+};
+
+DecodeGeom decode_geom(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t max_ctx, int32_t part) {
+  DecodeGeom gm{};
+  gm.part = part > 0 ? part : attn_decode_paged_auto_partition(num_seqs, hkv, max_ctx);
+  gm.max_parts = ceil_div(max_ctx, gm.part);
+  if (gm.max_parts > 1) {
+    const size_t rows = (size_t)num_seqs * hq * gm.max_parts;
+    gm.o_bytes = (rows * d * sizeof(float) + 255) / 256 * 256;
+    gm.ml_bytes = rows * 2 * sizeof(float);
+  }
+  return gm;
+}
+}  // namespace
+
+extern "C" size_t attn_decode_paged_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                   int32_t head_dim, int32_t max_context_len,
+                                                   int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0 ||
+      partition_size < 0)
+    return 0;
+  DecodeGeom gm = decode_geom(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+  return gm.o_bytes + gm.ml_bytes;
+}
+
+extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* context_lens, void* o,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 int32_t partition_size, float scale, attn_dtype dtype,
+                                 void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  static const char* fn = "attn_decode_paged";
+  if (!q || !k_cache || !v_cache || !block_table || !context_lens || !o)
+    return fail(ATTN_E_INVALID, "%s: pointer arguments must be non-NULL", fn);
+  if (num_seqs < 0 || num_blocks < 1 || max_context_len < 1)
+    return fail(ATTN_E_INVALID, "%s: bad size", fn);
+  int st;
+  if ((st = check_heads(num_q_heads, num_kv_heads, fn)) != ATTN_OK) return st;
+  if ((st = check_head_dim(head_dim, fn)) != ATTN_OK) return st;
+  if (dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "%s: paged kernels take bf16 only", fn);
+  if (block_size != kBlockSizeHost) return fail(ATTN_E_UNSUPPORTED, "%s: block_size %d (supported: 16)", fn, block_size);
+  if (max_blocks_per_seq < ceil_div(max_context_len, kBlockSizeHost))
+    return fail(ATTN_E_INVALID, "%s: max_blocks_per_seq %d cannot hold max_context_len %d", fn,
+                max_blocks_per_seq, max_context_len);
+  if (partition_size < 0 || partition_size % 128 != 0)
+    return fail(ATTN_E_INVALID, "%s: partition_size must be 0 or a positive multiple of 128", fn);
+  float scale_log2;
+  if ((st = check_scale(scale, head_dim, &scale_log2, fn)) != ATTN_OK) return st;
+  const void* ptrs[] = {q, k_cache, v_cache, o};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return fail(ATTN_E_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4))
+    return fail(ATTN_E_INVALID, "%s: int32 arrays must be 4-byte aligned", fn);
+  if (num_seqs > 65535) return fail(ATTN_E_UNSUPPORTED, "%s: at most 65535 sequences per call", fn);
+  DecodeGeom gm = decode_geom(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+  const size_t need = gm.o_bytes + gm.ml_bytes;
+  if (need > 0) {
+    if (!workspace) return fail(ATTN_E_INVALID, "%s: workspace of %zu bytes required", fn, need);
+    if (!aligned(workspace, 256)) return fail(ATTN_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
+    if (workspace_bytes < need)
+      return fail(ATTN_E_NOMEM, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);
+  }
+  if (num_seqs == 0) return ok();
+  const int32_t group = num_q_heads / num_kv_heads;
+  DecodeArgs a{};
+  a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.block_table = block_table; a.bt_stride = max_blocks_per_seq;
+  a.context_lens = context_lens; a.o = o;
+  a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + gm.o_bytes) : nullptr;
+  a.num_seqs = num_seqs; a.hq = num_q_heads; a.hkv = num_kv_heads;
+  a.group = group; a.head_groups = ceil_div(group, 16);
+  a.part_size = gm.part; a.max_parts = gm.max_parts;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale_log2;
+  if ((int64_t)num_kv_heads * a.head_groups > 65535)
+    return fail(ATTN_E_UNSUPPORTED, "%s: too many kv heads", fn);
+  return launched(launch_decode(a, head_dim, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
+extern "C" int attn_kv_cache_write_rope(void* q, const void* k, const void* v, const int32_t* positions,
+                                        const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                                        int32_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                        float rope_base, attn_dtype dtype, attn_stream_t stream) {
+  static const char* fn = "attn_kv_cache_write_rope";
+  if (!k || !v || !positions || !slot_mapping || !k_cache || !v_cache)
+    return fail(ATTN_E_INVALID, "%s: pointer arguments (except q) must be non-NULL", fn);
+  if (num_tokens < 0 || num_blocks < 1) return fail(ATTN_E_INVALID, "%s: bad size", fn);
+  int st;
+  if ((st = check_heads(num_q_heads, num_kv_heads, fn)) != ATTN_OK) return st;
+  if ((st = check_head_dim(head_dim, fn)) != ATTN_OK) return st;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  if (block_size != kBlockSizeHost) return fail(ATTN_E_UNSUPPORTED, "%s: block_size %d (supported: 16)", fn, block_size);
+  if (!std::isfinite(rope_base) || rope_base < 0.f || (rope_base > 0.f && rope_base <= 1.f))
+    return fail(ATTN_E_INVALID, "%s: rope_base must be 0 (no rotation) or > 1", fn);
+  if ((int64_t)num_blocks * kBlockSizeHost > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: pool too large", fn);
+  const uintptr_t el = dtype == ATTN_BF16 ? 2 : 4;
+  const void* ptrs[] = {k, v, k_cache, v_cache};
+  for (const void* p : ptrs)
+    if (!aligned(p, el)) return fail(ATTN_E_INVALID, "%s: misaligned tensor pointer", fn);
+  if (q && !aligned(q, el)) return fail(ATTN_E_INVALID, "%s: misaligned q", fn);
+  if (!aligned(positions, 4) || !aligned(slot_mapping, 4))
+    return fail(ATTN_E_INVALID, "%s: int32 arrays must be 4-byte aligned", fn);
+  if (num_tokens == 0) return ok();
+  RopeWriteArgs a{};
+  a.q = q; a.k = k; a.v = v; a.positions = positions; a.slot_mapping = slot_mapping;
+  a.k_cache = k_cache; a.v_cache = v_cache;
+  a.num_tokens = num_tokens; a.hq = num_q_heads; a.hkv = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.rope_base = (double)rope_base;
+  return launched(launch_rope_write(a, head_dim, dtype == ATTN_BF16, reinterpret_cast<hipStream_t>(stream)), fn);
+}

@@ -1,0 +1,82 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA
+// wrappers, cross-lane reductions, bf16 packing and the XCD-aware
+// workgroup order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi_attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBlockSize = 16;  // paged KV block, in tokens
+
+// 32x32 output tile, K = 16.  A: lane l holds row l%32, 8 contraction
+// elements; B: lane l holds column l%32, the same 8 contraction elements.
+// D: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// 16x16 output tile, K = 32.  D: lane l, register r holds row 4*(l/16) + r,
+// column l%16.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Value held by lane l ^ 32 (the other half of the wavefront).
+__device__ __forceinline__ float xor32(float x) {
+  int v = __float_as_int(x);
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  // lanes 0..31: r[1] holds lane l+32; lanes 32..63: r[0] holds lane l-32
+  return __int_as_float((__lane_id() < 32) ? r[1] : r[0]);
+}
+
+// Value held by lane l ^ 16 (within each 32-lane half): ds_swizzle in
+// bit-mask mode with and_mask 0x1f, xor_mask 0x10.
+__device__ __forceinline__ float xor16(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x401F));
+}
+
+// Round-to-nearest-even float -> bf16 bits (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f2bf_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f2bf_bits(lo) | (f2bf_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// bf16 value of a float after rounding, as a float (for sums that must see
+// exactly the rounded weights).
+__device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f2bf_bits(f) << 16); }
+
+// A block-table entry outside the pool is replaced by block 0 so that a
+// corrupt table can never address memory outside the cache.
+__device__ __forceinline__ int32_t safe_block(int32_t blk, int32_t num_blocks) {
+  return (blk >= 0 && blk < num_blocks) ? blk : 0;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (id i runs on XCD
+// i % 8).  This renumbers them so that each XCD receives a contiguous range
+// of logical ids, which keeps workgroups that share K/V tiles on one L2.
+__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t i, uint32_t n) {
+  const uint32_t q = n / 8, r = n % 8, x = i % 8;
+  return x * q + (x < r ? x : r) + i / 8;
+}
+
+}  // namespace mi_attn

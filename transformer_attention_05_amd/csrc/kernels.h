@@ -1,0 +1,76 @@
+// Argument blocks and launchers shared by the C ABI (api.cpp) and the HIP
+// kernel sources.  Launchers assume validated arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mi_attn {
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  // element strides of (batch, token, head); head_dim is contiguous
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t os_b, os_t, os_h;
+  int32_t batch, tq, tk, hq, hkv, group;
+  int32_t causal;
+  float scale_log2;  // softmax scale times log2(e)
+  int32_t num_m_tiles;
+  uint32_t num_wg;
+  // paged variant only
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* cu_seqlens_q;
+  const int32_t* context_lens;
+  int32_t num_blocks;  // pool size; out-of-range table entries are redirected to block 0
+  int32_t total_q;     // packed query rows; rows past it are never touched
+};
+
+struct DecodeArgs {
+  const void* q;        // [S][Hq][D]
+  const void* k_cache;  // [NB][Hkv][16][D]
+  const void* v_cache;  // [NB][Hkv][D][16]
+  const int32_t* block_table;
+  int32_t bt_stride;
+  const int32_t* context_lens;
+  void* o;              // [S][Hq][D]
+  float* ws_ml;         // [S][Hq][max_parts][2]  (running max, running sum)
+  float* ws_o;          // [S][Hq][max_parts][D]  (unnormalised output)
+  int32_t num_seqs, hq, hkv, group, head_groups;
+  int32_t part_size, max_parts;
+  int32_t num_blocks;  // pool size; out-of-range table entries read as zeros
+  float scale_log2;
+};
+
+struct RopeWriteArgs {
+  void* q;
+  const void* k;
+  const void* v;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  void* k_cache;
+  void* v_cache;
+  int32_t num_tokens, hq, hkv;
+  int32_t num_blocks;  // slots at or past num_blocks * 16 are skipped
+  double rope_base;    // 0 = no rotation
+};
+
+// Launchers return the launch status (hipSuccess or the error).
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hipStream_t s);
+
+// Tile geometry of the bf16 prefill kernel, used to size its grid.
+constexpr int kPrefillBlockM = 128;
+constexpr int kPrefillBlockN = 64;
+constexpr int kPrefillF32BlockM = 64;
+constexpr int kBlockSizeHost = 16;  // paged KV block, in tokens
+
+}  // namespace mi_attn

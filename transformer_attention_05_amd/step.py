@@ -1,0 +1,83 @@
+"""One serving step over a shared paged cache: fused RoPE + cache write for
+every new token, chunked prefill for the prefill requests, decode for the
+decode sequences (partition pass + merge).  Four kernel launches on one
+stream with no host synchronisation in between.
+
+The host side (block pool, block tables, slot mapping) is built once in
+``__init__``; ``run()`` only enqueues the launches, so the same buffers can be
+replayed step after step.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (Pool, attn_decode_paged, attn_decode_paged_workspace_size, attn_kv_cache_write_rope,
+               attn_prefill_paged)
+
+
+class MixedStep:
+    """Device state of one mixed step.
+
+    ``case`` supplies the new tokens (q, k, v, positions), the cached keys and
+    values of every sequence and the chunk/decode lengths; ``assign`` is a
+    callable (case, pool) -> case that reserves blocks and fills
+    ``case.tables`` and ``case.slots`` through the pool.
+    """
+
+    def __init__(self, case, assign, device="cuda", partition_size=0, scatter=None):
+        self.case = case
+        self.device = device
+        self.pool = Pool(case.num_blocks)
+        assign(case, self.pool)
+        R = len(case.cached)
+        S = len(case.dec_lengths)
+        self.R, self.S = R, S
+        self.n_prefill = R * case.chunk
+        hkv, d = case.hkv, case.d
+        dt = case.q_new.dtype
+        self.k_cache = torch.zeros(case.num_blocks, hkv, 16, d, dtype=dt, device=device)
+        self.v_cache = torch.zeros(case.num_blocks, hkv, d, 16, dtype=dt, device=device)
+        if scatter is not None:
+            for s in range(R + S):
+                scatter(self.k_cache, self.v_cache, case.tables[s], case.k_old[s], case.v_old[s])
+        self.q = case.q_new.to(device).contiguous()
+        self.k = case.k_new.to(device).contiguous()
+        self.v = case.v_new.to(device).contiguous()
+        self.positions = torch.from_numpy(case.positions.astype(np.int32)).to(device)
+        self.slots = torch.from_numpy(case.slots.astype(np.int32)).to(device)
+        self.tables = torch.from_numpy(case.tables).to(device)
+        ctx = np.concatenate([case.cached + case.chunk, case.dec_lengths]).astype(np.int32)
+        self.context_lens = torch.from_numpy(ctx).to(device)
+        cu = np.arange(R + 1, dtype=np.int32) * case.chunk
+        self.cu_seqlens_q = torch.from_numpy(cu).to(device)
+        self.max_dec_ctx = int(case.dec_lengths.max()) if S else 1
+        self.partition_size = partition_size
+        self.o_prefill = torch.empty(self.n_prefill, case.hq, d, dtype=dt, device=device)
+        self.o_decode = torch.empty(S, case.hq, d, dtype=dt, device=device)
+        need = attn_decode_paged_workspace_size(S, case.hq, hkv, d, self.max_dec_ctx, partition_size)
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+
+    def write(self):
+        attn_kv_cache_write_rope(self.q, self.k, self.v, self.positions, self.slots, self.k_cache, self.v_cache,
+                                 rope_base=self.case.rope_base)
+
+    def prefill(self):
+        R = self.R
+        attn_prefill_paged(self.q[: self.n_prefill], self.k_cache, self.v_cache, self.tables[:R],
+                           self.cu_seqlens_q, self.context_lens[:R], self.case.chunk, o=self.o_prefill,
+                           causal=True)
+
+    def decode(self):
+        R = self.R
+        attn_decode_paged(self.q[self.n_prefill:], self.k_cache, self.v_cache, self.tables[R:],
+                          self.context_lens[R:], self.max_dec_ctx, o=self.o_decode,
+                          partition_size=self.partition_size, workspace=self.workspace)
+
+    def run(self):
+        self.write()
+        if self.R:
+            self.prefill()
+        if self.S:
+            self.decode()

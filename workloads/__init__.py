@@ -94,8 +94,9 @@ def decode_case(seed, num_seqs, lo, hi, hq=12, hkv=2, d=128, dtype=torch.bfloat1
     lengths = np.asarray(lengths, dtype=np.int64)
     nblk = (lengths + BLOCK_SIZE - 1) // BLOCK_SIZE
     num_blocks = int(nblk.sum()) + slack_blocks
+    perm = g.permutation(num_blocks)  # always drawn, so values do not depend on block_order
     if block_order == "random":
-        perm = g.permutation(num_blocks)
+        pass
     elif block_order == "identity":
         perm = np.arange(num_blocks)
     elif block_order == "reversed":
