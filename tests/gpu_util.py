@@ -38,3 +38,27 @@ def check(out, ref, dtype, what=""):
         assert mx <= BF16_MAX, f"{what}: max err {mx:.3e} > {BF16_MAX}"
         assert mean <= BF16_MEAN, f"{what}: mean err {mean:.3e} > {BF16_MEAN}"
     return mx, mean
+
+
+def bf16_ulp(x):
+    """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
+    x = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(x)) - 7)
+
+
+def check_stored(out, exact, dtype, what=""):
+    """Values the method computes in fp32 and stores in `dtype` (rotated q
+    and k): compared with the exact fp64 value.  bf16 storage: at most half a
+    bf16 ulp of the exact value plus the fp32 arithmetic error (<= 1e-5 here),
+    since an absolute 1e-2 is finer than bf16 spacing once |x| >= 4.  fp32:
+    the fp32 bar."""
+    out = np.asarray(out, dtype=np.float64)
+    exact = np.asarray(exact, dtype=np.float64)
+    err = np.abs(out - exact)
+    if dtype == torch.float32:
+        bound = np.full_like(exact, F32_MAX)
+    else:
+        bound = 0.5 * bf16_ulp(np.abs(exact) + 1e-5) + 1e-5
+    worst = float((err / bound).max()) if err.size else 0.0
+    say(f"  {what}: max |err| {err.max():.3e}  worst err/bound {worst:.3f}")
+    assert np.all(err <= bound), f"{what}: error above the storage bound ({worst:.3f} of it)"

@@ -77,14 +77,15 @@ def test_block_order_invariance_and_worked_table(golden_dir):
 
 
 def test_gather_is_bit_exact():
-    """Each sequence's query selects one target token (a large score on one
-    channel); the value of every token encodes its position exactly in bf16,
+    """Each sequence's query selects one target token: its score exceeds every
+    other by more than 150 in log2 units, so every other weight is exactly 0
+    in fp32.  The value of every token encodes its position exactly in bf16,
     so the output names the token the kernel read through the block table."""
     say("case: gather")
     g = rng(43)
     lengths = g.integers(1, 3000, 40)
     case = decode_case(44, 40, 1, 1, lengths=lengths)
-    big = 16.0
+    big = 40.0   # score 1600 / sqrt(128) = 141.4, i.e. 204 in log2 units
     targets = np.array([int(g.integers(0, L)) for L in lengths])
     q = torch.zeros_like(case.q)
     q[:, :, 0] = big

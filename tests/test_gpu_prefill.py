@@ -16,6 +16,20 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
+# LSE bar.  bf16 path: the row sum accumulates the bf16-rounded weights that
+# feed the PV product (each within a relative 2**-9 of exact), so
+# |LSE - exact| <= ln(1 + 2**-9) ~ 1.95e-3 plus fp32 rounding.  fp32 path: 1e-5.
+LSE_BF16 = 2.0e-3
+LSE_F32 = 1e-5
+
+
+def check_lse(got, ref, dtype, what):
+    e = np.abs(np.asarray(got, dtype=np.float64) - ref)
+    bar = LSE_BF16 if dtype == torch.bfloat16 else LSE_F32
+    say(f"  {what} LSE: max |err| {e.max():.3e} (bar {bar})")
+    assert e.max() <= bar
+
+
 def run(q, k, v, causal=True, want_lse=False, scale=0.0):
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=DEV) if want_lse else None
@@ -31,7 +45,7 @@ def test_c1_single_head_f32():
     o, lse = run(q, k, v, want_lse=True)
     ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=True, scale=0.125)
     check(f64(o), ref, torch.float32, "C1 O")
-    np.testing.assert_allclose(f64(lse), ref_lse, rtol=0, atol=1e-5)
+    check_lse(f64(lse), ref_lse, torch.float32, "C1")
 
 
 def test_c2_qwen_shape_bf16():
@@ -41,7 +55,7 @@ def test_c2_qwen_shape_bf16():
     o, lse = run(q, k, v, want_lse=True)
     ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=True)
     check(f64(o), ref, torch.bfloat16, "C2 O")
-    np.testing.assert_allclose(f64(lse), ref_lse, rtol=0, atol=1e-3)
+    check_lse(f64(lse), ref_lse, torch.bfloat16, "C2")
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
@@ -86,7 +100,7 @@ def test_ragged_shapes(case, dtype):
     o, lse = run(q, k, v, causal=causal, want_lse=True)
     ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=causal)
     check(f64(o), ref, dtype, f"ragged {case}")
-    np.testing.assert_allclose(f64(lse), ref_lse, rtol=0, atol=1e-3 if dtype == torch.bfloat16 else 1e-5)
+    check_lse(f64(lse), ref_lse, dtype, "ragged")
 
 
 def test_explicit_scale():
@@ -148,7 +162,7 @@ def test_c4_long_prefill_sampled_rows():
                                      g.integers(0, 16384, 36)]))
     ref, ref_lse = oracle.attention_rows(to_f64(q[0]), to_f64(k[0]), to_f64(v[0]), rows, chunk=16)
     check(f64(o)[0, rows], ref, torch.bfloat16, "C4 rows")
-    np.testing.assert_allclose(f64(lse)[0][:, rows].T, ref_lse, rtol=0, atol=1e-3)
+    check_lse(f64(lse)[0][:, rows].T, ref_lse, torch.bfloat16, "C4 rows")
     # every row finite; first row exact
     assert torch.isfinite(o).all()
     np.testing.assert_array_equal(f64(o)[0, 0], f64(v)[0, 0].repeat(6, axis=0))

@@ -7,7 +7,7 @@ import torch
 
 import oracle
 import transformer_attention_05_amd as mi
-from tests.gpu_util import DEV, check, f64, say
+from tests.gpu_util import DEV, check, check_stored, f64, say
 from workloads import BLOCK_SIZE, normal, rng, to_f64
 
 pytestmark = [pytest.mark.gpu,
@@ -75,17 +75,22 @@ def test_rope_write(dtype):
                                 torch.from_numpy(slots).to(DEV), kc, vc, rope_base=10000.0)
     torch.cuda.synchronize()
     bf = dtype == torch.bfloat16
-    q_ref = oracle.rope(to_f64(q), pos, 10000.0)
-    if bf:
-        q_ref = oracle.round_bf16(q_ref)
-    check(f64(qd), q_ref, dtype, "q rotated")
+    check_stored(f64(qd), oracle.rope(to_f64(q), pos, 10000.0), dtype, "q rotated")
+    # exact (unrounded) rotated keys in the expected cache, to bound the stored ones
     ek, ev = oracle.kv_cache_write_expected(f64(kc0), f64(vc0), to_f64(k), to_f64(v), pos, slots,
-                                            rope_base=10000.0, bf16=bf)
+                                            rope_base=10000.0, bf16=False)
     written = ~np.isnan(ek) if bf else ek != -7.0
     # the set of written slots is exact
     got_written = ~np.isnan(f64(kc)) if bf else f64(kc) != -7.0
     assert np.array_equal(got_written, written)
-    check(f64(kc)[written], ek[written], dtype, "k rotated in cache")
+    check_stored(f64(kc)[written], ek[written], dtype, "k rotated in cache")
+    if bf:
+        # and nearly every stored key equals the oracle's rounding of the exact value
+        ekr, _ = oracle.kv_cache_write_expected(f64(kc0), f64(vc0), to_f64(k), to_f64(v), pos, slots,
+                                                rope_base=10000.0, bf16=True)
+        same = np.mean(f64(kc)[written] == ekr[written])
+        say(f"  stored keys equal to round(exact): {same:.6f}")
+        assert same > 0.999
     # values are copied bit-exactly
     vw = ~np.isnan(ev) if bf else ev != -7.0
     assert np.array_equal(f64(vc)[vw], ev[vw])

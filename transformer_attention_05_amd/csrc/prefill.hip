@@ -413,19 +413,21 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
 #pragma unroll
       for (int d = 0; d < 64; ++d) dot = fmaf(qr[d], ks[j][part * 64 + d], dot);
       if (LPQ == 2) dot += __shfl_xor(dot, 1);
-      s[j] = (n0 + j <= lim) ? dot : -INFINITY;
+      // scores are kept in log2 units (scale * log2 e folded in once), so the
+      // exponent below is a plain difference of stored values and the row
+      // maximum gets weight exactly 1
+      s[j] = (n0 + j <= lim) ? dot * c2 : -INFINITY;
       tmax = fmaxf(tmax, s[j]);
     }
     const float m_new = fmaxf(m_run, tmax);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2f((m_run - m_use) * c2);
+    const float alpha = exp2f(m_run - m_use);
     l_run *= alpha;
 #pragma unroll
     for (int d = 0; d < 64; ++d) acc[d] *= alpha;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      // unfused: the row maximum itself gets weight exactly 1
-      const float p = exp2f(__fsub_rn(__fmul_rn(s[j], c2), __fmul_rn(m_use, c2)));
+      const float p = exp2f(s[j] - m_use);
       l_run += p;
 #pragma unroll
       for (int d = 0; d < 64; ++d) acc[d] = fmaf(p, vs[j][part * 64 + d], acc[d]);
@@ -437,8 +439,7 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
 #pragma unroll
     for (int d = 0; d < 64; ++d) op[(int64_t)qi * a.os_t + part * 64 + d] = acc[d] * inv;
     if (a.lse != nullptr && part == 0)
-      a.lse[((int64_t)b * a.hq + h) * tq + qi] =
-          l_run > 0.f ? (m_run * c2 + log2f(l_run)) * kLn2 : -INFINITY;
+      a.lse[((int64_t)b * a.hq + h) * tq + qi] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   }
 }
 
