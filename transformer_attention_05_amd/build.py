@@ -36,8 +36,10 @@ def _flags(src: str):
     common = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
     if src.endswith(".hip"):
         # packed fp32 instructions are disabled for all device code
+        # MFMA accumulators in VGPRs: the softmax works on them directly
         return common + ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-                         "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast"]
+                         "-Xclang", "-packed-fp32-ops", "-ffp-contract=fast",
+                         "-mllvm", "--amdgpu-mfma-vgpr-form"]
     return common + ["-D__HIP_PLATFORM_AMD__"]
 
 

@@ -10,6 +10,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 
 #include "kernels.h"
 #include "mi_attn.h"
@@ -57,6 +59,29 @@ int launched(hipError_t e, const char* fn) {
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
+// Tile shape of the bf16 prefill kernel: two query heads of one kv group per
+// workgroup (each K/V tile serves both) and 128-query tiles when there is
+// enough work; smaller workgroups when that would leave CUs idle.  The
+// environment variable MI_ATTN_PREFILL_TILE="hpw,wph" overrides the choice
+// (tuning only).
+struct PrefillTile {
+  int hpw, wph;
+};
+
+PrefillTile prefill_tile(int64_t max_q, int32_t hq, int32_t group, int64_t batch) {
+  PrefillTile t{(group % 2 == 0) ? 2 : 1, 4};
+  auto wgs = [&](const PrefillTile& c) { return ((max_q + 32 * c.wph - 1) / (32 * c.wph)) * (hq / c.hpw) * batch; };
+  if (wgs(t) < 512 && t.hpw == 2) t.hpw = 1;
+  if (wgs(t) < 512) t.wph = 2;
+  static const char* env = std::getenv("MI_ATTN_PREFILL_TILE");
+  if (env) {
+    int h = 0, w = 0;
+    if (std::sscanf(env, "%d,%d", &h, &w) == 2 && ((h == 2 && w == 4 && group % 2 == 0) || (h == 1 && (w == 4 || w == 2))))
+      t = PrefillTile{h, w};
+  }
+  return t;
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -101,13 +126,19 @@ extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o
   a.hq = num_q_heads; a.hkv = num_kv_heads; a.group = num_q_heads / num_kv_heads;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = scale_log2;
-  const int bm = dtype == ATTN_BF16 ? kPrefillBlockM : kPrefillF32BlockM;
-  a.num_m_tiles = ceil_div(seqlen_q, bm);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16) {
+    const PrefillTile t = prefill_tile(seqlen_q, num_q_heads, a.group, batch);
+    a.num_m_tiles = ceil_div(seqlen_q, 32 * t.wph);
+    const int64_t nwg = (int64_t)a.num_m_tiles * (num_q_heads / t.hpw) * batch;
+    if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
+    a.num_wg = (uint32_t)nwg;
+    return launched(launch_prefill_bf16(a, head_dim, false, t.hpw, t.wph, s), fn);
+  }
+  a.num_m_tiles = ceil_div(seqlen_q, kPrefillF32BlockM);
   const int64_t nwg = (int64_t)a.num_m_tiles * num_q_heads * batch;
   if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
   a.num_wg = (uint32_t)nwg;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (dtype == ATTN_BF16) return launched(launch_prefill_bf16(a, head_dim, false, s), fn);
   return launched(launch_prefill_f32(a, head_dim, s), fn);
 }
 
@@ -145,15 +176,16 @@ extern "C" int attn_prefill_paged(const void* q, const void* k_cache, const void
   a.hq = num_q_heads; a.hkv = num_kv_heads; a.group = num_q_heads / num_kv_heads;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = scale_log2;
-  a.num_m_tiles = ceil_div(max_seqlen_q, kPrefillBlockM);
-  const int64_t nwg = (int64_t)a.num_m_tiles * num_q_heads * num_seqs;
+  const PrefillTile t = prefill_tile(max_seqlen_q, num_q_heads, a.group, num_seqs);
+  a.num_m_tiles = ceil_div(max_seqlen_q, 32 * t.wph);
+  const int64_t nwg = (int64_t)a.num_m_tiles * (num_q_heads / t.hpw) * num_seqs;
   if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
   a.num_wg = (uint32_t)nwg;
   a.block_table = block_table; a.bt_stride = max_blocks_per_seq;
   a.cu_seqlens_q = cu_seqlens_q; a.context_lens = context_lens;
   a.num_blocks = num_blocks;
   a.total_q = total_q;
-  return launched(launch_prefill_bf16(a, head_dim, true, reinterpret_cast<hipStream_t>(stream)), fn);
+  return launched(launch_prefill_bf16(a, head_dim, true, t.hpw, t.wph, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 // ---------------------------------------------------------------------------

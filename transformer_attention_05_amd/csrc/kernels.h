@@ -62,13 +62,14 @@ struct RopeWriteArgs {
 };
 
 // Launchers return the launch status (hipSuccess or the error).
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, hipStream_t s);
+// hpw: query heads sharing each K/V tile (1 or 2); wph: wavefronts of 32
+// queries per head (4, or 2 with hpw 1).  Query tile = 32 * wph rows.
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hipStream_t s);
 
 // Tile geometry of the bf16 prefill kernel, used to size its grid.
-constexpr int kPrefillBlockM = 128;
 constexpr int kPrefillBlockN = 64;
 constexpr int kPrefillF32BlockM = 64;
 constexpr int kBlockSizeHost = 16;  // paged KV block, in tokens

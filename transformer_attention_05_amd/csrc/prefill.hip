@@ -42,31 +42,54 @@ namespace mi_attn {
 
 namespace {
 
-constexpr int BM = kPrefillBlockM;  // queries per workgroup
 constexpr int BN = kPrefillBlockN;  // keys per tile
-constexpr int NW = 4;               // wavefronts per workgroup
-constexpr int NT = NW * 64;
+constexpr float kLazyTau = 8.f;     // rescale only when the row max grows by more than 2^8
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS tiles are unpadded and XOR-swizzled at 16-byte granularity so that
+// the MFMA operand reads are free of bank conflicts.  (row, chunk) is stored
+// in chunk slot  chunk ^ swizzle(row).
 template <int D>
-struct PrefillSmem {
-  static constexpr int KS = D + 8;   // K row stride (elements): 16B-aligned rows, conflict-free b128 reads
-  static constexpr int VS = BN + 4;  // V^T row stride: 8B-aligned, conflict-free b64 reads
-  __bf16 k[2][BN * KS];
-  __bf16 vt[2][D * VS];
-};
+__device__ __forceinline__ int k_swz(int r) {    // K rows: 16 consecutive rows hit 16 distinct slots
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int v_swz(int r) {    // V rows, read 4 rows x 64 B at a time by the transpose read
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+__device__ __forceinline__ int vt_swz(int d) {   // V^T rows (paged, 64 keys = 8 chunks per row)
+  return (d >> 1) & 7;
+}
 
-template <int D, bool PAGED>
-__global__ __launch_bounds__(NT) void prefill_bf16_kernel(const PrefillArgs a) {
-  using S = PrefillSmem<D>;
-  __shared__ S sm;
+// Tile geometry: HPW query heads share every K/V tile (same kv head under
+// GQA); each head has WPH wavefronts of 32 queries.
+template <int D, bool PAGED, int HPW, int WPH>
+__global__ __launch_bounds__(64 * HPW * WPH) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_bf16_kernel(const PrefillArgs a) {
+  constexpr int NW = HPW * WPH;
+  constexpr int BM = 32 * WPH;
+  constexpr int CH = D / 8;                  // 16-byte chunks per K/V row
+  constexpr int LOADS = BN * D * 2 / 1024;   // 1 KiB wave-wide DMA instructions per tile
+  constexpr int LPW = LOADS / NW;
+  static_assert(LPW * NW == LOADS, "tile DMA must split evenly over the wavefronts");
+  constexpr int RPI = 64 / CH;               // rows per DMA instruction
+
+  __shared__ __attribute__((aligned(1024))) __bf16 smk0[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 smk1[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 smv0[BN * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 smv1[BN * D];
 
   const uint32_t id = xcd_logical_id(blockIdx.x, a.num_wg);
-  const uint32_t per_tile = (uint32_t)a.hq * (uint32_t)a.batch;
+  const int hgroups = a.hq / HPW;
+  const uint32_t per_tile = (uint32_t)hgroups * (uint32_t)a.batch;
   const int mt = a.num_m_tiles - 1 - (int)(id / per_tile);
   const uint32_t rem = id % per_tile;
-  const int b = (int)(rem / a.hq);
-  const int h = (int)(rem % a.hq);
-  const int g = h / a.group;
+  const int b = (int)(rem / hgroups);
+  const int h0 = (int)(rem % hgroups) * HPW;
+  const int g = h0 / a.group;
 
   int32_t tq, tk;
   int64_t q_row0 = 0;
@@ -77,47 +100,40 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(const PrefillArgs a) {
     // the memory it touches
     tq = max(0, min(a.cu_seqlens_q[b + 1], a.total_q) - max(c0, 0));
     tk = min(a.context_lens[b], a.bt_stride * kBlockSize);
-    q_row0 = c0;
+    q_row0 = max(c0, 0);
     bt_row = a.block_table + (int64_t)b * a.bt_stride;
   } else {
     tq = a.tq;
     tk = a.tk;
   }
   const int m0 = mt * BM;
-  if (m0 >= tq) return;  // whole workgroup: no barrier is skipped by part of it
+  if (m0 >= tq) return;  // uniform over the workgroup
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int hh = lane >> 5;  // half of the wavefront
+  const int hh = lane >> 5;
   const int lq = lane & 31;
-  const int off = tk - tq;   // bottom-right causal alignment (tk >= tq for causal calls)
+  const int h = h0 + wave / WPH;
+  const int off = tk - tq;  // bottom-right causal alignment
 
   const __bf16* qp = static_cast<const __bf16*>(a.q);
-  const __bf16* kp = static_cast<const __bf16*>(a.k);
-  const __bf16* vp = static_cast<const __bf16*>(a.v);
   __bf16* op = static_cast<__bf16*>(a.o);
-
-  // Row addresses.  Contiguous: batch/token/head strides.  Paged: packed q
-  // rows [total_q][Hq][D]; K/V from the caches.
   const int64_t q_stride_t = PAGED ? (int64_t)a.hq * D : a.qs_t;
   const __bf16* q_base = PAGED ? qp + (q_row0 * a.hq + h) * D : qp + b * a.qs_b + h * a.qs_h;
   __bf16* o_base = PAGED ? op + (q_row0 * a.hq + h) * D : op + b * a.os_b + h * a.os_h;
   const int64_t o_stride_t = PAGED ? (int64_t)a.hq * D : a.os_t;
 
-  // ---- Q^T operand, resident for the whole kernel
-  const int wq0 = m0 + wave * 32;
+  // ---- Q^T operand (lane: query lq, channels 16c + 8hh .. +7), resident
+  const int wq0 = m0 + (wave % WPH) * 32;
   const int qi = wq0 + lq;
   bf16x8 qreg[D / 16];
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    if (qi < tq)
-      qreg[c] = *reinterpret_cast<const bf16x8*>(q_base + (int64_t)qi * q_stride_t + 16 * c + 8 * hh);
-    else
-      qreg[c] = bf16x8{};
-  }
+  for (int c = 0; c < D / 16; ++c)
+    qreg[c] = qi < tq ? *reinterpret_cast<const bf16x8*>(q_base + (int64_t)qi * q_stride_t + 16 * c + 8 * hh)
+                      : bf16x8{};
 
-  // ---- number of key tiles
+  // ---- key tiles this workgroup visits
   int n_tiles = (tk + BN - 1) / BN;
   if (a.causal) {
     const int q_hi = min(m0 + BM, tq) - 1;
@@ -125,212 +141,189 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(const PrefillArgs a) {
     n_tiles = kmax < 0 ? 0 : kmax / BN + 1;
   }
 
-  // ---- global -> register staging of one K/V tile
-  constexpr int CPR = D / 8;              // 16-byte chunks per K row
-  constexpr int KPT = BN * CPR / NT;      // K chunks per thread
-  static_assert(KPT * NT == BN * CPR, "K tile must split evenly");
-  u32x4 kreg[KPT];
-  // contiguous V: groups of 4 keys x 8 channels, transposed in registers
-  constexpr int VG = (BN / 4) * CPR;
-  constexpr int VPT_C = (VG + NT - 1) / NT;
-  // paged V: the cache is token-minor, chunks of 8 tokens x 1 channel
-  constexpr int VPT_P = (D * BN / 8) / NT;
-  constexpr int VREGS = PAGED ? VPT_P : 4 * VPT_C;
-  u32x4 vreg[VREGS];
-
-  auto k_row_ptr = [&](int key) -> const __bf16* {
+  // ---- global -> LDS DMA of one K/V tile (rows past the keys re-read the
+  // last key: finite values whose weights are masked to zero)
+  const __bf16* kbase = static_cast<const __bf16*>(a.k);
+  const __bf16* vbase = static_cast<const __bf16*>(a.v);
+  auto key_row = [&](const __bf16* base, int64_t sb, int64_t st, int64_t sh, int key) -> const __bf16* {
     if constexpr (PAGED) {
       const int32_t blk = safe_block(bt_row[key >> 4], a.num_blocks);
-      return static_cast<const __bf16*>(a.k) + (((int64_t)blk * a.hkv + g) * kBlockSize + (key & 15)) * D;
+      return base + (((int64_t)blk * a.hkv + g) * kBlockSize + (key & 15)) * D;
     } else {
-      return kp + b * a.ks_b + (int64_t)key * a.ks_t + g * a.ks_h;
+      return base + b * sb + (int64_t)key * st + g * sh;
     }
   };
-
-  auto load_tile = [&](int n0) {
+  auto issue_tile = [&](__bf16* dk, __bf16* dv, int n0) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = c % CPR;
-      const int key = n0 + row;
-      kreg[i] = key < tk ? *reinterpret_cast<const u32x4*>(k_row_ptr(key) + col * 8) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < LPW; ++i) {
+      const int ii = wave * LPW + i;
+      const int r = ii * RPI + lane / CH;
+      const int slot = lane % CH;
+      const int key = min(n0 + r, tk - 1);
+      const __bf16* ksrc = key_row(kbase, a.ks_b, a.ks_t, a.ks_h, key) + 8 * (slot ^ k_swz<D>(r));
+      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(dk + ii * 512), 16, 0, 0);
+      if constexpr (!PAGED) {
+        const __bf16* vsrc = key_row(vbase, a.vs_b, a.vs_t, a.vs_h, key) + 8 * (slot ^ v_swz<D>(r));
+        __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(dv + ii * 512), 16, 0, 0);
+      } else {
+        // V^T tile: row d holds the tile's 64 keys (8 chunks of 8 tokens),
+        // read straight from the token-minor value blocks
+        const int d = ii * 8 + lane / 8;
+        const int c = (lane % 8) ^ vt_swz(d);
+        int tok0 = n0 + 8 * c;
+        if (tok0 >= tk) tok0 = ((tk - 1) >> 3) << 3;
+        const int32_t blk = safe_block(bt_row[tok0 >> 4], a.num_blocks);
+        const __bf16* vsrc = vbase + (((int64_t)blk * a.hkv + g) * D + d) * kBlockSize + (tok0 & 8);
+        __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(dv + ii * 512), 16, 0, 0);
+      }
     }
+  };
+  // Paged V^T: past the context a block holds arbitrary bits and 0 * NaN is
+  // NaN, so the tokens of the last tile beyond the context are zeroed.
+  auto zero_tail = [&](__bf16* dv, int n0) {
     if constexpr (PAGED) {
-#pragma unroll
-      for (int i = 0; i < VPT_P; ++i) {
-        const int c = tid + i * NT;
-        const int d = c >> 3, part = c & 7;
-        const int bi = part >> 1, half = part & 1;
-        const int tok0 = n0 + 16 * bi + 8 * half;
-        u32x4 val = {0, 0, 0, 0};
-        if (tok0 < tk) {
-          const int32_t blk = safe_block(bt_row[tok0 >> 4], a.num_blocks);
-          const __bf16* src = static_cast<const __bf16*>(a.v) +
-                              (((int64_t)blk * a.hkv + g) * D + d) * kBlockSize + 8 * half;
-          val = *reinterpret_cast<const u32x4*>(src);
-          const int valid = tk - tok0;  // tokens of this chunk inside the context
-          if (valid < 8) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if (2 * e >= valid) val[e] = 0;
-              else if (2 * e + 1 >= valid) val[e] &= 0xffffu;
-            }
-          }
-        }
-        vreg[i] = val;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < VPT_C; ++i) {
-        const int grp = tid + i * NT;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vreg[4 * i + r] = u32x4{0, 0, 0, 0};
-        if (grp < VG) {
-          const int k4 = grp / CPR, dc = grp % CPR;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = n0 + 4 * k4 + r;
-            if (key < tk)
-              vreg[4 * i + r] = *reinterpret_cast<const u32x4*>(vp + b * a.vs_b + (int64_t)key * a.vs_t +
-                                                                 g * a.vs_h + dc * 8);
-          }
+      const int nz = n0 + BN - tk;
+      if (nz > 0) {
+        for (int e = tid; e < D * nz; e += 64 * NW) {
+          const int d = e / nz, kl = BN - nz + e % nz;
+          dv[d * BN + 8 * ((kl >> 3) ^ vt_swz(d)) + (kl & 7)] = __bf16{};
         }
       }
     }
   };
 
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(&sm.k[buf][row * S::KS + col * 8]) = kreg[i];
-    }
-    if constexpr (PAGED) {
-#pragma unroll
-      for (int i = 0; i < VPT_P; ++i) {
-        const int c = tid + i * NT;
-        const int d = c >> 3, part = c & 7;
-        const int bi = part >> 1, half = part & 1;
-        __bf16* dst = &sm.vt[buf][d * S::VS + 16 * bi + 8 * half];
-        reinterpret_cast<u32x2*>(dst)[0] = u32x2{vreg[i][0], vreg[i][1]};
-        reinterpret_cast<u32x2*>(dst)[1] = u32x2{vreg[i][2], vreg[i][3]};
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < VPT_C; ++i) {
-        const int grp = tid + i * NT;
-        if (grp < VG) {
-          const int k4 = grp / CPR, dc = grp % CPR;
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const uint32_t x0 = vreg[4 * i + 0][w], x1 = vreg[4 * i + 1][w];
-            const uint32_t x2 = vreg[4 * i + 2][w], x3 = vreg[4 * i + 3][w];
-            // channel 2w: low halves; channel 2w+1: high halves
-            const u32x2 lo = {(x0 & 0xffffu) | (x1 << 16), (x2 & 0xffffu) | (x3 << 16)};
-            const u32x2 hi = {(x0 >> 16) | (x1 & 0xffff0000u), (x2 >> 16) | (x3 & 0xffff0000u)};
-            *reinterpret_cast<u32x2*>(&sm.vt[buf][(dc * 8 + 2 * w) * S::VS + 4 * k4]) = lo;
-            *reinterpret_cast<u32x2*>(&sm.vt[buf][(dc * 8 + 2 * w + 1) * S::VS + 4 * k4]) = hi;
-          }
-        }
-      }
-    }
-  };
-
-  // ---- running statistics (raw-score units) and output accumulator
   const float c2 = a.scale_log2;
-  float m_run = -INFINITY;
-  float l_run = 0.f;  // this lane's half of the row sum
+  const float tau_raw = kLazyTau / c2;
+  float m_run = -INFINITY;  // running max of raw scores (the one the weights are relative to)
+  float l_run = 0.f;        // this lane's half of the row sum
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
 
   const int wq_hi = min(wq0 + 31, tq - 1);
   const bool wave_has_rows = wq0 < tq;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  if (n_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < n_tiles; ++j) {
-    const int buf = j & 1;
-    const int n0 = j * BN;
-    if (j + 1 < n_tiles) load_tile(n0 + BN);
-
-    const bool active = wave_has_rows && (!a.causal || n0 <= wq_hi + off);
-    if (active) {
-      // S^T = K Q^T for two 32-key subtiles
-      f32x16 sacc[2];
+  auto compute_tile = [&](const __bf16* sk, const __bf16* sv, int n0) {
+    if (!(wave_has_rows && (!a.causal || n0 <= wq_hi + off))) return;
+    // S^T = K Q^T, two 32-key subtiles
+    f32x16 sacc[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        sacc[kt] = f32x16{};
+    for (int kt = 0; kt < 2; ++kt) {
+      sacc[kt] = f32x16{};
+      const int r = kt * 32 + lq;
 #pragma unroll
-        for (int c = 0; c < D / 16; ++c) {
-          const bf16x8 kv = *reinterpret_cast<const bf16x8*>(&sm.k[buf][(kt * 32 + lq) * S::KS + 16 * c + 8 * hh]);
-          sacc[kt] = mfma32(kv, qreg[c], sacc[kt]);
-        }
+      for (int c = 0; c < D / 16; ++c) {
+        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(sk + r * D + 8 * ((2 * c + hh) ^ k_swz<D>(r)));
+        sacc[kt] = mfma32(kv, qreg[c], sacc[kt]);
       }
-      // mask: only tiles crossing the diagonal or the end of the keys
-      const bool need_mask = (n0 + BN > tk) || (a.causal && n0 + BN - 1 > wq0 + off);
-      if (need_mask) {
-        const int lim = a.causal ? min(tk - 1, qi + off) : tk - 1;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = n0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > lim) sacc[kt][r] = -INFINITY;
-          }
-      }
-      // online softmax
-      float tmax = -INFINITY;
+    }
+    if ((n0 + BN > tk) || (a.causal && n0 + BN - 1 > wq0 + off)) {
+      const int lim = a.causal ? min(tk - 1, qi + off) : tk - 1;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kt][r]);
-      tmax = fmaxf(tmax, xor32(tmax));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-      const float mc = m_use * c2;
-      bf16x8 pb[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][8 * (kc & 1) + i], c2, -mc));
-          const __bf16 pbf = static_cast<__bf16>(p);
-          pb[kc][i] = pbf;
-          lsum += static_cast<float>(pbf);
+        for (int r = 0; r < 16; ++r) {
+          const int key = n0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key > lim) sacc[kt][r] = -INFINITY;
         }
-      }
-      l_run = fmaf(l_run, alpha, lsum);
-      m_run = m_new;
+    }
+    // online softmax; the reference max moves only when it grows by > 2^8
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kt][r]);
+    tmax = fmaxf(tmax, xor32(tmax));
+    if (__any(tmax > m_run + tau_raw)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c2);
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
-      // O^T += V^T P^T, keys of step kc in the accumulator's order
+      m_run = m_new;
+    }
+    const float mc = (m_run == -INFINITY ? 0.f : m_run) * c2;
+    bf16x8 pb[4];
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        const __bf16* vrow = &sm.vt[buf][(dt * 32 + lq) * S::VS];
+    for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow + 16 * kc + 4 * hh);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 16 * kc + 8 + 4 * hh);
-          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-          oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w), pb[kc], oacc[dt]);
+      for (int i = 0; i < 8; ++i)
+        pb[kc][i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][8 * (kc & 1) + i], c2, -mc)));
+    // row sum of exactly the bf16 weights that enter the PV product
+    float lsum = l_run;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x2 pr = {pb[kc][2 * i], pb[kc][2 * i + 1]};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+      }
+    l_run = lsum;
+    // O^T += V^T P^T; keys of step kc in the accumulator's order
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+        u32x4 w;
+        if constexpr (PAGED) {
+          const int d = dt * 32 + lq;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc) ^ vt_swz(d)) + 4 * hh);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc + 1) ^ vt_swz(d)) + 4 * hh);
+          w = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          // transpose read: lane j of each 16-lane group addresses row
+          // (key) base + j/4, channels 4*(j%4) .. +3 of its 16-channel slice
+          const int grp = lane >> 4, j = lane & 15;
+          const int dch = dt * 32 + 16 * (grp & 1) + 4 * (j & 3);  // first channel of the 8-byte piece
+          const int r0 = 16 * kc + 4 * hh + (j >> 2);
+          const int r1 = r0 + 8;
+          const __bf16* p0 = sv + r0 * D + 8 * ((dch >> 3) ^ v_swz<D>(r0)) + (dch & 4);
+          const __bf16* p1 = sv + r1 * D + 8 * ((dch >> 3) ^ v_swz<D>(r1)) + (dch & 4);
+          const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+          const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
+          const u32x2 lo = __builtin_bit_cast(u32x2, t0);
+          const u32x2 hi = __builtin_bit_cast(u32x2, t1);
+          w = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
+        oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w), pb[kc], oacc[dt]);
       }
     }
+  };
 
-    if (j + 1 < n_tiles) store_tile(buf ^ 1);
+  // ---- main loop: DMA of tile j+1 overlaps the MFMAs of tile j.  The two
+  // buffers are separate LDS objects and the loop is unrolled by two, so the
+  // DMA into one buffer never forces a wait before reading the other.
+  if (n_tiles > 0) {
+    issue_tile(smk0, smv0, 0);
+    __builtin_amdgcn_s_waitcnt(0);   // also retires the Q loads
     __syncthreads();
+    zero_tail(smv0, 0);
+    if (PAGED && BN > tk) __syncthreads();
+  }
+  for (int j = 0; j < n_tiles; j += 2) {
+    const int n0 = j * BN;
+    if (j + 1 < n_tiles) issue_tile(smk1, smv1, n0 + BN);
+    compute_tile(smk0, smv0, n0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (j + 1 >= n_tiles) break;
+    if (PAGED && n0 + 2 * BN > tk) {
+      zero_tail(smv1, n0 + BN);
+      __syncthreads();
+    }
+    if (j + 2 < n_tiles) issue_tile(smk0, smv0, n0 + 2 * BN);
+    compute_tile(smk1, smv1, n0 + BN);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (PAGED && j + 2 < n_tiles && n0 + 3 * BN > tk) {
+      zero_tail(smv0, n0 + 2 * BN);
+      __syncthreads();
+    }
   }
 
-  // ---- epilogue: O = O / l, optional LSE
-  const float l_tot = l_run + xor32(l_run);  // both halves of the row, wave-uniform call
+  // ---- epilogue: O = O / l, optional LSE (natural log)
+  const float l_tot = l_run + xor32(l_run);
   if (qi < tq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     __bf16* orow = o_base + (int64_t)qi * o_stride_t;
@@ -445,14 +438,21 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
 
 }  // namespace
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, hipStream_t s) {
-  dim3 grid(a.num_wg), block(NT);
+template <int D, bool PAGED>
+static void launch_cfg(const PrefillArgs& a, int hpw, int wph, hipStream_t s) {
+  dim3 grid(a.num_wg);
+  if (hpw == 2 && wph == 4) hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 2, 4>), grid, dim3(512), 0, s, a);
+  else if (hpw == 1 && wph == 4) hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 1, 4>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 1, 2>), grid, dim3(128), 0, s, a);
+}
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, hipStream_t s) {
   if (head_dim == 128) {
-    if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<128, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<128, false>), grid, block, 0, s, a);
+    if (paged) launch_cfg<128, true>(a, hpw, wph, s);
+    else launch_cfg<128, false>(a, hpw, wph, s);
   } else {
-    if (paged) hipLaunchKernelGGL((prefill_bf16_kernel<64, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((prefill_bf16_kernel<64, false>), grid, block, 0, s, a);
+    if (paged) launch_cfg<64, true>(a, hpw, wph, s);
+    else launch_cfg<64, false>(a, hpw, wph, s);
   }
   return hipGetLastError();
 }
