@@ -140,7 +140,7 @@ ATTN_API int attn_prefill_paged(const void* q, const void* k_cache, const void* 
  *   context_lens device int32 [num_seqs], 1 .. max_context_len (the new
  *                token included)
  *   o            device bf16 [num_seqs][num_q_heads][head_dim], written
- *   partition_size: 0 = automatic, else a multiple of 128.
+ *   partition_size: 0 = automatic, else a multiple of 128, at most 1024.
  *   workspace    device scratch of at least
  *                attn_decode_paged_workspace_size(...) bytes (same arguments)
  * ---------------------------------------------------------------------- */

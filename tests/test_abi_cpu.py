@@ -103,6 +103,7 @@ def decode(lib, **kw):
     (dict(maxb=7), ATTN_E_INVALID),             # 128 tokens need 8 blocks
     (dict(part=100), ATTN_E_INVALID),
     (dict(part=-128), ATTN_E_INVALID),
+    (dict(part=2048), ATTN_E_INVALID),
     (dict(maxctx=0), ATTN_E_INVALID),
     (dict(maxctx=4096, maxb=256, part=128, ws=None), ATTN_E_INVALID),
     (dict(maxctx=4096, maxb=256, part=128, wsb=16), ATTN_E_NOMEM),

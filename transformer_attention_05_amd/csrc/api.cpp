@@ -191,14 +191,16 @@ extern "C" int attn_prefill_paged(const void* q, const void* k_cache, const void
 // ---------------------------------------------------------------------------
 extern "C" int32_t attn_decode_paged_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
                                                     int32_t max_context_len) {
-  // Largest power-of-two partition (128 .. 1024 tokens) that still yields
-  // about 2048 partition workgroups if every sequence were as long as the
-  // longest: enough to fill 256 CUs several times over.
-  int32_t p = 1024;
+  // Largest partition from {768, 512, 384, 256, 128} tokens that still gives
+  // about 512 partition workgroups (two per CU) if every sequence were as
+  // long as the longest.  768 measured best for long mixed contexts; smaller
+  // partitions keep the CUs busy when contexts are short.
+  static const int32_t cand[] = {768, 512, 384, 256, 128};
   const int64_t units = (int64_t)(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
   const int64_t ctx = max_context_len > 0 ? max_context_len : 1;
-  while (p > 128 && units * ((ctx + p - 1) / p) < 2048) p /= 2;
-  return p;
+  for (int32_t p : cand)
+    if (units * ((ctx + p - 1) / p) >= 512) return p;
+  return 128;
 }
 
 namespace {
@@ -250,8 +252,8 @@ extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void*
   if (max_blocks_per_seq < ceil_div(max_context_len, kBlockSizeHost))
     return fail(ATTN_E_INVALID, "%s: max_blocks_per_seq %d cannot hold max_context_len %d", fn,
                 max_blocks_per_seq, max_context_len);
-  if (partition_size < 0 || partition_size % 128 != 0)
-    return fail(ATTN_E_INVALID, "%s: partition_size must be 0 or a positive multiple of 128", fn);
+  if (partition_size < 0 || partition_size % 128 != 0 || partition_size > 1024)
+    return fail(ATTN_E_INVALID, "%s: partition_size must be 0 or a multiple of 128 up to 1024", fn);
   float scale_log2;
   if ((st = check_scale(scale, head_dim, &scale_log2, fn)) != ATTN_OK) return st;
   const void* ptrs[] = {q, k_cache, v_cache, o};
@@ -259,7 +261,6 @@ extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void*
     if (!aligned(p, 16)) return fail(ATTN_E_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
   if (!aligned(block_table, 4) || !aligned(context_lens, 4))
     return fail(ATTN_E_INVALID, "%s: int32 arrays must be 4-byte aligned", fn);
-  if (num_seqs > 65535) return fail(ATTN_E_UNSUPPORTED, "%s: at most 65535 sequences per call", fn);
   DecodeGeom gm = decode_geom(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
   const size_t need = gm.o_bytes + gm.ml_bytes;
   if (need > 0) {
@@ -281,8 +282,8 @@ extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void*
   a.part_size = gm.part; a.max_parts = gm.max_parts;
   a.num_blocks = num_blocks;
   a.scale_log2 = scale_log2;
-  if ((int64_t)num_kv_heads * a.head_groups > 65535)
-    return fail(ATTN_E_UNSUPPORTED, "%s: too many kv heads", fn);
+  if ((int64_t)num_kv_heads * a.head_groups > 65535 || num_seqs > 65535)
+    return fail(ATTN_E_UNSUPPORTED, "%s: at most 65535 sequences (and kv head slices) per call", fn);
   return launched(launch_decode(a, head_dim, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 

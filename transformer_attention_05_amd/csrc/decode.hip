@@ -8,20 +8,24 @@
 // partition statistics are the running max and sum of the online softmax,
 // merged exactly by rescaling each partition with exp(m_p - max m).
 //
-// Partition kernel, workgroup = (partition, kv head [x 16-head slice], seq),
-// 4 wavefronts.  Each wavefront takes pairs of 16-token blocks:
-//   * K block (16 tokens x D, one contiguous 4 KiB run per kv head at D=128)
-//     is loaded straight into the A operand of v_mfma_f32_16x16x32_bf16:
-//     lane l reads token l%16, 8 channels.  The B operand is Q^T of up to 16
-//     query heads of the kv group (GQA: every K/V byte is read once per kv
-//     head, for all its query heads).  S^T lands as lane = head, 4 tokens.
-//   * V blocks are stored token-minor ([D][16]), so the A operand of
-//     O^T += V^T P^T (lane = channel, 4 consecutive tokens from each block of
-//     the pair) is two 8-byte loads, and P goes from the S accumulator to the
-//     B operand without leaving registers.
-//   * the four wavefronts are combined through LDS; a sequence with a single
-//     partition writes its output directly, otherwise (m, l, O) partials go
-//     to the workspace for the merge kernel.
+// Partition kernel: one workgroup of 4 wavefronts per (partition, kv head
+// [x 16-head slice], sequence).  Each wavefront takes every fourth 16-token
+// block of the partition and keeps two blocks' loads in flight while it
+// consumes a third; the block-table entries of the partition come in with one
+// lane-parallel load.  Per block:
+//   * the K block (16 tokens x D, contiguous per kv head) goes straight into
+//     the A operand of v_mfma_f32_16x16x32_bf16 (lane: token l%16, 8
+//     channels); the B operand is Q^T of up to 16 query heads of the kv
+//     group, so every K/V byte is read once for all heads of the group.  S^T
+//     lands as lane = head, 4 consecutive tokens.
+//   * value blocks are token-minor ([D][16]), so the A operand of
+//     O^T += V^T P^T with v_mfma_f32_16x16x16_bf16 (lane: channel, the same
+//     4 tokens) is one 8-byte load, and P passes from the S accumulator to
+//     the B operand without any data movement.
+// The wavefronts are combined through LDS.  A sequence with a single
+// partition writes its output directly; otherwise
+// the (m, l, O) partials go to the workspace and the merge kernel combines
+// them.
 
 #include <math.h>
 
@@ -32,10 +36,36 @@ namespace mi_attn {
 
 namespace {
 
-constexpr int DW = 4;  // wavefronts per workgroup
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+constexpr float kLazyTau = 8.f;  // keep the reference max until a score exceeds it by 2^8
+constexpr int DW = 4;            // wavefronts per partition workgroup
+
+__device__ __forceinline__ f32x4 mfma16k16(v4i16 a, v4i16 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
 
 template <int D>
-__global__ __launch_bounds__(DW * 64) void decode_partition_kernel(const DecodeArgs a) {
+struct BlockRegs {
+  bf16x8 k[D / 32];  // K: token l%16, channels 32c + 8*(l/16) .. +7
+  u32x2 v[D / 16];   // V^T: channel 16dt + l%16, tokens 4*(l/16) .. +3
+};
+
+template <int D>
+__device__ __forceinline__ void load_block(BlockRegs<D>& r, const __bf16* kb, const __bf16* vb) {
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) r.k[c] = *reinterpret_cast<const bf16x8*>(kb + 32 * c);
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) r.v[dt] = *reinterpret_cast<const u32x2*>(vb + 16 * dt * kBlockSize);
+}
+
+// Grid (partition, kv head x head slice, sequence), partitions fastest so a
+// long context's partitions start together.  Workgroups are dealt to the 8
+// XCDs round-robin in dispatch order; the partition dimension is padded to an
+// odd size so that partition p lands on a different XCD for each sequence
+// (with a multiple of 8, short contexts would load only a few XCDs).
+template <int D>
+__global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeArgs a) {
   const int p = blockIdx.x;
   const int s = blockIdx.z;
   // the grid and the block table bound what a malformed length can reach
@@ -50,18 +80,33 @@ __global__ __launch_bounds__(DW * 64) void decode_partition_kernel(const DecodeA
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int col = lane & 15;  // token (K operand) / head (Q operand, S and O columns)
-  const int g4 = lane >> 4;   // 8-element contraction group
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15;  // token (K operand) / head (Q operand, S and O columns) / channel (V operand)
+  const int g4 = lane >> 4;
 
   const int tok_begin = p * a.part_size;
   const int tok_end = min(ctx, tok_begin + a.part_size);
   const int blk_begin = tok_begin >> 4;
   const int blk_end = (tok_end + 15) >> 4;
   const int32_t* bt = a.block_table + (int64_t)s * a.bt_stride;
-
   const __bf16* kc = static_cast<const __bf16*>(a.k_cache);
   const __bf16* vc = static_cast<const __bf16*>(a.v_cache);
+  const int64_t k_lane = (int64_t)col * D + 8 * g4;          // within a K block of one kv head
+  const int64_t v_lane = (int64_t)col * kBlockSize + 4 * g4;  // within a V^T block of one kv head
+
+  // block-table entries of the partition (at most 64 blocks), one per lane
+  const int tab = (blk_begin + lane < blk_end) ? bt[blk_begin + lane] : 0;
+
+  // Block pointers.  Blocks past the partition (prefetched, never consumed)
+  // and table entries outside the pool read block 0, so every load is
+  // unconditional and in bounds.
+  auto block_ptrs = [&](int blk, const __bf16*& kb, const __bf16*& vb) {
+    const int idx = min(blk - blk_begin, 63);
+    const int32_t phys = safe_block(__builtin_amdgcn_readlane(tab, idx), a.num_blocks);
+    const int64_t base = ((int64_t)phys * a.hkv + kvh) * (kBlockSize * D);
+    kb = kc + base + k_lane;
+    vb = vc + base + v_lane;
+  };
 
   // Q^T: lane holds head `col`, channels 32c + 8*g4 .. +7
   bf16x8 qreg[D / 32];
@@ -72,101 +117,99 @@ __global__ __launch_bounds__(DW * 64) void decode_partition_kernel(const DecodeA
       qreg[c] = col < nh ? *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g4) : bf16x8{};
   }
 
+  // the table and Q^T must be in registers before the block pipeline starts:
+  // waiting here keeps the loop's waits to the blocks themselves
+  __builtin_amdgcn_s_waitcnt(0);
+
   const float c2 = a.scale_log2;
+  const float tau_raw = kLazyTau / c2;
   float m_run = -INFINITY;
   float l_run = 0.f;  // this lane's share of the row sum
   f32x4 oacc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = f32x4{};
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  for (int blk = blk_begin + 2 * wave; blk < blk_end; blk += 2 * DW) {
-    int32_t phys[2];
-    bool valid[2];
+  auto consume = [&](BlockRegs<D>& r, int blk) {
+    // S^T = K Q^T (16 tokens x 16 heads)
+    f32x4 sacc = f32x4{};
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      valid[i] = blk + i < blk_end;
-      phys[i] = valid[i] ? bt[blk + i] : 0;
-      if (phys[i] < 0 || phys[i] >= a.num_blocks) valid[i] = false;  // corrupt table: read zeros
-    }
-    // ---- loads
-    bf16x8 kreg[2][D / 32];
-    u32x2 vreg[2][D / 16];
+    for (int c = 0; c < D / 32; ++c) sacc = mfma16(r.k[c], qreg[c], sacc);
+    // tokens past the partition: masked; past the context the cache holds
+    // arbitrary bits (0 * NaN is NaN), so their values are zeroed too
+    const int t0 = blk * 16 + 4 * g4;
+    if (blk * 16 + 16 > tok_end) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const __bf16* kb = kc + (((int64_t)phys[i] * a.hkv + kvh) * kBlockSize + col) * D + 8 * g4;
-      const __bf16* vb = vc + (((int64_t)phys[i] * a.hkv + kvh) * D + col) * kBlockSize + 4 * g4;
+      for (int i = 0; i < 4; ++i)
+        if (t0 + i >= tok_end) sacc[i] = -INFINITY;
+      const int nvalid = tok_end - t0;
 #pragma unroll
-      for (int c = 0; c < D / 32; ++c)
-        kreg[i][c] = valid[i] ? *reinterpret_cast<const bf16x8*>(kb + 32 * c) : bf16x8{};
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-        vreg[i][dt] = valid[i] ? *reinterpret_cast<const u32x2*>(vb + (int64_t)16 * dt * kBlockSize) : u32x2{0, 0};
-    }
-    // ---- S^T = K Q^T, one 16x16 tile per block
-    f32x4 sacc[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      sacc[i] = f32x4{};
-#pragma unroll
-      for (int c = 0; c < D / 32; ++c) sacc[i] = mfma16(kreg[i][c], qreg[c], sacc[i]);
-    }
-    // ---- mask tokens past the partition; zero their V (past the context the
-    // cache holds arbitrary bits, and 0 * NaN would poison the sum)
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t0 = (blk + i) * 16 + 4 * g4;
-      if (t0 + 3 >= tok_end) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (t0 + r >= tok_end) sacc[i][r] = -INFINITY;
-        const int nvalid = tok_end - t0;  // 4-token run of this lane
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          u32x2 w = vreg[i][dt];
-          if (nvalid <= 0) w = u32x2{0, 0};
-          else if (nvalid == 1) w = u32x2{w[0] & 0xffffu, 0};
-          else if (nvalid == 2) w = u32x2{w[0], 0};
-          else if (nvalid == 3) w = u32x2{w[0], w[1] & 0xffffu};
-          vreg[i][dt] = w;
-        }
+      for (int dt = 0; dt < D / 16; ++dt) {
+        u32x2 w = r.v[dt];
+        if (nvalid <= 0) w = u32x2{0, 0};
+        else if (nvalid == 1) w = u32x2{w[0] & 0xffffu, 0};
+        else if (nvalid == 2) w = u32x2{w[0], 0};
+        else if (nvalid == 3) w = u32x2{w[0], w[1] & 0xffffu};
+        r.v[dt] = w;
       }
     }
-    // ---- online softmax over the 32 tokens of the pair (per head = column)
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, sacc[i][r]);
+    float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     tmax = fmaxf(tmax, xor16(tmax));
     tmax = fmaxf(tmax, xor32(tmax));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-    const float mc = m_use * c2;
-    bf16x8 pb;
-    float lsum = 0.f;
+    if (__any(tmax > m_run + tau_raw)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c2);
+      l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const __bf16 pv = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[i][r], c2, -mc)));
-        pb[4 * i + r] = pv;
-        lsum += static_cast<float>(pv);
-      }
-    l_run = fmaf(l_run, alpha, lsum);
-    m_run = m_new;
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      const u32x4 w = {vreg[0][dt][0], vreg[0][dt][1], vreg[1][dt][0], vreg[1][dt][1]};
-      oacc[dt] = mfma16(__builtin_bit_cast(bf16x8, w), pb, oacc[dt] * alpha);
+      for (int dt = 0; dt < D / 16; ++dt) oacc[dt] *= alpha;
+      m_run = m_new;
     }
+    const float mc = (m_run == -INFINITY ? 0.f : m_run) * c2;
+    bf16x4 pb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pb[i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[i], c2, -mc)));
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0], pb[1]}, ones, l_run, false);
+    l_run = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2], pb[3]}, ones, l_run, false);
+    const v4i16 pbi = __builtin_bit_cast(v4i16, pb);
+    // O^T += V^T P^T
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = mfma16k16(__builtin_bit_cast(v4i16, r.v[dt]), pbi, oacc[dt]);
+  };
+
+  // ---- this wavefront's blocks: blk_begin + wave, + DW, ...; three register
+  // buffers keep two blocks in flight while one is consumed
+  // (the scheduling barriers pin the issue order of the load groups, which
+  // the wait counters rely on: loads retire in issue order)
+  BlockRegs<D> r0, r1, r2;
+  const __bf16 *kb, *vb;
+  const int first = blk_begin + wave;
+  block_ptrs(first, kb, vb);
+  load_block<D>(r0, kb, vb);
+  __builtin_amdgcn_sched_barrier(0);
+  block_ptrs(first + DW, kb, vb);
+  load_block<D>(r1, kb, vb);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int blk = first; blk < blk_end; blk += 3 * DW) {
+    block_ptrs(blk + 2 * DW, kb, vb);
+    load_block<D>(r2, kb, vb);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(r0, blk);
+    if (blk + DW >= blk_end) break;
+    block_ptrs(blk + 3 * DW, kb, vb);
+    load_block<D>(r0, kb, vb);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(r1, blk + DW);
+    if (blk + 2 * DW >= blk_end) break;
+    block_ptrs(blk + 4 * DW, kb, vb);
+    load_block<D>(r1, kb, vb);
+    __builtin_amdgcn_sched_barrier(0);
+    consume(r2, blk + 2 * DW);
   }
 
-  // ---- combine the wavefronts
+  // ---- combine the wavefronts (lane holds head `col`, channels 16dt + 4*g4 .. +3)
   __shared__ float sm_m[DW][16];
   __shared__ float sm_l[DW][16];
-  __shared__ float sm_o[DW][D][17];
+  __shared__ f32x4 sm_o[DW][D / 16][4][17];  // [wave][dt][g4][head], padded
   float l_all = l_run + xor16(l_run);
   l_all += xor32(l_all);
   if (g4 == 0) {
@@ -174,33 +217,35 @@ __global__ __launch_bounds__(DW * 64) void decode_partition_kernel(const DecodeA
     sm_l[wave][col] = l_all;
   }
 #pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sm_o[wave][16 * dt + 4 * g4 + r][col] = oacc[dt][r];
+  for (int dt = 0; dt < D / 16; ++dt) sm_o[wave][dt][g4][col] = oacc[dt];
   __syncthreads();
 
+  // thread = (head, 4 channels)
   const bool single = nparts == 1;
-  for (int idx = tid; idx < nh * D; idx += DW * 64) {
-    const int hl = idx / D, d = idx % D;
+  for (int t = tid; t < nh * (D / 4); t += 64 * DW) {
+    const int hl = t / (D / 4), d4 = t % (D / 4);
+    const int dt = d4 >> 2, gg = d4 & 3;
     float mx = -INFINITY;
 #pragma unroll
     for (int w = 0; w < DW; ++w) mx = fmaxf(mx, sm_m[w][hl]);
     const float mu = (mx == -INFINITY) ? 0.f : mx;
-    float lsum = 0.f, osum = 0.f;
+    float lsum = 0.f;
+    f32x4 osum = f32x4{};
 #pragma unroll
     for (int w = 0; w < DW; ++w) {
       const float f = __builtin_amdgcn_exp2f((sm_m[w][hl] - mu) * c2);
       lsum = fmaf(f, sm_l[w][hl], lsum);
-      osum = fmaf(f, sm_o[w][d][hl], osum);
+      osum += f * sm_o[w][dt][gg][hl];
     }
     const int64_t row = (int64_t)s * a.hq + head0 + hl;
     if (single) {
       const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-      static_cast<__bf16*>(a.o)[row * D + d] = static_cast<__bf16>(osum * inv);
+      const u32x2 w2 = {pack_bf16x2(osum[0] * inv, osum[1] * inv), pack_bf16x2(osum[2] * inv, osum[3] * inv)};
+      *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + row * D + 4 * d4) = w2;
     } else {
       const int64_t slot = row * a.max_parts + p;
-      a.ws_o[slot * D + d] = osum;
-      if (d == 0) {
+      *reinterpret_cast<f32x4*>(a.ws_o + slot * D + 4 * d4) = osum;
+      if (d4 == 0) {
         a.ws_ml[slot * 2 + 0] = mx;
         a.ws_ml[slot * 2 + 1] = lsum;
       }
@@ -208,8 +253,9 @@ __global__ __launch_bounds__(DW * 64) void decode_partition_kernel(const DecodeA
   }
 }
 
-// Merge kernel: workgroup = (query head, seq); O = sum_p f_p O_p / sum_p f_p l_p
-// with f_p = exp(m_p - max m).
+// Merge kernel: workgroup = (query head, sequence), thread = channel.
+// O = sum_p f_p O_p / sum_p f_p l_p with f_p = exp(m_p - max m); the
+// partition weights are computed once, in parallel, into LDS.
 template <int D>
 __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeArgs a) {
   const int h = blockIdx.x;
@@ -218,60 +264,59 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeArgs a) {
   const int nparts = (ctx + a.part_size - 1) / a.part_size;
   if (nparts <= 1) return;
   extern __shared__ float sm_w[];  // [max_parts]
-  __shared__ float sm_red[128];
-  __shared__ float sm_scalar[2];
+  __shared__ float sm_red[2][2];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int64_t row = (int64_t)s * a.hq + h;
   const float* ml = a.ws_ml + row * a.max_parts * 2;
   const float c2 = a.scale_log2;
 
   float mx = -INFINITY;
   for (int i = tid; i < nparts; i += 128) mx = fmaxf(mx, ml[2 * i]);
-  sm_red[tid] = mx;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) sm_red[0][wave] = mx;
   __syncthreads();
-  for (int w = 64; w > 0; w >>= 1) {
-    if (tid < w) sm_red[tid] = fmaxf(sm_red[tid], sm_red[tid + w]);
-    __syncthreads();
-  }
-  mx = sm_red[0];
+  mx = fmaxf(sm_red[0][0], sm_red[0][1]);
   const float mu = (mx == -INFINITY) ? 0.f : mx;
-  __syncthreads();
   float lsum = 0.f;
   for (int i = tid; i < nparts; i += 128) {
     const float f = __builtin_amdgcn_exp2f((ml[2 * i] - mu) * c2);
     sm_w[i] = f;
     lsum = fmaf(f, ml[2 * i + 1], lsum);
   }
-  sm_red[tid] = lsum;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
+  if (lane == 0) sm_red[1][wave] = lsum;
   __syncthreads();
-  for (int w = 64; w > 0; w >>= 1) {
-    if (tid < w) sm_red[tid] += sm_red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) sm_scalar[0] = sm_red[0] > 0.f ? 1.f / sm_red[0] : 0.f;
-  __syncthreads();
-  const float inv = sm_scalar[0];
-  const float* po = a.ws_o + row * a.max_parts * D;
-  for (int d = tid; d < D; d += 128) {
-    float acc = 0.f;
-    for (int i = 0; i < nparts; ++i) acc = fmaf(sm_w[i], po[(int64_t)i * D + d], acc);
-    static_cast<__bf16*>(a.o)[row * D + d] = static_cast<__bf16>(acc * inv);
+  lsum = sm_red[1][0] + sm_red[1][1];
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  if (tid < D) {
+    const float* po = a.ws_o + row * a.max_parts * D + tid;
+    float acc0 = 0.f, acc1 = 0.f;
+    int i = 0;
+    for (; i + 1 < nparts; i += 2) {
+      acc0 = fmaf(sm_w[i], po[(int64_t)i * D], acc0);
+      acc1 = fmaf(sm_w[i + 1], po[(int64_t)(i + 1) * D], acc1);
+    }
+    if (i < nparts) acc0 = fmaf(sm_w[i], po[(int64_t)i * D], acc0);
+    static_cast<__bf16*>(a.o)[row * D + tid] = static_cast<__bf16>((acc0 + acc1) * inv);
   }
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t st) {
-  dim3 grid1(a.max_parts, a.hkv * a.head_groups, a.num_seqs);
+  dim3 grid1(a.max_parts | 1, a.hkv * a.head_groups, a.num_seqs);
   dim3 grid2(a.hq, a.num_seqs);
   const size_t merge_smem = sizeof(float) * (size_t)a.max_parts;
   if (head_dim == 128) {
-    hipLaunchKernelGGL(decode_partition_kernel<128>, grid1, dim3(DW * 64), 0, st, a);
+    hipLaunchKernelGGL(decode_partition_kernel<128>, grid1, dim3(64 * DW), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.max_parts > 1) hipLaunchKernelGGL(decode_merge_kernel<128>, grid2, dim3(128), merge_smem, st, a);
   } else {
-    hipLaunchKernelGGL(decode_partition_kernel<64>, grid1, dim3(DW * 64), 0, st, a);
+    hipLaunchKernelGGL(decode_partition_kernel<64>, grid1, dim3(64 * DW), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.max_parts > 1) hipLaunchKernelGGL(decode_merge_kernel<64>, grid2, dim3(128), merge_smem, st, a);
