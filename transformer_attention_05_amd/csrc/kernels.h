@@ -63,7 +63,7 @@ struct RopeWriteArgs {
 
 // Launchers return the launch status (hipSuccess or the error).
 // hpw: query heads sharing each K/V tile (1 or 2); wph: wavefronts of 32
-// queries per head (4, or 2 with hpw 1).  Query tile = 32 * wph rows.
+// queries per head (4 or 2).  Query tile = 32 * wph rows.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s);

@@ -206,18 +206,34 @@ void prefill_bf16_kernel(const PrefillArgs a) {
 
   auto compute_tile = [&](const __bf16* sk, const __bf16* sv, int n0) {
     if (!(wave_has_rows && (!a.causal || n0 <= wq_hi + off))) return;
-    // S^T = K Q^T, two 32-key subtiles
+    // S^T = K Q^T, two 32-key subtiles.  The K operand reads run ahead of
+    // the MFMAs (first subtile's reads, then one read of the second subtile
+    // per MFMA of the first), so the MFMAs issue back to back.
+    constexpr int NC = D / 16;
     f32x16 sacc[2];
+    bf16x8 kop[2][NC];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int r = kt * 32 + lq;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        kop[kt][c] = *reinterpret_cast<const bf16x8*>(sk + r * D + 8 * ((2 * c + hh) ^ k_swz<D>(r)));
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       sacc[kt] = f32x16{};
-      const int r = kt * 32 + lq;
 #pragma unroll
-      for (int c = 0; c < D / 16; ++c) {
-        const bf16x8 kv = *reinterpret_cast<const bf16x8*>(sk + r * D + 8 * ((2 * c + hh) ^ k_swz<D>(r)));
-        sacc[kt] = mfma32(kv, qreg[c], sacc[kt]);
-      }
+      for (int c = 0; c < NC; ++c) sacc[kt] = mfma32(kop[kt][c], qreg[c], sacc[kt]);
     }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+#pragma unroll
+    for (int i = 0; i < NC; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     if ((n0 + BN > tk) || (a.causal && n0 + BN - 1 > wq0 + off)) {
       const int lim = a.causal ? min(tk - 1, qi + off) : tk - 1;
 #pragma unroll
@@ -260,17 +276,18 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
       }
     l_run = lsum;
-    // O^T += V^T P^T; keys of step kc in the accumulator's order
+    // O^T += V^T P^T; keys of step kc in the accumulator's order.  The V^T
+    // operand reads run one channel tile ahead of the MFMAs.
+    u32x4 vop[D / 32][4];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) {
-        u32x4 w;
         if constexpr (PAGED) {
           const int d = dt * 32 + lq;
           const u32x2 lo = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc) ^ vt_swz(d)) + 4 * hh);
           const u32x2 hi = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc + 1) ^ vt_swz(d)) + 4 * hh);
-          w = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          vop[dt][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         } else {
           // transpose read: lane j of each 16-lane group addresses row
           // (key) base + j/4, channels 4*(j%4) .. +3 of its 16-channel slice
@@ -284,11 +301,23 @@ void prefill_bf16_kernel(const PrefillArgs a) {
           const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
           const u32x2 lo = __builtin_bit_cast(u32x2, t0);
           const u32x2 hi = __builtin_bit_cast(u32x2, t1);
-          w = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          vop[dt][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
-        oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, w), pb[kc], oacc[dt]);
       }
     }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, vop[dt][kc]), pb[kc], oacc[dt]);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
+#pragma unroll
+    for (int i = 0; i < 4 * (D / 32) - 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // 2 DS reads
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
   };
 
   // ---- main loop: DMA of tile j+1 overlaps the MFMAs of tile j.  The two
@@ -442,6 +471,7 @@ template <int D, bool PAGED>
 static void launch_cfg(const PrefillArgs& a, int hpw, int wph, hipStream_t s) {
   dim3 grid(a.num_wg);
   if (hpw == 2 && wph == 4) hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 2, 4>), grid, dim3(512), 0, s, a);
+  else if (hpw == 2 && wph == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 2, 2>), grid, dim3(256), 0, s, a);
   else if (hpw == 1 && wph == 4) hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 1, 4>), grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 1, 2>), grid, dim3(128), 0, s, a);
 }
