@@ -34,6 +34,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "prefill attention TFLOP/s + paged-decode KV GB/s on 1 MI355X (% of roofline)"
 PEAK_BF16_FLOPS = 2.5e15
+TRAFFIC_PROBE_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "transformer_attention_05_amd", "csrc", "decode.hip")
 PEAK_HBM = 8.0e12
 HQ, HKV, D, BS = 12, 2, 128, 16
 ELT = 2  # bf16 bytes
@@ -103,6 +106,8 @@ def main():
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--only", choices=["mixed", "prefill", "decode"], default=None,
                     help="run one workload only (for profiling)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="first copy a 256 MiB buffer (known bytes) so hardware byte counters can be scaled")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
@@ -120,6 +125,13 @@ def main():
     mi.load()
     dev = "cuda"
     out = {}
+    if args.traffic_probe:
+        src = torch.empty(TRAFFIC_PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ------------------------------------------------------------------ the step (mixed)
     if args.only in (None, "mixed"):
@@ -245,6 +257,22 @@ def cpu_baseline(case, m):
                        "fp64 NumPy, once")
 
 
+def measured_traffic():
+    """HBM bytes per decode launch from the committed counter profile, or
+    None if the decode source changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        with open(DECODE_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if t.get("decode_src_sha256") != sha:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
 def emit(args, out, cpu):
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
@@ -265,7 +293,7 @@ def emit(args, out, cpu):
         gbps = m["B_dec"] / dec_s / 1e9
         res["roofline"] = {"kernel": "paged decode (decode_partition_kernel + decode_merge_kernel)",
                            "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                           "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": None,
+                           "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": measured_traffic(),
                            "algorithmic_bytes_per_launch": m["B_dec"], "avg_launch_us": round(m["ms_decode"] * 1e3, 2)}
         comps["step_write"] = {"us": round(m["ms_write"] * 1e3, 2), "GB/s": round(m["B_wr"] / (m["ms_write"] / 1e3) / 1e9, 1)}
         comps["step_chunked_prefill"] = {"us": round(m["ms_prefill"] * 1e3, 2),
