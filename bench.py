@@ -146,15 +146,25 @@ def main():
         for _ in range(args.warmup):
             step.run()
         torch.cuda.synchronize()
-        t_wr, t_pre, t_dec = EventTimer(torch), EventTimer(torch), EventTimer(torch)
+        # the timed steps: nothing between the launches (an event recorded
+        # between two kernels leaves the GPU idle for ~10 us on this stack)
         t0 = time.perf_counter()
         for _ in range(args.steps):
-            e = t_wr.start(); step.write(); t_wr.stop(e)
-            e = t_pre.start(); step.prefill(); t_pre.stop(e)
-            e = t_dec.start(); step.decode(); t_dec.stop(e)
+            step.run()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / args.steps
-        ms_wr, ms_pre, ms_dec = t_wr.mean_ms(), t_pre.mean_ms(), t_dec.mean_ms()
+        # per-stage durations: each stage repeated on its own, HIP events on
+        # the stream the kernels are launched on around every call
+        stage_ms = []
+        for fn in (step.write, step.prefill, step.decode):
+            fn()
+            torch.cuda.synchronize()
+            tm = EventTimer(torch)
+            for _ in range(args.steps):
+                e = tm.start(); fn(); tm.stop(e)
+            torch.cuda.synchronize()
+            stage_ms.append(tm.mean_ms())
+        ms_wr, ms_pre, ms_dec = stage_ms
         t_roof = F / PEAK_BF16_FLOPS + (B_dec + B_wr) / PEAK_HBM
         out["mixed"] = dict(wall_s=wall, ms_write=ms_wr, ms_prefill=ms_pre, ms_decode=ms_dec, F=F, B_dec=B_dec,
                             B_wr=B_wr, t_roof=t_roof, n_new=n_new, part=mi.attn_decode_paged_auto_partition(

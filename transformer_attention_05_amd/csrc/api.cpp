@@ -308,11 +308,10 @@ extern "C" int attn_kv_cache_write_rope(void* q, const void* k, const void* v, c
   if (!std::isfinite(rope_base) || rope_base < 0.f || (rope_base > 0.f && rope_base <= 1.f))
     return fail(ATTN_E_INVALID, "%s: rope_base must be 0 (no rotation) or > 1", fn);
   if ((int64_t)num_blocks * kBlockSizeHost > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: pool too large", fn);
-  const uintptr_t el = dtype == ATTN_BF16 ? 2 : 4;
   const void* ptrs[] = {k, v, k_cache, v_cache};
   for (const void* p : ptrs)
-    if (!aligned(p, el)) return fail(ATTN_E_INVALID, "%s: misaligned tensor pointer", fn);
-  if (q && !aligned(q, el)) return fail(ATTN_E_INVALID, "%s: misaligned q", fn);
+    if (!aligned(p, 16)) return fail(ATTN_E_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (q && !aligned(q, 16)) return fail(ATTN_E_INVALID, "%s: q must be 16-byte aligned", fn);
   if (!aligned(positions, 4) || !aligned(slot_mapping, 4))
     return fail(ATTN_E_INVALID, "%s: int32 arrays must be 4-byte aligned", fn);
   if (num_tokens == 0) return ok();
