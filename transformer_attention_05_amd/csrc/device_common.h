@@ -72,12 +72,4 @@ __device__ __forceinline__ int32_t safe_block(int32_t blk, int32_t num_blocks) {
   return (blk >= 0 && blk < num_blocks) ? blk : 0;
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (id i runs on XCD
-// i % 8).  This renumbers them so that each XCD receives a contiguous range
-// of logical ids, which keeps workgroups that share K/V tiles on one L2.
-__device__ __forceinline__ uint32_t xcd_logical_id(uint32_t i, uint32_t n) {
-  const uint32_t q = n / 8, r = n % 8, x = i % 8;
-  return x * q + (x < r ? x : r) + i / 8;
-}
-
 }  // namespace mi_attn

@@ -22,8 +22,10 @@
 //     loads are issued before the current tile's MFMAs.
 //   * causal tiles wholly above the diagonal are never loaded; masking runs
 //     only on tiles that cross the diagonal or the sequence end.
-//   * workgroups are ordered heaviest first (last query tile first) and
-//     renumbered so each XCD receives a contiguous range (K/V sharing in L2).
+//   * workgroups are ordered heaviest first (last query tile first).  The
+//     hardware deals workgroup ids round-robin over the 8 XCDs, so every XCD
+//     receives an equal share of heavy and light tiles; workgroups that start
+//     together walk the same key tiles, so K/V is still shared in each L2.
 //   * P is rounded to bf16 for the PV MFMA and the row sum l accumulates the
 //     same rounded values, so the output weights stay exactly normalised.
 // The paged variant is the same loop with K/V rows gathered through the
@@ -48,6 +50,16 @@ constexpr float kLazyTau = 8.f;     // rescale only when the row max grows by mo
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte global -> LDS DMA of one lane (lane l's bytes land at lds + 16 l).
+// Issued as inline asm so that the compiler does not track the LDS write:
+// completion is ordered by the explicit vmcnt waits before the barriers that
+// publish a tile, and the LDS ring buffers can then live in one array
+// addressed by a uniform buffer offset.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_dst);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
+}
 
 // LDS tiles are unpadded and XOR-swizzled at 16-byte granularity so that
 // the MFMA operand reads are free of bank conflicts.  (row, chunk) is stored
@@ -77,12 +89,11 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   static_assert(LPW * NW == LOADS, "tile DMA must split evenly over the wavefronts");
   constexpr int RPI = 64 / CH;               // rows per DMA instruction
 
-  __shared__ __attribute__((aligned(1024))) __bf16 smk0[BN * D];
-  __shared__ __attribute__((aligned(1024))) __bf16 smk1[BN * D];
-  __shared__ __attribute__((aligned(1024))) __bf16 smv0[BN * D];
-  __shared__ __attribute__((aligned(1024))) __bf16 smv1[BN * D];
+  // LDS: a ring of three K tiles followed by a ring of three V tiles
+  constexpr int TILE = BN * D;
+  __shared__ __attribute__((aligned(1024))) __bf16 sm[6 * TILE];
 
-  const uint32_t id = xcd_logical_id(blockIdx.x, a.num_wg);
+  const uint32_t id = blockIdx.x;
   const int hgroups = a.hq / HPW;
   const uint32_t per_tile = (uint32_t)hgroups * (uint32_t)a.batch;
   const int mt = a.num_m_tiles - 1 - (int)(id / per_tile);
@@ -141,30 +152,54 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     n_tiles = kmax < 0 ? 0 : kmax / BN + 1;
   }
 
-  // ---- global -> LDS DMA of one K/V tile (rows past the keys re-read the
-  // last key: finite values whose weights are masked to zero)
+  // ---- global -> LDS DMA of one K or V tile.  Rows past the keys re-read
+  // the last key: finite values whose weights are masked to zero.  A paged
+  // tile spans four 16-token blocks; their table entries are uniform over the
+  // workgroup and come through scalar loads, so no vector-memory wait is ever
+  // needed to form an address.
   const __bf16* kbase = static_cast<const __bf16*>(a.k);
   const __bf16* vbase = static_cast<const __bf16*>(a.v);
-  auto key_row = [&](const __bf16* base, int64_t sb, int64_t st, int64_t sh, int key) -> const __bf16* {
-    if constexpr (PAGED) {
-      const int32_t blk = safe_block(bt_row[key >> 4], a.num_blocks);
-      return base + (((int64_t)blk * a.hkv + g) * kBlockSize + (key & 15)) * D;
-    } else {
-      return base + b * sb + (int64_t)key * st + g * sh;
-    }
+  typedef __attribute__((address_space(4))) const int32_t const_i32;
+  auto tile_blocks = [&](int n0, int32_t (&blk)[4]) {
+    const int last = (tk - 1) >> 4;
+    const const_i32* row = (const const_i32*)bt_row;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) blk[i] = safe_block(row[min((n0 >> 4) + i, last)], a.num_blocks);
   };
-  auto issue_tile = [&](__bf16* dk, __bf16* dv, int n0) {
+  auto pick4 = [](const int32_t (&blk)[4], int i) -> int32_t {
+    return i == 0 ? blk[0] : i == 1 ? blk[1] : i == 2 ? blk[2] : blk[3];
+  };
+  auto issue_k = [&](__bf16* dk, int t) {
+    const int n0 = t * BN;
+    int32_t blk[4];
+    if constexpr (PAGED) tile_blocks(n0, blk);
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int ii = wave * LPW + i;
       const int r = ii * RPI + lane / CH;
-      const int slot = lane % CH;
       const int key = min(n0 + r, tk - 1);
-      const __bf16* ksrc = key_row(kbase, a.ks_b, a.ks_t, a.ks_h, key) + 8 * (slot ^ k_swz<D>(r));
-      __builtin_amdgcn_global_load_lds(ksrc, (lds_void*)(dk + ii * 512), 16, 0, 0);
+      const __bf16* src;
+      if constexpr (PAGED) {
+        const int32_t bk = pick4(blk, (key >> 4) - (n0 >> 4));
+        src = kbase + (((int64_t)bk * a.hkv + g) * kBlockSize + (key & 15)) * D;
+      } else {
+        src = kbase + b * a.ks_b + (int64_t)key * a.ks_t + g * a.ks_h;
+      }
+      dma16(src + 8 * ((lane % CH) ^ k_swz<D>(r)), dk + ii * 512);
+    }
+  };
+  auto issue_v = [&](__bf16* dv, int t) {
+    const int n0 = t * BN;
+    int32_t blk[4];
+    if constexpr (PAGED) tile_blocks(n0, blk);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int ii = wave * LPW + i;
       if constexpr (!PAGED) {
-        const __bf16* vsrc = key_row(vbase, a.vs_b, a.vs_t, a.vs_h, key) + 8 * (slot ^ v_swz<D>(r));
-        __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(dv + ii * 512), 16, 0, 0);
+        const int r = ii * RPI + lane / CH;
+        const int key = min(n0 + r, tk - 1);
+        const __bf16* src = vbase + b * a.vs_b + (int64_t)key * a.vs_t + g * a.vs_h;
+        dma16(src + 8 * ((lane % CH) ^ v_swz<D>(r)), dv + ii * 512);
       } else {
         // V^T tile: row d holds the tile's 64 keys (8 chunks of 8 tokens),
         // read straight from the token-minor value blocks
@@ -172,85 +207,183 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         const int c = (lane % 8) ^ vt_swz(d);
         int tok0 = n0 + 8 * c;
         if (tok0 >= tk) tok0 = ((tk - 1) >> 3) << 3;
-        const int32_t blk = safe_block(bt_row[tok0 >> 4], a.num_blocks);
-        const __bf16* vsrc = vbase + (((int64_t)blk * a.hkv + g) * D + d) * kBlockSize + (tok0 & 8);
-        __builtin_amdgcn_global_load_lds(vsrc, (lds_void*)(dv + ii * 512), 16, 0, 0);
+        const int32_t bk = pick4(blk, (tok0 >> 4) - (n0 >> 4));
+        const __bf16* src = vbase + (((int64_t)bk * a.hkv + g) * D + d) * kBlockSize + (tok0 & 8);
+        dma16(src, dv + ii * 512);
       }
     }
   };
   // Paged V^T: past the context a block holds arbitrary bits and 0 * NaN is
   // NaN, so the tokens of the last tile beyond the context are zeroed.
-  auto zero_tail = [&](__bf16* dv, int n0) {
-    if constexpr (PAGED) {
-      const int nz = n0 + BN - tk;
-      if (nz > 0) {
-        for (int e = tid; e < D * nz; e += 64 * NW) {
-          const int d = e / nz, kl = BN - nz + e % nz;
-          dv[d * BN + 8 * ((kl >> 3) ^ vt_swz(d)) + (kl & 7)] = __bf16{};
-        }
-      }
+  auto zero_tail = [&](__bf16* dv, int t) {
+    const int nz = (t + 1) * BN - tk;
+    for (int e = tid; e < D * nz; e += 64 * NW) {
+      const int d = e / nz, kl = BN - nz + e % nz;
+      dv[d * BN + 8 * ((kl >> 3) ^ vt_swz(d)) + (kl & 7)] = __bf16{};
     }
   };
+  auto tail_tile = [&](int t) { return PAGED && t == n_tiles - 1 && (t + 1) * BN > tk; };
 
   const float c2 = a.scale_log2;
   const float tau_raw = kLazyTau / c2;
   float m_run = -INFINITY;  // running max of raw scores (the one the weights are relative to)
+  float mc = 0.f;           // m_run * c2 (0 while m_run is -inf)
   float l_run = 0.f;        // this lane's half of the row sum
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
-
-  const int wq_hi = min(wq0 + 31, tq - 1);
-  const bool wave_has_rows = wq0 < tq;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  bf16x8 pb[4];  // P of the current tile, B operand of the PV MFMAs
 
-  auto compute_tile = [&](const __bf16* sk, const __bf16* sv, int n0) {
-    if (!(wave_has_rows && (!a.causal || n0 <= wq_hi + off))) return;
-    // S^T = K Q^T, two 32-key subtiles.  The K operand reads run ahead of
-    // the MFMAs (first subtile's reads, then one read of the second subtile
-    // per MFMA of the first), so the MFMAs issue back to back.
-    constexpr int NC = D / 16;
-    f32x16 sacc[2];
-    bf16x8 kop[2][NC];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      const int r = kt * 32 + lq;
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-        kop[kt][c] = *reinterpret_cast<const bf16x8*>(sk + r * D + 8 * ((2 * c + hh) ^ k_swz<D>(r)));
+  constexpr int NC = D / 16;        // contraction steps of S (16 channels each)
+  constexpr int NS = 2 * NC;        // S MFMAs per tile
+  constexpr int NP = 4 * (D / 32);  // PV MFMAs per tile
+  constexpr int EXP_VALU = 96;      // 32 x (fma + exp) + 16 cvt + 16 dot2 per lane per tile
+  constexpr int VPS = EXP_VALU / NS;
+
+  // K operand of S^T = K Q^T: row kt*32 + lq, channels 16c + 8hh .. +7
+  auto k_op = [&](const __bf16* sk, int kt, int c) -> bf16x8 {
+    const int r = kt * 32 + lq;
+    return *reinterpret_cast<const bf16x8*>(sk + r * D + 8 * ((2 * c + hh) ^ k_swz<D>(r)));
+  };
+  // V^T operand of O^T += V^T P^T for channel tile dt and key step kc, keys
+  // in the order the S accumulator hands P over
+  auto v_op = [&](const __bf16* sv, int dt, int kc) -> bf16x8 {
+    if constexpr (PAGED) {
+      const int d = dt * 32 + lq;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc) ^ vt_swz(d)) + 4 * hh);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc + 1) ^ vt_swz(d)) + 4 * hh);
+      return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    } else {
+      // transpose read: lane j of each 16-lane group addresses row (key)
+      // base + j/4, channels 4*(j%4) .. +3 of its 16-channel slice
+      const int grp = lane >> 4, j = lane & 15;
+      const int dch = dt * 32 + 16 * (grp & 1) + 4 * (j & 3);
+      const int r0 = 16 * kc + 4 * hh + (j >> 2);
+      const int r1 = r0 + 8;
+      const __bf16* p0 = sv + r0 * D + 8 * ((dch >> 3) ^ v_swz<D>(r0)) + (dch & 4);
+      const __bf16* p1 = sv + r1 * D + 8 * ((dch >> 3) ^ v_swz<D>(r1)) + (dch & 4);
+      const u32x2 lo = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0));
+      const u32x2 hi = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1));
+      return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
+  };
+
+  // S^T for one tile (two 32-key subtiles, MFMAs alternate between them);
+  // used once, before the pipeline starts
+  auto s_mfma = [&](const __bf16* sk, f32x16 (&s)[2]) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      sacc[kt] = f32x16{};
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) sacc[kt] = mfma32(kop[kt][c], qreg[c], sacc[kt]);
+      for (int kt = 0; kt < 2; ++kt) s[kt] = mfma32(k_op(sk, kt, c), qreg[c], c == 0 ? f32x16{} : s[kt]);
+  };
+  // P = 2^(S c2 - m c2) for half h of key step kc, rounded to bf16, and
+  // the row sum of exactly those rounded weights
+  auto exp_half = [&](const f32x16 (&s)[2], int kc, int h, float& lsum) {
+#pragma unroll
+    for (int i = 4 * h; i < 4 * h + 4; ++i)
+      pb[kc][i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], c2, -mc)));
+#pragma unroll
+    for (int i = 2 * h; i < 2 * h + 2; ++i) {
+      const bf16x2 pr = {pb[kc][2 * i], pb[kc][2 * i + 1]};
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
     }
+  };
+  // Phase A: S(next) = K Q^T on the matrix cores while the VALU forms P
+  // from S(cur).  Eight chunks; each issues NS/8 MFMAs, reads the K operands
+  // of the next chunk and does half a key step of the exponentials.
+  // sched_barrier(0) between chunks keeps the operand registers bounded.
+  constexpr int SPC = NS / 8;  // S MFMAs per chunk
+  auto phase_a = [&](const __bf16* sk, const f32x16 (&s)[2], f32x16 (&sn)[2]) {
+    float lsum = l_run;
+    bf16x8 kcur[SPC], knxt[SPC];
 #pragma unroll
-    for (int i = 0; i < NC; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    for (int u = 0; u < SPC; ++u) kcur[u] = k_op(sk, u & 1, u >> 1);
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
+    for (int q = 0; q < 8; ++q) {
+      if (q < 7) {
 #pragma unroll
-    for (int i = 0; i < NC; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if ((n0 + BN > tk) || (a.causal && n0 + BN - 1 > wq0 + off)) {
-      const int lim = a.causal ? min(tk - 1, qi + off) : tk - 1;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > lim) sacc[kt][r] = -INFINITY;
+        for (int u = 0; u < SPC; ++u) {
+          const int m = (q + 1) * SPC + u;
+          knxt[u] = k_op(sk, m & 1, m >> 1);
         }
+      }
+#pragma unroll
+      for (int u = 0; u < SPC; ++u) {
+        const int m = q * SPC + u;
+        const int c = m >> 1, kt = m & 1;
+        sn[kt] = mfma32(kcur[u], qreg[c], c == 0 ? f32x16{} : sn[kt]);
+      }
+      exp_half(s, q >> 1, q & 1, lsum);
+      // keep the exponentials in this chunk: without a use here, code motion
+      // above the scheduler sinks them to the PV product that consumes them
+      if (q & 1) asm volatile("" : "+v"(pb[q >> 1]));
+      asm volatile("" : "+v"(lsum));
+#pragma unroll
+      for (int u = 0; u < SPC; ++u) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (q < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (next chunk)
+        __builtin_amdgcn_sched_group_barrier(0x002, 12 / SPC, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (q < 7) {
+#pragma unroll
+        for (int u = 0; u < SPC; ++u) kcur[u] = knxt[u];
+      }
     }
-    // online softmax; the reference max moves only when it grows by > 2^8
+    l_run = lsum;
+  };
+  // Phase B: O^T += V^T P^T, one key step per chunk, V^T operands read a
+  // chunk ahead; the VALU takes the row max of S(next) meanwhile.
+  constexpr int DT = D / 32;
+  auto phase_b = [&](const __bf16* sv, const f32x16 (&sn)[2], float& tmax) {
+    bf16x8 vcur[DT], vnxt[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vcur[dt] = v_op(sv, dt, 0);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+      if (kc < 3) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vnxt[dt] = v_op(sv, dt, kc + 1);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(vcur[dt], pb[kc], oacc[dt]);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, sn[kc >> 1][8 * (kc & 1) + r]);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        if (kc < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // DS reads (next chunk)
+        __builtin_amdgcn_sched_group_barrier(0x002, 1, 1);  // VALU
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kc < 3) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vcur[dt] = vnxt[dt];
+      }
+    }
+  };
+  auto needs_mask = [&](int t) { return (t + 1) * BN > tk || (a.causal && (t + 1) * BN - 1 > wq0 + off); };
+  auto mask_tile = [&](f32x16 (&s)[2], int t) {
+    const int lim = a.causal ? min(tk - 1, qi + off) : tk - 1;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t * BN + kt * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key > lim) s[kt][r] = -INFINITY;
+      }
+  };
+  auto row_max = [&](const f32x16 (&s)[2]) -> float {
     float tmax = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[kt][r]);
-    tmax = fmaxf(tmax, xor32(tmax));
+      for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[kt][r]);
+    return fmaxf(tmax, xor32(tmax));
+  };
+  // online softmax: the reference max moves only when it grows by > 2^8
+  auto update_max = [&](float tmax) {
     if (__any(tmax > m_run + tau_raw)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c2);
@@ -258,97 +391,70 @@ void prefill_bf16_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
+      mc = (m_run == -INFINITY ? 0.f : m_run) * c2;
     }
-    const float mc = (m_run == -INFINITY ? 0.f : m_run) * c2;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pb[kc][i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(sacc[kc >> 1][8 * (kc & 1) + i], c2, -mc)));
-    // row sum of exactly the bf16 weights that enter the PV product
-    float lsum = l_run;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16x2 pr = {pb[kc][2 * i], pb[kc][2 * i + 1]};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
-      }
-    l_run = lsum;
-    // O^T += V^T P^T; keys of step kc in the accumulator's order.  The V^T
-    // operand reads run one channel tile ahead of the MFMAs.
-    u32x4 vop[D / 32][4];
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-        if constexpr (PAGED) {
-          const int d = dt * 32 + lq;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc) ^ vt_swz(d)) + 4 * hh);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc + 1) ^ vt_swz(d)) + 4 * hh);
-          vop[dt][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        } else {
-          // transpose read: lane j of each 16-lane group addresses row
-          // (key) base + j/4, channels 4*(j%4) .. +3 of its 16-channel slice
-          const int grp = lane >> 4, j = lane & 15;
-          const int dch = dt * 32 + 16 * (grp & 1) + 4 * (j & 3);  // first channel of the 8-byte piece
-          const int r0 = 16 * kc + 4 * hh + (j >> 2);
-          const int r1 = r0 + 8;
-          const __bf16* p0 = sv + r0 * D + 8 * ((dch >> 3) ^ v_swz<D>(r0)) + (dch & 4);
-          const __bf16* p1 = sv + r1 * D + 8 * ((dch >> 3) ^ v_swz<D>(r1)) + (dch & 4);
-          const v4i16 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
-          const v4i16 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
-          const u32x2 lo = __builtin_bit_cast(u32x2, t0);
-          const u32x2 hi = __builtin_bit_cast(u32x2, t1);
-          vop[dt][kc] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
-      }
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) oacc[dt] = mfma32(__builtin_bit_cast(bf16x8, vop[dt][kc]), pb[kc], oacc[dt]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // DS read
-#pragma unroll
-    for (int i = 0; i < 4 * (D / 32) - 4; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // 2 DS reads
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+  };
+  auto tile_barrier = [&]() {
+    // s_waitcnt vmcnt(2*LPW) (expcnt and lgkmcnt fields at their no-wait maximum)
+    __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * LPW) & 15) | (((2 * LPW) >> 4) << 14));
+    __syncthreads();
   };
 
-  // ---- main loop: DMA of tile j+1 overlaps the MFMAs of tile j.  The two
-  // buffers are separate LDS objects and the loop is unrolled by two, so the
-  // DMA into one buffer never forces a wait before reading the other.
+  // ---- software pipeline.  Iteration j: S(j+1) = K(j+1) Q^T on the matrix
+  // cores while the VALU turns S(j) into P(j); then O += V(j)^T P(j) while
+  // the VALU takes the row max of S(j+1).  Tile t of K (of V) lives in ring
+  // buffer t % 3; the DMA issued in iteration j (K(j+3), V(j+2)) has two
+  // iterations to land.  Every iteration issues the same number of DMA
+  // instructions (the tile index is clamped), so one vmcnt covers them.
+  __bf16* const kring = sm;
+  __bf16* const vring = sm + 3 * TILE;
+  f32x16 sa[2], sb[2];
   if (n_tiles > 0) {
-    issue_tile(smk0, smv0, 0);
+    issue_k(kring, 0);
+    issue_v(vring, 0);
+    issue_k(kring + TILE, min(1, n_tiles - 1));
+    issue_v(vring + TILE, min(1, n_tiles - 1));
+    issue_k(kring + 2 * TILE, min(2, n_tiles - 1));
     __builtin_amdgcn_s_waitcnt(0);   // also retires the Q loads
     __syncthreads();
-    zero_tail(smv0, 0);
-    if (PAGED && BN > tk) __syncthreads();
+    if (tail_tile(0)) zero_tail(vring, 0);
+    s_mfma(kring, sa);
+    if (needs_mask(0)) mask_tile(sa, 0);
+    update_max(row_max(sa));
+    __syncthreads();
   }
-  for (int j = 0; j < n_tiles; j += 2) {
-    const int n0 = j * BN;
-    if (j + 1 < n_tiles) issue_tile(smk1, smv1, n0 + BN);
-    compute_tile(smk0, smv0, n0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (j + 1 >= n_tiles) break;
-    if (PAGED && n0 + 2 * BN > tk) {
-      zero_tail(smv1, n0 + BN);
+  // Iteration j.  The last iteration also computes S for tile n_tiles: its
+  // K buffer holds a re-read of the last tile and every score of it is
+  // masked (its keys lie past the last key any row of the workgroup may
+  // see), so it changes nothing and the loop body has a single form.
+  // r0, r1, r2 = j % 3, (j + 1) % 3, (j + 2) % 3.
+  int r0 = 0, r1 = 1, r2 = 2;
+  auto iteration = [&](int j, const f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    issue_k(kring + r0 * TILE, min(j + 3, n_tiles - 1));
+    issue_v(vring + r2 * TILE, min(j + 2, n_tiles - 1));
+    phase_a(kring + r1 * TILE, sc, sn);
+    if (needs_mask(j + 1)) mask_tile(sn, j + 1);
+    float tmax = -INFINITY;
+    phase_b(vring + r0 * TILE, sn, tmax);
+    update_max(fmaxf(tmax, xor32(tmax)));
+    tile_barrier();
+    if (tail_tile(j + 1)) {
+      zero_tail(vring + r1 * TILE, j + 1);
       __syncthreads();
     }
-    if (j + 2 < n_tiles) issue_tile(smk0, smv0, n0 + 2 * BN);
-    compute_tile(smk1, smv1, n0 + BN);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (PAGED && j + 2 < n_tiles && n0 + 3 * BN > tk) {
-      zero_tail(smv0, n0 + 2 * BN);
-      __syncthreads();
+    const int t = r0;
+    r0 = r1;
+    r1 = r2;
+    r2 = t;
+  };
+  if (n_tiles > 0) {
+    for (int j = 0; j < n_tiles; j += 2) {
+      iteration(j, sa, sb);
+      if (j + 1 >= n_tiles) break;
+      iteration(j + 1, sb, sa);
     }
+    // no DMA may still be writing this workgroup's LDS when it exits
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   // ---- epilogue: O = O / l, optional LSE (natural log)
@@ -371,7 +477,6 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     }
   }
 }
-
 // ---------------------------------------------------------------------------
 // f32 VALU kernel: LPQ = D / 64 lanes per query, each holding 64 channels.
 template <int D>
