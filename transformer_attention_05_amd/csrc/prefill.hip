@@ -122,7 +122,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: lets wave-derived values live in SGPRs
   const int hh = lane >> 5;
   const int lq = lane & 31;
   const int h = h0 + wave / WPH;
@@ -160,56 +160,85 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   const __bf16* kbase = static_cast<const __bf16*>(a.k);
   const __bf16* vbase = static_cast<const __bf16*>(a.v);
   typedef __attribute__((address_space(4))) const int32_t const_i32;
-  auto tile_blocks = [&](int n0, int32_t (&blk)[4]) {
-    const int last = (tk - 1) >> 4;
-    const const_i32* row = (const const_i32*)bt_row;
+  auto tile_blocks = [&](int t, int32_t (&blk)[4]) {
+    if constexpr (PAGED) {
+      const int last = (tk - 1) >> 4;
+      const const_i32* row = (const const_i32*)bt_row;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) blk[i] = safe_block(row[min((n0 >> 4) + i, last)], a.num_blocks);
-  };
-  auto pick4 = [](const int32_t (&blk)[4], int i) -> int32_t {
-    return i == 0 ? blk[0] : i == 1 ? blk[1] : i == 2 ? blk[2] : blk[3];
-  };
-  auto issue_k = [&](__bf16* dk, int t) {
-    const int n0 = t * BN;
-    int32_t blk[4];
-    if constexpr (PAGED) tile_blocks(n0, blk);
-#pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int ii = wave * LPW + i;
-      const int r = ii * RPI + lane / CH;
-      const int key = min(n0 + r, tk - 1);
-      const __bf16* src;
-      if constexpr (PAGED) {
-        const int32_t bk = pick4(blk, (key >> 4) - (n0 >> 4));
-        src = kbase + (((int64_t)bk * a.hkv + g) * kBlockSize + (key & 15)) * D;
-      } else {
-        src = kbase + b * a.ks_b + (int64_t)key * a.ks_t + g * a.ks_h;
-      }
-      dma16(src + 8 * ((lane % CH) ^ k_swz<D>(r)), dk + ii * 512);
+      for (int i = 0; i < 4; ++i) blk[i] = safe_block(row[min(4 * t + i, last)], a.num_blocks);
     }
   };
-  auto issue_v = [&](__bf16* dv, int t) {
-    const int n0 = t * BN;
-    int32_t blk[4];
-    if constexpr (PAGED) tile_blocks(n0, blk);
+  // one of the four block entries by a per-lane index (selects, no branches)
+  auto pick4 = [](const int32_t (&blk)[4], int i) -> int32_t {
+    const int32_t lo = (i & 1) ? blk[1] : blk[0];
+    const int32_t hi = (i & 1) ? blk[3] : blk[2];
+    return (i & 2) ? hi : lo;
+  };
+  // contiguous layout: lane source of DMA slot i for key row r of tile 0;
+  // a whole tile in range is that plus a uniform offset
+  const __bf16* ksrc0[LPW];
+  const __bf16* vsrc0[LPW];
+  if constexpr (!PAGED) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
-      const int ii = wave * LPW + i;
-      if constexpr (!PAGED) {
+      const int r = (wave * LPW + i) * RPI + lane / CH;
+      ksrc0[i] = kbase + b * a.ks_b + g * a.ks_h + (int64_t)r * a.ks_t + 8 * ((lane % CH) ^ k_swz<D>(r));
+      vsrc0[i] = vbase + b * a.vs_b + g * a.vs_h + (int64_t)r * a.vs_t + 8 * ((lane % CH) ^ v_swz<D>(r));
+    }
+  }
+  // Paged rows past the context read a valid slot of the last block (the
+  // table entries are clamped to it); their scores are masked and their
+  // values zeroed, so only the address has to stay inside the pool.
+  auto issue_k = [&](__bf16* dk, int t, const int32_t (&blk)[4]) {
+    const int n0 = t * BN;
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int ii = wave * LPW + i;
+        const int r = ii * RPI + lane / CH;  // the RPI rows of one DMA share a block
+        const int32_t bk = pick4(blk, (ii * RPI) >> 4);
+        dma16(kbase + (((int64_t)bk * a.hkv + g) * kBlockSize + (r & 15)) * D + 8 * ((lane % CH) ^ k_swz<D>(r)),
+              dk + ii * 512);
+      }
+    } else if (n0 + BN <= tk) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) dma16(ksrc0[i] + (int64_t)n0 * a.ks_t, dk + (wave * LPW + i) * 512);
+    } else {
+      // last partial tile: rows past the keys re-read the last key
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int ii = wave * LPW + i;
         const int r = ii * RPI + lane / CH;
         const int key = min(n0 + r, tk - 1);
-        const __bf16* src = vbase + b * a.vs_b + (int64_t)key * a.vs_t + g * a.vs_h;
-        dma16(src + 8 * ((lane % CH) ^ v_swz<D>(r)), dv + ii * 512);
-      } else {
-        // V^T tile: row d holds the tile's 64 keys (8 chunks of 8 tokens),
-        // read straight from the token-minor value blocks
+        dma16(kbase + b * a.ks_b + (int64_t)key * a.ks_t + g * a.ks_h + 8 * ((lane % CH) ^ k_swz<D>(r)),
+              dk + ii * 512);
+      }
+    }
+  };
+  auto issue_v = [&](__bf16* dv, int t, const int32_t (&blk)[4]) {
+    const int n0 = t * BN;
+    if constexpr (PAGED) {
+      // V^T tile: row d holds the tile's 64 keys (8 chunks of 8 tokens),
+      // read straight from the token-minor value blocks
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int ii = wave * LPW + i;
         const int d = ii * 8 + lane / 8;
         const int c = (lane % 8) ^ vt_swz(d);
-        int tok0 = n0 + 8 * c;
-        if (tok0 >= tk) tok0 = ((tk - 1) >> 3) << 3;
-        const int32_t bk = pick4(blk, (tok0 >> 4) - (n0 >> 4));
-        const __bf16* src = vbase + (((int64_t)bk * a.hkv + g) * D + d) * kBlockSize + (tok0 & 8);
-        dma16(src, dv + ii * 512);
+        const int32_t bk = pick4(blk, c >> 1);
+        dma16(vbase + (((int64_t)bk * a.hkv + g) * D + d) * kBlockSize + 8 * (c & 1), dv + ii * 512);
+      }
+    } else if (n0 + BN <= tk) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) dma16(vsrc0[i] + (int64_t)n0 * a.vs_t, dv + (wave * LPW + i) * 512);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int ii = wave * LPW + i;
+        const int r = ii * RPI + lane / CH;
+        const int key = min(n0 + r, tk - 1);
+        dma16(vbase + b * a.vs_b + (int64_t)key * a.vs_t + g * a.vs_h + 8 * ((lane % CH) ^ v_swz<D>(r)),
+              dv + ii * 512);
       }
     }
   };
@@ -409,12 +438,23 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   __bf16* const kring = sm;
   __bf16* const vring = sm + 3 * TILE;
   f32x16 sa[2], sb[2];
+  // paged: block-table entries of the K tile and the V tile the next
+  // iteration loads (the V tile of one iteration is the K tile of the one
+  // before, and the K entries are fetched an iteration ahead)
+  int32_t blk_k[4], blk_v[4];
   if (n_tiles > 0) {
-    issue_k(kring, 0);
-    issue_v(vring, 0);
-    issue_k(kring + TILE, min(1, n_tiles - 1));
-    issue_v(vring + TILE, min(1, n_tiles - 1));
-    issue_k(kring + 2 * TILE, min(2, n_tiles - 1));
+    {
+      int32_t b0[4], b1[4];
+      tile_blocks(0, b0);
+      tile_blocks(min(1, n_tiles - 1), b1);
+      tile_blocks(min(2, n_tiles - 1), blk_v);
+      tile_blocks(min(3, n_tiles - 1), blk_k);
+      issue_k(kring, 0, b0);
+      issue_v(vring, 0, b0);
+      issue_k(kring + TILE, min(1, n_tiles - 1), b1);
+      issue_v(vring + TILE, min(1, n_tiles - 1), b1);
+      issue_k(kring + 2 * TILE, min(2, n_tiles - 1), blk_v);
+    }
     __builtin_amdgcn_s_waitcnt(0);   // also retires the Q loads
     __syncthreads();
     if (tail_tile(0)) zero_tail(vring, 0);
@@ -430,8 +470,13 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // r0, r1, r2 = j % 3, (j + 1) % 3, (j + 2) % 3.
   int r0 = 0, r1 = 1, r2 = 2;
   auto iteration = [&](int j, const f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    issue_k(kring + r0 * TILE, min(j + 3, n_tiles - 1));
-    issue_v(vring + r2 * TILE, min(j + 2, n_tiles - 1));
+    issue_k(kring + r0 * TILE, min(j + 3, n_tiles - 1), blk_k);
+    issue_v(vring + r2 * TILE, min(j + 2, n_tiles - 1), blk_v);
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) blk_v[i] = blk_k[i];
+      tile_blocks(min(j + 4, n_tiles - 1), blk_k);
+    }
     phase_a(kring + r1 * TILE, sc, sn);
     if (needs_mask(j + 1)) mask_tile(sn, j + 1);
     float tmax = -INFINITY;
