@@ -1,7 +1,10 @@
 """One serving step over a shared paged cache: fused RoPE + cache write for
 every new token, chunked prefill for the prefill requests, decode for the
-decode sequences (partition pass + merge).  Four kernel launches on one
-stream with no host synchronisation in between.
+decode sequences (partition pass + merge).  Four kernel launches with no host
+synchronisation in between.  The chunked prefill (bound by the matrix cores)
+and the decode (bound by HBM) depend only on the cache write, not on each
+other, so with ``concurrent`` the decode runs on a second stream beside the
+prefill and the caller's stream waits for both.
 
 The host side (block pool, block tables, slot mapping) is built once in
 ``__init__``; ``run()`` only enqueues the launches, so the same buffers can be
@@ -26,8 +29,9 @@ class MixedStep:
     ``case.tables`` and ``case.slots`` through the pool.
     """
 
-    def __init__(self, case, assign, device="cuda", partition_size=0, scatter=None):
+    def __init__(self, case, assign, device="cuda", partition_size=0, scatter=None, concurrent=True):
         self.case = case
+        self.concurrent = concurrent
         self.device = device
         self.pool = Pool(case.num_blocks)
         assign(case, self.pool)
@@ -58,6 +62,9 @@ class MixedStep:
         self.o_decode = torch.empty(S, case.hq, d, dtype=dt, device=device)
         need = attn_decode_paged_workspace_size(S, case.hq, hkv, d, self.max_dec_ctx, partition_size)
         self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        # side stream (default priority) and the event that orders it after the write
+        self.side = torch.cuda.Stream(device=device)
+        self.written = torch.cuda.Event()
 
     def write(self):
         attn_kv_cache_write_rope(self.q, self.k, self.v, self.positions, self.slots, self.k_cache, self.v_cache,
@@ -77,6 +84,15 @@ class MixedStep:
 
     def run(self):
         self.write()
+        if self.concurrent and self.R and self.S:
+            main = torch.cuda.current_stream()
+            self.written.record(main)
+            self.side.wait_event(self.written)
+            with torch.cuda.stream(self.side):
+                self.decode()
+            self.prefill()
+            main.wait_stream(self.side)
+            return
         if self.R:
             self.prefill()
         if self.S:
