@@ -68,14 +68,20 @@ struct PrefillTile {
   int hpw, wph;
 };
 
-PrefillTile prefill_tile(int64_t max_q, int32_t hq, int32_t group, int64_t batch) {
+PrefillTile prefill_tile(int64_t max_q, int32_t hq, int32_t group, int64_t batch, bool paged) {
   const int hpw = (group % 2 == 0) ? 2 : 1;
-  PrefillTile t{hpw, 4};
+  // measured on MI355X.  Contiguous: 4-wavefront tiles (2 heads x 64 queries,
+  // or 1 x 128) hold 80 KiB of LDS, so two workgroups share a CU and their
+  // phases drift apart: one's matrix work overlaps the other's softmax; this
+  // beats the 8-wavefront tile at every size measured.  Paged: the 8-wavefront
+  // 2 x 128 tile (it halves the K/V gathers per query) down to ~128
+  // workgroups, then 64-query tiles to keep more CUs busy.
+  PrefillTile t{hpw, hpw == 2 ? 2 : 4};
   auto wgs = [&](const PrefillTile& c) { return ((max_q + 32 * c.wph - 1) / (32 * c.wph)) * (hq / c.hpw) * batch; };
-  // measured on MI355X: a 128-query tile over two heads stays the fastest
-  // down to ~128 workgroups (it halves the K/V tile traffic per query); below
-  // that, 64-query tiles keep more CUs busy
-  if (wgs(t) < 128) t.wph = 2;
+  if (paged) {
+    t = PrefillTile{hpw, 4};
+    if (wgs(t) < 128) t.wph = 2;
+  }
   static const char* env = std::getenv("MI_ATTN_PREFILL_TILE");
   if (env) {
     int h = 0, w = 0;
@@ -131,7 +137,7 @@ extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o
   a.scale_log2 = scale_log2;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16) {
-    const PrefillTile t = prefill_tile(seqlen_q, num_q_heads, a.group, batch);
+    const PrefillTile t = prefill_tile(seqlen_q, num_q_heads, a.group, batch, false);
     a.num_m_tiles = ceil_div(seqlen_q, 32 * t.wph);
     const int64_t nwg = (int64_t)a.num_m_tiles * (num_q_heads / t.hpw) * batch;
     if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
@@ -179,7 +185,7 @@ extern "C" int attn_prefill_paged(const void* q, const void* k_cache, const void
   a.hq = num_q_heads; a.hkv = num_kv_heads; a.group = num_q_heads / num_kv_heads;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = scale_log2;
-  const PrefillTile t = prefill_tile(max_seqlen_q, num_q_heads, a.group, num_seqs);
+  const PrefillTile t = prefill_tile(max_seqlen_q, num_q_heads, a.group, num_seqs, true);
   a.num_m_tiles = ceil_div(max_seqlen_q, 32 * t.wph);
   const int64_t nwg = (int64_t)a.num_m_tiles * (num_q_heads / t.hpw) * num_seqs;
   if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);

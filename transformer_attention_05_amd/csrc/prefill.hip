@@ -91,7 +91,10 @@ void prefill_bf16_kernel(const PrefillArgs a) {
 
   // LDS: a ring of three K tiles followed by a ring of three V tiles
   constexpr int TILE = BN * D;
-  __shared__ __attribute__((aligned(1024))) __bf16 sm[6 * TILE];
+  // V ring depth: three tiles, or two for 4-wavefront contiguous workgroups,
+  // which keeps them at 80 KiB of LDS so that two fit on a CU
+  constexpr int NVB = (!PAGED && NW == 4) ? 2 : 3;
+  __shared__ __attribute__((aligned(1024))) __bf16 sm[(3 + NVB) * TILE];
 
   const uint32_t id = blockIdx.x;
   const int hgroups = a.hq / HPW;
@@ -423,17 +426,22 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       mc = (m_run == -INFINITY ? 0.f : m_run) * c2;
     }
   };
+  // DMA instructions of the current iteration that may still be in flight
+  // at its end: K(j+3) and V(j+2) with the three-deep V ring; only K(j+3)
+  // with the two-deep one (its V(j+1) is issued first and must land)
+  constexpr int PENDING = NVB == 3 ? 2 * LPW : LPW;
   auto tile_barrier = [&]() {
-    // s_waitcnt vmcnt(2*LPW) (expcnt and lgkmcnt fields at their no-wait maximum)
-    __builtin_amdgcn_s_waitcnt(0x0f70 | ((2 * LPW) & 15) | (((2 * LPW) >> 4) << 14));
+    // s_waitcnt vmcnt(PENDING) (expcnt and lgkmcnt fields at their no-wait maximum)
+    __builtin_amdgcn_s_waitcnt(0x0f70 | (PENDING & 15) | ((PENDING >> 4) << 14));
     __syncthreads();
   };
 
   // ---- software pipeline.  Iteration j: S(j+1) = K(j+1) Q^T on the matrix
   // cores while the VALU turns S(j) into P(j); then O += V(j)^T P(j) while
-  // the VALU takes the row max of S(j+1).  Tile t of K (of V) lives in ring
-  // buffer t % 3; the DMA issued in iteration j (K(j+3), V(j+2)) has two
-  // iterations to land.  Every iteration issues the same number of DMA
+  // the VALU takes the row max of S(j+1).  Tile t of K lives in ring buffer
+  // t % 3 and the DMA of K(j+3) issued in iteration j has two iterations to
+  // land; tile t of V lives in buffer t % NVB and is loaded NVB - 1
+  // iterations ahead.  Every iteration issues the same number of DMA
   // instructions (the tile index is clamped), so one vmcnt covers them.
   __bf16* const kring = sm;
   __bf16* const vring = sm + 3 * TILE;
@@ -452,7 +460,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       issue_k(kring, 0, b0);
       issue_v(vring, 0, b0);
       issue_k(kring + TILE, min(1, n_tiles - 1), b1);
-      issue_v(vring + TILE, min(1, n_tiles - 1), b1);
+      if constexpr (NVB == 3) issue_v(vring + TILE, min(1, n_tiles - 1), b1);
       issue_k(kring + 2 * TILE, min(2, n_tiles - 1), blk_v);
     }
     __builtin_amdgcn_s_waitcnt(0);   // also retires the Q loads
@@ -470,8 +478,15 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // r0, r1, r2 = j % 3, (j + 1) % 3, (j + 2) % 3.
   int r0 = 0, r1 = 1, r2 = 2;
   auto iteration = [&](int j, const f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-    issue_k(kring + r0 * TILE, min(j + 3, n_tiles - 1), blk_k);
-    issue_v(vring + r2 * TILE, min(j + 2, n_tiles - 1), blk_v);
+    const int vcur = NVB == 3 ? r0 : (j & 1);  // ring buffer of V(j)
+    const int vnext = NVB == 3 ? r1 : (vcur ^ 1);  // of V(j+1)
+    if constexpr (NVB == 3) {
+      issue_k(kring + r0 * TILE, min(j + 3, n_tiles - 1), blk_k);
+      issue_v(vring + r2 * TILE, min(j + 2, n_tiles - 1), blk_v);
+    } else {
+      issue_v(vring + vnext * TILE, min(j + 1, n_tiles - 1), blk_v);
+      issue_k(kring + r0 * TILE, min(j + 3, n_tiles - 1), blk_k);
+    }
     if constexpr (PAGED) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) blk_v[i] = blk_k[i];
@@ -480,11 +495,11 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     phase_a(kring + r1 * TILE, sc, sn);
     if (needs_mask(j + 1)) mask_tile(sn, j + 1);
     float tmax = -INFINITY;
-    phase_b(vring + r0 * TILE, sn, tmax);
+    phase_b(vring + vcur * TILE, sn, tmax);
     update_max(fmaxf(tmax, xor32(tmax)));
     tile_barrier();
     if (tail_tile(j + 1)) {
-      zero_tail(vring + r1 * TILE, j + 1);
+      zero_tail(vring + vnext * TILE, j + 1);
       __syncthreads();
     }
     const int t = r0;
