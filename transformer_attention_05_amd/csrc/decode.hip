@@ -292,15 +292,28 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeArgs a) {
   lsum = sm_red[1][0] + sm_red[1][1];
   const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
   if (tid < D) {
+    // eight partitions per step: their loads are independent and in flight
+    // together (the merge is bound by load latency, not bandwidth)
     const float* po = a.ws_o + row * a.max_parts * D + tid;
-    float acc0 = 0.f, acc1 = 0.f;
+    float acc[8] = {};
     int i = 0;
-    for (; i + 1 < nparts; i += 2) {
-      acc0 = fmaf(sm_w[i], po[(int64_t)i * D], acc0);
-      acc1 = fmaf(sm_w[i + 1], po[(int64_t)(i + 1) * D], acc1);
+    for (; i + 8 <= nparts; i += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = po[(int64_t)(i + u) * D];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = fmaf(sm_w[i + u], x[u], acc[u]);
     }
-    if (i < nparts) acc0 = fmaf(sm_w[i], po[(int64_t)i * D], acc0);
-    static_cast<__bf16*>(a.o)[row * D + tid] = static_cast<__bf16>((acc0 + acc1) * inv);
+    {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = i + u < nparts ? po[(int64_t)(i + u) * D] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i + u < nparts) acc[u] = fmaf(sm_w[i + u], x[u], acc[u]);
+    }
+    const float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    static_cast<__bf16*>(a.o)[row * D + tid] = static_cast<__bf16>(sum * inv);
   }
 }
 
