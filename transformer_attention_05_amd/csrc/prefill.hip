@@ -6,8 +6,9 @@
 // the output on chip.  The Tq x Tk score matrix never reaches HBM.
 //
 // bf16 path (both contractions on MFMA, fp32 accumulate):
-//   * workgroup = 4 wavefronts = 128 queries of one (batch, query head);
-//     each wavefront owns 32 queries.
+//   * workgroup = HPW query heads of one kv group x WPH wavefronts; each
+//     wavefront owns 32 queries of one head, and every K/V tile in LDS
+//     serves all HPW heads.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16: Q^T stays in registers
 //     for the whole kernel, K comes from LDS.  In the S^T accumulator a lane
 //     holds one query (lane % 32) and 16 of the 32 keys of the subtile, so the
@@ -18,8 +19,11 @@
 //     V^T operand is read from a transposed LDS copy of the V tile in the same
 //     permuted order.  Each lane owns one query of O^T, so the rescale by
 //     exp(m_old - m_new) is lane-local.
-//   * K/V tiles of 64 keys are double-buffered in LDS; the next tile's global
-//     loads are issued before the current tile's MFMAs.
+//   * software pipeline: the MFMAs of S(j+1) run interleaved with the
+//     exponentials of S(j), the PV MFMAs of tile j with the row max of S(j+1).
+//   * K/V tiles of 64 keys cycle through LDS rings fed by global->LDS DMA one
+//     or two iterations ahead.  With 4 wavefronts a workgroup needs 80 KiB,
+//     so two workgroups share a CU and overlap each other's phases.
 //   * causal tiles wholly above the diagonal are never loaded; masking runs
 //     only on tiles that cross the diagonal or the sequence end.
 //   * workgroups are ordered heaviest first (last query tile first).  The
