@@ -86,13 +86,27 @@ ATTN_API const char* attn_last_error(void);
  *     (bottom-right aligned); requires seqlen_k >= seqlen_q.
  *   A query row that sees no key (only possible when seqlen_k == 0) gets O = 0.
  *   q, k, v, o must not overlap o.
+ *   workspace    optional device scratch (256-byte aligned) of
+ *                attn_prefill_workspace_size(...) bytes.  When that size is
+ *                non-zero and a workspace is given, launches with too few
+ *                query tiles to fill the GPU cut each query tile's keys into
+ *                shares computed by separate workgroups, and a second kernel
+ *                merges the shares' partial (max, sum, output) exactly, the
+ *                recombination of the online softmax that §FlashAttention-
+ *                Style Kernels describes.  NULL: one pass per query tile.  A
+ *                non-NULL workspace smaller than the size returns
+ *                ATTN_E_NOMEM.  Concurrent calls need separate workspaces.
  * ---------------------------------------------------------------------- */
+ATTN_API size_t attn_prefill_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   attn_dtype dtype);
 ATTN_API int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                  int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                  const int64_t q_strides[3], const int64_t k_strides[3],
                  const int64_t v_strides[3], const int64_t o_strides[3],
-                 float scale, int32_t causal, attn_dtype dtype, attn_stream_t stream);
+                 float scale, int32_t causal, attn_dtype dtype,
+                 void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* -------------------------------------------------------------------------
  * attn_prefill_paged -- prefill of new query chunks over a paged KV cache.
@@ -115,14 +129,25 @@ ATTN_API int attn_prefill(const void* q, const void* k, const void* v, void* o, 
  *   o            device bf16, same shape as q, written
  *   Chunk row i of sequence s sits at position context_lens[s] - n_s + i and,
  *   when causal, sees keys 0 .. that position.
+ *   max_context_len  the longest context_lens entry, or 0 for the bound
+ *                max_blocks_per_seq * 16.  Only the split plan uses it: a
+ *                longer context is still computed whole, by longer shares.
+ *   workspace    optional device scratch of
+ *                attn_prefill_paged_workspace_size(...) bytes (same meaning
+ *                and rules as attn_prefill's).
  * ---------------------------------------------------------------------- */
+ATTN_API size_t attn_prefill_paged_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                         int32_t max_context_len, int32_t num_q_heads,
+                                         int32_t num_kv_heads, int32_t head_dim);
 ATTN_API int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache,
                        const int32_t* block_table, int32_t max_blocks_per_seq,
                        const int32_t* cu_seqlens_q, const int32_t* context_lens,
                        void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                       int32_t max_context_len,
                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                        int32_t block_size, int32_t num_blocks,
-                       float scale, int32_t causal, attn_dtype dtype, attn_stream_t stream);
+                       float scale, int32_t causal, attn_dtype dtype,
+                       void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* -------------------------------------------------------------------------
  * attn_decode_paged -- one query token per sequence over its paged cache.

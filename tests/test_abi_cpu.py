@@ -29,7 +29,8 @@ def declared_symbols():
 
 def test_header_declares_entry_points():
     syms = declared_symbols()
-    for name in ("attn_prefill", "attn_prefill_paged", "attn_decode_paged", "attn_decode_paged_workspace_size",
+    for name in ("attn_prefill", "attn_prefill_paged", "attn_prefill_workspace_size",
+                 "attn_prefill_paged_workspace_size", "attn_decode_paged", "attn_decode_paged_workspace_size",
                  "attn_kv_cache_write_rope", "attn_pool_create", "attn_pool_alloc", "attn_pool_free",
                  "attn_pool_retain", "attn_seq_reserve", "attn_last_error"):
         assert name in syms
@@ -51,11 +52,11 @@ S3 = (ctypes.c_int64 * 3)(8 * 128, 128, 128)
 
 def prefill(lib, **kw):
     args = dict(q=P, k=P, v=P, o=P, lse=None, batch=1, tq=64, tk=64, hq=1, hkv=1, d=64,
-                qs=S3, ks=S3, vs=S3, os_=S3, scale=0.0, causal=1, dtype=ATTN_F32)
+                qs=S3, ks=S3, vs=S3, os_=S3, scale=0.0, causal=1, dtype=ATTN_F32, ws=None, wsb=0)
     args.update(kw)
     return lib.attn_prefill(args["q"], args["k"], args["v"], args["o"], args["lse"], args["batch"], args["tq"],
                             args["tk"], args["hq"], args["hkv"], args["d"], args["qs"], args["ks"], args["vs"],
-                            args["os_"], args["scale"], args["causal"], args["dtype"], None)
+                            args["os_"], args["scale"], args["causal"], args["dtype"], args["ws"], args["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -75,9 +76,44 @@ def prefill(lib, **kw):
     (dict(q=P + 2), ATTN_E_INVALID),            # misaligned
     (dict(qs=(ctypes.c_int64 * 3)(8 * 128, 130, 128)), ATTN_E_INVALID),  # stride not a multiple of 4
     (dict(dtype=ATTN_BF16, ks=(ctypes.c_int64 * 3)(1024, 132, 128)), ATTN_E_INVALID),
+    (dict(dtype=ATTN_BF16, vs=(ctypes.c_int64 * 3)(1 << 30, 1 << 28, 128)), ATTN_E_UNSUPPORTED),
 ])
 def test_prefill_rejects(lib, kw, status):
     assert prefill(lib, **kw) == status
+    assert lib.attn_last_error().decode().startswith("attn_prefill")
+
+
+# batch 1, T 2048, 12/2 heads, D 128: too few query tiles to fill the GPU, so
+# the plan splits each query tile's keys and needs a workspace
+SPLIT = dict(dtype=ATTN_BF16, batch=1, tq=2048, tk=2048, hq=12, hkv=2, d=128,
+             qs=(ctypes.c_int64 * 3)(2048 * 12 * 128, 12 * 128, 128),
+             ks=(ctypes.c_int64 * 3)(2048 * 2 * 128, 2 * 128, 128),
+             vs=(ctypes.c_int64 * 3)(2048 * 2 * 128, 2 * 128, 128),
+             os_=(ctypes.c_int64 * 3)(2048 * 12 * 128, 12 * 128, 128))
+
+
+def test_prefill_workspace_size(lib):
+    rows = 2048 * 12
+    n = lib.attn_prefill_workspace_size(1, 2048, 2048, 12, 2, 128, ATTN_BF16)
+    # whole shares of (D floats of output + max + sum) per (query row, head)
+    assert n > 0 and n % (rows * (128 * 4 + 8)) == 0 and 2 <= n // (rows * (128 * 4 + 8)) <= 64
+    # enough query tiles to fill the GPU, the f32 kernel and degenerate sizes: no split
+    assert lib.attn_prefill_workspace_size(1, 16384, 16384, 12, 2, 128, ATTN_BF16) == 0
+    assert lib.attn_prefill_workspace_size(1, 2048, 2048, 12, 2, 128, ATTN_F32) == 0
+    assert lib.attn_prefill_workspace_size(1, 0, 2048, 12, 2, 128, ATTN_BF16) == 0
+    assert lib.attn_prefill_workspace_size(1, 64, 64, 12, 2, 128, ATTN_BF16) == 0
+    # two chunks (200 + 50 new tokens) over up to 3200 keys: few query tiles, long rows
+    m = lib.attn_prefill_paged_workspace_size(2, 250, 200, 3200, 12, 2, 128)
+    assert m > 0 and m % (250 * 12 * (128 * 4 + 8)) == 0
+    assert lib.attn_prefill_paged_workspace_size(2, 250, 200, 0, 12, 2, 128) == 0
+    # eight 512-token chunks fill the GPU without splitting
+    assert lib.attn_prefill_paged_workspace_size(8, 4096, 512, 2560, 12, 2, 128) == 0
+
+
+def test_prefill_workspace_rejects(lib):
+    need = lib.attn_prefill_workspace_size(1, 2048, 2048, 12, 2, 128, ATTN_BF16)
+    assert prefill(lib, **SPLIT, ws=P, wsb=need - 1) == ATTN_E_NOMEM
+    assert prefill(lib, **SPLIT, ws=P + 16, wsb=need) == ATTN_E_INVALID   # not 256-byte aligned
     assert lib.attn_last_error().decode().startswith("attn_prefill")
 
 
@@ -125,12 +161,21 @@ def test_decode_workspace_size(lib):
 
 
 def test_paged_prefill_and_write_reject(lib):
-    st = lib.attn_prefill_paged(P, P, P, P, 8, P, P, P, 2, 100, 60, 12, 2, 128, 16, 100, 0.0, 1, ATTN_F32, None)
-    assert st == ATTN_E_UNSUPPORTED
-    st = lib.attn_prefill_paged(P, P, P, None, 8, P, P, P, 2, 100, 60, 12, 2, 128, 16, 100, 0.0, 1, ATTN_BF16, None)
-    assert st == ATTN_E_INVALID
-    st = lib.attn_prefill_paged(P, P, P, P, 8, P, P, P, 2, 50, 60, 12, 2, 128, 16, 100, 0.0, 1, ATTN_BF16, None)
-    assert st == ATTN_E_INVALID   # max_seqlen_q > total_q
+    def paged(**kw):
+        a = dict(bt=P, tot=100, maxq=60, maxctx=0, dtype=ATTN_BF16, ws=None, wsb=0)
+        a.update(kw)
+        return lib.attn_prefill_paged(P, P, P, a["bt"], 8, P, P, P, 2, a["tot"], a["maxq"], a["maxctx"], 12, 2,
+                                      128, 16, 100, 0.0, 1, a["dtype"], a["ws"], a["wsb"], None)
+    assert paged(dtype=ATTN_F32) == ATTN_E_UNSUPPORTED
+    assert paged(bt=None) == ATTN_E_INVALID
+    assert paged(tot=50) == ATTN_E_INVALID       # max_seqlen_q > total_q
+    assert paged(maxctx=-1) == ATTN_E_INVALID
+    # two chunks over up to 3200 keys: the plan splits
+    need = lib.attn_prefill_paged_workspace_size(2, 250, 200, 3200, 12, 2, 128)
+    assert need > 0
+    st = lib.attn_prefill_paged(P, P, P, P, 200, P, P, P, 2, 250, 200, 3200, 12, 2, 128, 16, 100, 0.0, 1,
+                                ATTN_BF16, P, need - 256, None)
+    assert st == ATTN_E_NOMEM
     st = lib.attn_kv_cache_write_rope(P, P, P, P, P, P, P, 10, 12, 2, 128, 8, 100, 10000.0, ATTN_BF16, None)
     assert st == ATTN_E_UNSUPPORTED
     st = lib.attn_kv_cache_write_rope(P, None, P, P, P, P, P, 10, 12, 2, 128, 16, 100, 10000.0, ATTN_BF16, None)

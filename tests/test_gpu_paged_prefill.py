@@ -39,12 +39,12 @@ def paged_setup(seed, cached, new, hq=12, hkv=2, d=128, order="random"):
     return qs, ks, vs, bt, kc, vc, total
 
 
-def run_paged(qs, bt, kc, vc, total, causal=True):
+def run_paged(qs, bt, kc, vc, total, causal=True, **kw):
     q = torch.cat(qs).to(DEV)
     cu = np.concatenate([[0], np.cumsum([x.shape[0] for x in qs])]).astype(np.int32)
     o = mi.attn_prefill_paged(q, kc, vc, torch.from_numpy(bt).to(DEV), torch.from_numpy(cu).to(DEV),
                               torch.from_numpy(total.astype(np.int32)).to(DEV), int(np.diff(cu).max()),
-                              causal=causal)
+                              causal=causal, **kw)
     torch.cuda.synchronize()
     return o.cpu(), cu
 
@@ -63,13 +63,35 @@ def test_chunked_prefill(cached, new):
 
 def test_chunk_equals_rows_of_contiguous_prefill():
     """Chunked prefill at cached c = rows c .. c+n-1 of the contiguous causal
-    prefill over c + n tokens (paged and contiguous kernels agree)."""
+    prefill over c + n tokens (paged and contiguous kernels agree bit for bit
+    when each query tile is one pass)."""
     c, n = 300, 200
     qs, ks, vs, bt, kc, vc, total = paged_setup(80, [c], [n])
-    o, _ = run_paged(qs, bt, kc, vc, total)
+    o, _ = run_paged(qs, bt, kc, vc, total, workspace=False)
     qfull = torch.cat([normal(rng(1), (c, 12, 128), torch.bfloat16), qs[0]])[None]
-    full = mi.attn_prefill(qfull.to(DEV), ks[0][None].to(DEV), vs[0][None].to(DEV), causal=True).cpu()
+    full = mi.attn_prefill(qfull.to(DEV), ks[0][None].to(DEV), vs[0][None].to(DEV), causal=True,
+                           workspace=False).cpu()
     assert torch.equal(full[0, c:], o)
+
+
+@pytest.mark.parametrize("ctx_hint", [0, 3200, 1100])
+def test_split_kv_chunked_prefill(ctx_hint):
+    """Split-KV shares + merge = one pass per query tile = the oracle, for a
+    context bound from the block table (0), the exact longest context, and a
+    bound below it (the kernel lengthens the shares to cover every key)."""
+    cached, new = [3000, 100], [200, 50]
+    say(f"case: paged split-KV, max_context_len hint {ctx_hint}")
+    s, tot, mq = len(new), sum(new), max(new)
+    bound = ctx_hint or 3200
+    assert mi.attn_prefill_paged_workspace_size(s, tot, mq, bound, 12, 2, 128) > 0   # the plan splits
+    qs, ks, vs, bt, kc, vc, total = paged_setup(90, cached, new)
+    o_split, _ = run_paged(qs, bt, kc, vc, total, max_context_len=ctx_hint)
+    o_one, _ = run_paged(qs, bt, kc, vc, total, workspace=False)
+    refs = np.concatenate(oracle.chunked_prefill([to_f64(q) for q in qs], [to_f64(k) for k in ks],
+                                                 [to_f64(v) for v in vs]))
+    check(f64(o_split), refs, torch.bfloat16, "split-KV chunked")
+    check(f64(o_one), refs, torch.bfloat16, "one-pass chunked")
+    check(f64(o_split), f64(o_one), torch.bfloat16, "split vs one pass")
 
 
 def test_noncausal_paged():

@@ -30,10 +30,10 @@ def check_lse(got, ref, dtype, what):
     assert e.max() <= bar
 
 
-def run(q, k, v, causal=True, want_lse=False, scale=0.0):
+def run(q, k, v, causal=True, want_lse=False, scale=0.0, workspace=None):
     qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
     lse = torch.empty(q.shape[0], q.shape[2], q.shape[1], dtype=torch.float32, device=DEV) if want_lse else None
-    o = mi.attn_prefill(qd, kd, vd, lse=lse, causal=causal, scale=scale)
+    o = mi.attn_prefill(qd, kd, vd, lse=lse, causal=causal, scale=scale, workspace=workspace)
     torch.cuda.synchronize()
     return (o.cpu(), lse.cpu() if want_lse else None)
 
@@ -101,6 +101,34 @@ def test_ragged_shapes(case, dtype):
     ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=causal)
     check(f64(o), ref, dtype, f"ragged {case}")
     check_lse(f64(lse), ref_lse, dtype, "ragged")
+
+
+SPLIT_CASES = [
+    # (batch, tq, tk, hq, hkv, d, causal): few query tiles, many key tiles
+    (1, 2048, 2048, 12, 2, 128, True),
+    (2, 1000, 1000, 12, 2, 128, True),
+    (1, 300, 1800, 4, 2, 64, False),
+    (1, 77, 3001, 6, 1, 128, True),
+    (3, 129, 1400, 2, 2, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[f"b{c[0]}_tq{c[1]}_tk{c[2]}_h{c[3]}x{c[4]}_d{c[5]}"
+                                                   for c in SPLIT_CASES])
+def test_split_kv_equals_single_pass(case):
+    """Split-KV (key shares on separate workgroups, merged) against the
+    oracle and against one pass per query tile, output and LSE."""
+    b, tq, tk, hq, hkv, d, causal = case
+    say(f"case: split-KV {case}")
+    assert mi.attn_prefill_workspace_size(b, tq, tk, hq, hkv, d) > 0   # the plan splits
+    q, k, v = prefill_case(4000 + SPLIT_CASES.index(case), b, tq, hq, hkv, d, torch.bfloat16, seqlen_k=tk)
+    o_s, lse_s = run(q, k, v, causal=causal, want_lse=True)
+    o_1, lse_1 = run(q, k, v, causal=causal, want_lse=True, workspace=False)
+    ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=causal)
+    check(f64(o_s), ref, torch.bfloat16, "split O")
+    check(f64(o_1), ref, torch.bfloat16, "one-pass O")
+    check_lse(f64(lse_s), ref_lse, torch.bfloat16, "split")
+    check(f64(o_s), f64(o_1), torch.bfloat16, "split vs one pass")
 
 
 def test_explicit_scale():

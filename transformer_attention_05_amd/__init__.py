@@ -25,6 +25,8 @@ __all__ = [
     "attn_last_error",
     "attn_prefill",
     "attn_prefill_paged",
+    "attn_prefill_paged_workspace_size",
+    "attn_prefill_workspace_size",
     "lib_path",
     "load",
 ]
@@ -43,11 +45,14 @@ _vp = ctypes.c_void_p
 
 _SIGNATURES = {
     "attn_last_error": (ctypes.c_char_p, []),
+    "attn_prefill_workspace_size": (ctypes.c_size_t, [_c_i32] * 6 + [ctypes.c_int]),
     "attn_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
-                                    _c_i64p, _c_i64p, _c_i64p, _c_i64p, ctypes.c_float, _c_i32, ctypes.c_int, _vp]),
+                                    _c_i64p, _c_i64p, _c_i64p, _c_i64p, ctypes.c_float, _c_i32, ctypes.c_int,
+                                    _vp, ctypes.c_size_t, _vp]),
+    "attn_prefill_paged_workspace_size": (ctypes.c_size_t, [_c_i32] * 7),
     "attn_prefill_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
-                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float, _c_i32,
-                                          ctypes.c_int, _vp]),
+                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
+                                          _c_i32, ctypes.c_int, _vp, ctypes.c_size_t, _vp]),
     "attn_decode_paged_workspace_size": (ctypes.c_size_t, [_c_i32] * 6),
     "attn_decode_paged_auto_partition": (_c_i32, [_c_i32] * 3),
     "attn_decode_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -138,33 +143,69 @@ def _bth_strides(t: torch.Tensor, name: str):
 
 # ----------------------------------------------------------------------------- kernels
 
-def attn_prefill(q, k, v, o=None, lse=None, causal=True, scale=0.0):
-    """Contiguous attention on [B, T, H, D] tensors (any batch/token/head strides)."""
+def _workspace(ws, need, device):
+    """(pointer, bytes) of a split-KV workspace: None allocates one of `need`
+    bytes, False passes none (one pass per query tile)."""
+    if ws is False or need == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return _dev(ws, "workspace"), ws.numel() * ws.element_size()
+
+
+def attn_prefill_workspace_size(batch, seqlen_q, seqlen_k, num_q_heads, num_kv_heads, head_dim,
+                                dtype=torch.bfloat16) -> int:
+    code = ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F32
+    return int(load().attn_prefill_workspace_size(batch, seqlen_q, seqlen_k, num_q_heads, num_kv_heads,
+                                                  head_dim, code))
+
+
+def attn_prefill(q, k, v, o=None, lse=None, causal=True, scale=0.0, workspace=None):
+    """Contiguous attention on [B, T, H, D] tensors (any batch/token/head strides).
+
+    ``workspace``: a uint8 GPU tensor of at least
+    attn_prefill_workspace_size(...) bytes, None to allocate one here, or
+    False to run without split-KV."""
     if o is None:
         o = torch.empty_like(q)
     b, tq, hq, d = q.shape
     _, tk, hkv, _ = k.shape
+    need = attn_prefill_workspace_size(b, tq, tk, hq, hkv, d, q.dtype)
+    ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
     st = load().attn_prefill(
         _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(lse, "lse") if lse is not None else None,
         b, tq, tk, hq, hkv, d,
         _bth_strides(q, "q"), _bth_strides(k, "k"), _bth_strides(v, "v"), _bth_strides(o, "o"),
-        float(scale), 1 if causal else 0, _dtype_code(q), _stream(q))
+        float(scale), 1 if causal else 0, _dtype_code(q), ws_ptr, ws_bytes, _stream(q))
     _check(st)
     return o
 
 
+def attn_prefill_paged_workspace_size(num_seqs, total_q, max_seqlen_q, max_context_len, num_q_heads,
+                                      num_kv_heads, head_dim) -> int:
+    return int(load().attn_prefill_paged_workspace_size(num_seqs, total_q, max_seqlen_q, max_context_len,
+                                                        num_q_heads, num_kv_heads, head_dim))
+
+
 def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, context_lens, max_seqlen_q,
-                       o=None, causal=True, scale=0.0):
-    """Chunked prefill of packed queries q [total_q, Hq, D] over the paged caches."""
+                       o=None, causal=True, scale=0.0, max_context_len=0, workspace=None):
+    """Chunked prefill of packed queries q [total_q, Hq, D] over the paged caches.
+
+    ``max_context_len``: the longest context (0: what the block table holds),
+    used to plan split-KV; ``workspace`` as for attn_prefill."""
     if o is None:
         o = torch.empty_like(q)
     total_q, hq, d = q.shape
     nb, hkv, bs, _ = k_cache.shape
+    s = context_lens.shape[0]
+    bound = int(max_context_len) if max_context_len else block_table.shape[1] * bs
+    need = attn_prefill_paged_workspace_size(s, total_q, int(max_seqlen_q), bound, hq, hkv, d)
+    ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
     st = load().attn_prefill_paged(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
         block_table.shape[1], _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(context_lens, "context_lens"),
-        _dev(o, "o"), context_lens.shape[0], total_q, int(max_seqlen_q), hq, hkv, d, bs, nb,
-        float(scale), 1 if causal else 0, _dtype_code(q), _stream(q))
+        _dev(o, "o"), s, total_q, int(max_seqlen_q), int(max_context_len), hq, hkv, d, bs, nb,
+        float(scale), 1 if causal else 0, _dtype_code(q), ws_ptr, ws_bytes, _stream(q))
     _check(st)
     return o
 

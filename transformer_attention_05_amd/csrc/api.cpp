@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -91,7 +92,102 @@ PrefillTile prefill_tile(int64_t max_q, int32_t hq, int32_t group, int64_t batch
   return t;
 }
 
+// Split-KV plan of the bf16 prefill.  A launch with too few query tiles to
+// fill the chip (a short prompt, one long-context chunk) leaves CUs idle
+// while the longest query tile walks all of its key tiles.  Cutting each query
+// tile's key tiles into shares of split_tiles tiles multiplies the workgroups
+// and shortens that critical path; a merge pass recombines the shares' (m, l,
+// O) exactly, as the decode does with its partitions.  A query tile whose key
+// tiles fit in one share still writes its output directly.  Every share pays
+// a workgroup's fixed cost (Q and the first K/V tiles in, the pipeline's fill
+// and drain, the output out: ~6-13 us measured on MI355X) and its fp32
+// partials are written and read back, so only launches that would fill less
+// than half of the workgroup slots split, into shares of at least 8 tiles.
+// A launch that already fills most CUs (the chunks of a serving step, which
+// also share the GPU with the decode) gains nothing and runs in one pass.
+constexpr int kCUs = 256;           // MI355X compute units
+constexpr int kMinSplitTiles = 8;
+struct PrefillPlan {
+  PrefillTile t;
+  int32_t num_m_tiles = 0;
+  int64_t num_wg = 0;
+  int32_t num_splits = 1, split_tiles = 0;
+  int64_t ws_rows = 0;
+  size_t o_bytes = 0, ml_bytes = 0;
+};
+
+// rows: (query row, head) pairs of the output, the workspace's row count.
+// max_k: keys of the longest sequence (an upper bound for a paged batch).
+PrefillPlan plan_prefill(int64_t max_q, int64_t max_k, int32_t hq, int32_t group, int64_t batch,
+                         int32_t d, bool paged, int64_t rows) {
+  PrefillPlan p;
+  p.t = prefill_tile(max_q, hq, group, batch, paged);
+  p.num_m_tiles = ceil_div(max_q, 32 * p.t.wph);
+  p.num_wg = (int64_t)p.num_m_tiles * (hq / p.t.hpw) * batch;
+  // two 4-wavefront contiguous workgroups share a CU (80 KiB of LDS each)
+  const int64_t slots = (int64_t)kCUs * ((!paged && p.t.hpw * p.t.wph == 4) ? 2 : 1);
+  const int64_t t_max = (max_k + 63) / 64;  // key tiles of the longest query tile
+  int64_t split = 0;                        // forced share length (tuning only)
+  static const char* env = std::getenv("MI_ATTN_PREFILL_SPLIT");
+  if (env) split = std::atoll(env);
+  int64_t L = 0;
+  if (env && split <= 0) {
+    L = 0;
+  } else if (split > 0) {
+    L = split;
+  } else if (2 * p.num_wg <= slots && t_max >= 2 * kMinSplitTiles) {
+    const int64_t s = std::min((slots + p.num_wg - 1) / p.num_wg, (t_max + kMinSplitTiles - 1) / kMinSplitTiles);
+    if (s > 1) L = (t_max + s - 1) / s;
+  }
+  if (L > 0 && L < t_max) {
+    p.split_tiles = (int32_t)L;
+    p.num_splits = (int32_t)((t_max + L - 1) / L);
+    p.ws_rows = rows;
+    p.o_bytes = ((size_t)p.num_splits * rows * d * sizeof(float) + 255) / 256 * 256;
+    p.ml_bytes = (size_t)p.num_splits * rows * 2 * sizeof(float);
+  }
+  return p;
+}
+
+// Checks a caller's workspace against a plan: NULL runs the single pass.
+int use_workspace(PrefillPlan& p, void* workspace, size_t workspace_bytes, PrefillArgs& a, const char* fn) {
+  a.num_splits = 1;
+  if (p.num_splits <= 1 || !workspace) return ATTN_OK;
+  if (!aligned(workspace, 256)) return fail(ATTN_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
+  const size_t need = p.o_bytes + p.ml_bytes;
+  if (workspace_bytes < need) return fail(ATTN_E_NOMEM, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);
+  a.num_splits = p.num_splits;
+  a.split_tiles = p.split_tiles;
+  a.ws_rows = p.ws_rows;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + p.o_bytes);
+  return ATTN_OK;
+}
+
 }  // namespace
+
+// ---------------------------------------------------------------------------
+extern "C" size_t attn_prefill_workspace_size(int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                              attn_dtype dtype) {
+  if (dtype != ATTN_BF16 || batch <= 0 || seqlen_q <= 0 || seqlen_k <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128))
+    return 0;
+  const PrefillPlan p = plan_prefill(seqlen_q, seqlen_k, num_q_heads, num_q_heads / num_kv_heads, batch, head_dim,
+                                     false, (int64_t)batch * seqlen_q * num_q_heads);
+  return p.o_bytes + p.ml_bytes;
+}
+
+extern "C" size_t attn_prefill_paged_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                                    int32_t max_context_len, int32_t num_q_heads,
+                                                    int32_t num_kv_heads, int32_t head_dim) {
+  if (num_seqs <= 0 || total_q <= 0 || max_seqlen_q <= 0 || max_context_len <= 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128))
+    return 0;
+  const PrefillPlan p = plan_prefill(max_seqlen_q, max_context_len, num_q_heads, num_q_heads / num_kv_heads,
+                                     num_seqs, head_dim, true, (int64_t)total_q * num_q_heads);
+  return p.o_bytes + p.ml_bytes;
+}
 
 // ---------------------------------------------------------------------------
 extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -99,7 +195,8 @@ extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o
                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                             const int64_t q_strides[3], const int64_t k_strides[3],
                             const int64_t v_strides[3], const int64_t o_strides[3],
-                            float scale, int32_t causal, attn_dtype dtype, attn_stream_t stream) {
+                            float scale, int32_t causal, attn_dtype dtype,
+                            void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   static const char* fn = "attn_prefill";
   if (!q || !k || !v || !o) return fail(ATTN_E_INVALID, "%s: q, k, v and o must be non-NULL", fn);
   if (!q_strides || !k_strides || !v_strides || !o_strides)
@@ -123,6 +220,10 @@ extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o
     for (int i = 0; i < 3; ++i)
       if (sa[i] < 0 || sa[i] % mult != 0)
         return fail(ATTN_E_INVALID, "%s: strides must be >= 0 and multiples of %lld elements", fn, (long long)mult);
+  // the bf16 kernel forms each lane's key/value load address as a 32-bit
+  // byte offset from a row base: up to 7 token strides of 2 bytes
+  if (dtype == ATTN_BF16 && (k_strides[1] >= (int64_t(1) << 28) || v_strides[1] >= (int64_t(1) << 28)))
+    return fail(ATTN_E_UNSUPPORTED, "%s: key/value token strides must be below 2^28 elements", fn);
   if (batch == 0 || seqlen_q == 0) return ok();
 
   PrefillArgs a{};
@@ -137,13 +238,15 @@ extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o
   a.scale_log2 = scale_log2;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16) {
-    const PrefillTile t = prefill_tile(seqlen_q, num_q_heads, a.group, batch, false);
-    a.num_m_tiles = ceil_div(seqlen_q, 32 * t.wph);
-    const int64_t nwg = (int64_t)a.num_m_tiles * (num_q_heads / t.hpw) * batch;
-    if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
-    a.num_wg = (uint32_t)nwg;
-    return launched(launch_prefill_bf16(a, head_dim, false, t.hpw, t.wph, s), fn);
+    PrefillPlan p = plan_prefill(seqlen_q, seqlen_k, num_q_heads, a.group, batch, head_dim, false,
+                                 (int64_t)batch * seqlen_q * num_q_heads);
+    if ((st = use_workspace(p, workspace, workspace_bytes, a, fn)) != ATTN_OK) return st;
+    a.num_m_tiles = p.num_m_tiles;
+    if (p.num_wg * a.num_splits > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
+    a.num_wg = (uint32_t)p.num_wg;
+    return launched(launch_prefill_bf16(a, head_dim, false, p.t.hpw, p.t.wph, s), fn);
   }
+  a.num_splits = 1;
   a.num_m_tiles = ceil_div(seqlen_q, kPrefillF32BlockM);
   const int64_t nwg = (int64_t)a.num_m_tiles * num_q_heads * batch;
   if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
@@ -156,13 +259,16 @@ extern "C" int attn_prefill_paged(const void* q, const void* k_cache, const void
                                   const int32_t* block_table, int32_t max_blocks_per_seq,
                                   const int32_t* cu_seqlens_q, const int32_t* context_lens,
                                   void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                  int32_t max_context_len,
                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                   int32_t block_size, int32_t num_blocks,
-                                  float scale, int32_t causal, attn_dtype dtype, attn_stream_t stream) {
+                                  float scale, int32_t causal, attn_dtype dtype,
+                                  void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   static const char* fn = "attn_prefill_paged";
   if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !context_lens || !o)
     return fail(ATTN_E_INVALID, "%s: pointer arguments must be non-NULL", fn);
-  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_blocks_per_seq < 1 || num_blocks < 1)
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_context_len < 0 || max_blocks_per_seq < 1 ||
+      num_blocks < 1)
     return fail(ATTN_E_INVALID, "%s: bad size", fn);
   if (max_seqlen_q > total_q) return fail(ATTN_E_INVALID, "%s: max_seqlen_q > total_q", fn);
   int st;
@@ -185,16 +291,19 @@ extern "C" int attn_prefill_paged(const void* q, const void* k_cache, const void
   a.hq = num_q_heads; a.hkv = num_kv_heads; a.group = num_q_heads / num_kv_heads;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = scale_log2;
-  const PrefillTile t = prefill_tile(max_seqlen_q, num_q_heads, a.group, num_seqs, true);
-  a.num_m_tiles = ceil_div(max_seqlen_q, 32 * t.wph);
-  const int64_t nwg = (int64_t)a.num_m_tiles * (num_q_heads / t.hpw) * num_seqs;
-  if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
-  a.num_wg = (uint32_t)nwg;
+  // the plan's key bound: the caller's, else what the block table can hold
+  const int64_t ctx_bound = max_context_len > 0 ? max_context_len : (int64_t)max_blocks_per_seq * kBlockSizeHost;
+  PrefillPlan p = plan_prefill(max_seqlen_q, ctx_bound, num_q_heads, a.group, num_seqs, head_dim, true,
+                               (int64_t)total_q * num_q_heads);
+  if ((st = use_workspace(p, workspace, workspace_bytes, a, fn)) != ATTN_OK) return st;
+  a.num_m_tiles = p.num_m_tiles;
+  if (p.num_wg * a.num_splits > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
+  a.num_wg = (uint32_t)p.num_wg;
   a.block_table = block_table; a.bt_stride = max_blocks_per_seq;
   a.cu_seqlens_q = cu_seqlens_q; a.context_lens = context_lens;
   a.num_blocks = num_blocks;
   a.total_q = total_q;
-  return launched(launch_prefill_bf16(a, head_dim, true, t.hpw, t.wph, reinterpret_cast<hipStream_t>(stream)), fn);
+  return launched(launch_prefill_bf16(a, head_dim, true, p.t.hpw, p.t.wph, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 // ---------------------------------------------------------------------------

@@ -30,6 +30,16 @@ struct PrefillArgs {
   const int32_t* context_lens;
   int32_t num_blocks;  // pool size; out-of-range table entries are redirected to block 0
   int32_t total_q;     // packed query rows; rows past it are never touched
+  // split-KV (bf16 path): grid = num_wg query tiles x num_splits, the share
+  // index fastest; share s of a query tile takes its key tiles
+  // [s * L, (s + 1) * L) with L = split_tiles, or longer when the tile has
+  // more than num_splits * split_tiles key tiles.  A query tile with more
+  // than one share writes fp32 partials, merged by prefill_merge_kernel.
+  int32_t num_splits;   // 1: no split
+  int32_t split_tiles;  // key tiles per split (when num_splits > 1)
+  int64_t ws_rows;      // partial rows per split: (query row, head) pairs
+  float* ws_o;          // [num_splits][ws_rows][D], unnormalised output
+  float* ws_ml;         // [num_splits][ws_rows][2]: max (log2 units), row sum
 };
 
 struct DecodeArgs {

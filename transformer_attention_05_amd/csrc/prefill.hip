@@ -64,6 +64,24 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_dst);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
+// the same from a uniform (scalar) base plus a 32-bit per-lane byte offset
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, const void* lds_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_dst);
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  // readfirstlane returns int: widen through uint32_t (no sign extension)
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint64_t sb = ((uint64_t)hi << 32) | (uint64_t)lo;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(lds) : "memory", "m0");
+}
+
+// Key tiles per split-KV share of a query tile that sees n_all key tiles:
+// the planned length, or more when n_all exceeds what num_splits shares of
+// that length cover (a context longer than the host planned for), so the
+// shares always cover every tile.
+__device__ __forceinline__ int split_len(int n_all, const PrefillArgs& a) {
+  return a.num_splits > 1 ? max(a.split_tiles, (n_all + a.num_splits - 1) / a.num_splits) : max(n_all, 1);
+}
 
 // LDS tiles are unpadded and XOR-swizzled at 16-byte granularity so that
 // the MFMA operand reads are free of bank conflicts.  (row, chunk) is stored
@@ -100,7 +118,10 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NVB = (!PAGED && NW == 4) ? 2 : 3;
   __shared__ __attribute__((aligned(1024))) __bf16 sm[(3 + NVB) * TILE];
 
-  const uint32_t id = blockIdx.x;
+  // split-KV share index fastest: all shares of the longest query tiles
+  // (dispatched first) start together
+  const int split = (int)(blockIdx.x % (uint32_t)a.num_splits);
+  const uint32_t id = blockIdx.x / (uint32_t)a.num_splits;
   const int hgroups = a.hq / HPW;
   const uint32_t per_tile = (uint32_t)hgroups * (uint32_t)a.batch;
   const int mt = a.num_m_tiles - 1 - (int)(id / per_tile);
@@ -151,13 +172,21 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     qreg[c] = qi < tq ? *reinterpret_cast<const bf16x8*>(q_base + (int64_t)qi * q_stride_t + 16 * c + 8 * hh)
                       : bf16x8{};
 
-  // ---- key tiles this workgroup visits
-  int n_tiles = (tk + BN - 1) / BN;
+  // ---- key tiles this query tile visits, and this split's share of them
+  int n_all = (tk + BN - 1) / BN;
   if (a.causal) {
     const int q_hi = min(m0 + BM, tq) - 1;
     const int kmax = min(tk - 1, q_hi + off);
-    n_tiles = kmax < 0 ? 0 : kmax / BN + 1;
+    n_all = kmax < 0 ? 0 : kmax / BN + 1;
   }
+  const int L = split_len(n_all, a);
+  const int nsplit = max(1, (n_all + L - 1) / L);
+  const int T0 = split * L;                    // first key tile of this split
+  if (split > 0 && T0 >= n_all) return;        // uniform: no tiles left for this split
+  int n_tiles = max(0, min(n_all - T0, L));        // tiles of this split
+  // opaque to the optimiser: reasoning over how the count is derived costs
+  // ~15 registers in the loop below
+  asm volatile("" : "+s"(n_tiles));
 
   // ---- global -> LDS DMA of one K or V tile.  Rows past the keys re-read
   // the last key: finite values whose weights are masked to zero.  A paged
@@ -181,16 +210,17 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     const int32_t hi = (i & 1) ? blk[3] : blk[2];
     return (i & 2) ? hi : lo;
   };
-  // contiguous layout: lane source of DMA slot i for key row r of tile 0;
-  // a whole tile in range is that plus a uniform offset
-  const __bf16* ksrc0[LPW];
-  const __bf16* vsrc0[LPW];
+  // contiguous layout: a DMA of a whole tile in range reads from a scalar
+  // row base plus this lane's byte offset (row within the DMA, swizzled
+  // chunk); the offset fits in 32 bits for token strides below 2^28
+  // elements, which attn_prefill requires
+  uint32_t koff[LPW], voff[LPW];  // bytes
   if constexpr (!PAGED) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int r = (wave * LPW + i) * RPI + lane / CH;
-      ksrc0[i] = kbase + b * a.ks_b + g * a.ks_h + (int64_t)r * a.ks_t + 8 * ((lane % CH) ^ k_swz<D>(r));
-      vsrc0[i] = vbase + b * a.vs_b + g * a.vs_h + (int64_t)r * a.vs_t + 8 * ((lane % CH) ^ v_swz<D>(r));
+      koff[i] = 2u * (uint32_t)((lane / CH) * (int32_t)a.ks_t + 8 * ((lane % CH) ^ k_swz<D>(r)));
+      voff[i] = 2u * (uint32_t)((lane / CH) * (int32_t)a.vs_t + 8 * ((lane % CH) ^ v_swz<D>(r)));
     }
   }
   // Paged rows past the context read a valid slot of the last block (the
@@ -209,7 +239,10 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       }
     } else if (n0 + BN <= tk) {
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) dma16(ksrc0[i] + (int64_t)n0 * a.ks_t, dk + (wave * LPW + i) * 512);
+      for (int i = 0; i < LPW; ++i) {
+        const int ii = wave * LPW + i;
+        dma16s(kbase + b * a.ks_b + g * a.ks_h + (int64_t)(n0 + ii * RPI) * a.ks_t, koff[i], dk + ii * 512);
+      }
     } else {
       // last partial tile: rows past the keys re-read the last key
 #pragma unroll
@@ -237,7 +270,10 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       }
     } else if (n0 + BN <= tk) {
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) dma16(vsrc0[i] + (int64_t)n0 * a.vs_t, dv + (wave * LPW + i) * 512);
+      for (int i = 0; i < LPW; ++i) {
+        const int ii = wave * LPW + i;
+        dma16s(vbase + b * a.vs_b + g * a.vs_h + (int64_t)(n0 + ii * RPI) * a.vs_t, voff[i], dv + ii * 512);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
@@ -258,7 +294,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       dv[d * BN + 8 * ((kl >> 3) ^ vt_swz(d)) + (kl & 7)] = __bf16{};
     }
   };
-  auto tail_tile = [&](int t) { return PAGED && t == n_tiles - 1 && (t + 1) * BN > tk; };
+  auto tail_tile = [&](int t) { return PAGED && t == n_all - 1 && (t + 1) * BN > tk; };
 
   const float c2 = a.scale_log2;
   const float tau_raw = kLazyTau / c2;
@@ -399,9 +435,14 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       }
     }
   };
-  auto needs_mask = [&](int t) { return (t + 1) * BN > tk || (a.causal && (t + 1) * BN - 1 > wq0 + off); };
+  // Keys of the split end at key_end; the tile after the split's last one
+  // (the loop's dummy) lies wholly past it and is masked completely.
+  const int key_end = min(tk, (T0 + n_tiles) * BN);
+  auto needs_mask = [&](int t) {
+    return (t + 1) * BN > key_end || (a.causal && (t + 1) * BN - 1 > wq0 + off);
+  };
   auto mask_tile = [&](f32x16 (&s)[2], int t) {
-    const int lim = a.causal ? min(tk - 1, qi + off) : tk - 1;
+    const int lim = a.causal ? min(key_end - 1, qi + off) : key_end - 1;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -457,53 +498,53 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   if (n_tiles > 0) {
     {
       int32_t b0[4], b1[4];
-      tile_blocks(0, b0);
-      tile_blocks(min(1, n_tiles - 1), b1);
-      tile_blocks(min(2, n_tiles - 1), blk_v);
-      tile_blocks(min(3, n_tiles - 1), blk_k);
-      issue_k(kring, 0, b0);
-      issue_v(vring, 0, b0);
-      issue_k(kring + TILE, min(1, n_tiles - 1), b1);
-      if constexpr (NVB == 3) issue_v(vring + TILE, min(1, n_tiles - 1), b1);
-      issue_k(kring + 2 * TILE, min(2, n_tiles - 1), blk_v);
+      tile_blocks(T0, b0);
+      tile_blocks(T0 + min(1, n_tiles - 1), b1);
+      tile_blocks(T0 + min(2, n_tiles - 1), blk_v);
+      tile_blocks(T0 + min(3, n_tiles - 1), blk_k);
+      issue_k(kring, T0, b0);
+      issue_v(vring, T0, b0);
+      issue_k(kring + TILE, T0 + min(1, n_tiles - 1), b1);
+      if constexpr (NVB == 3) issue_v(vring + TILE, T0 + min(1, n_tiles - 1), b1);
+      issue_k(kring + 2 * TILE, T0 + min(2, n_tiles - 1), blk_v);
     }
     __builtin_amdgcn_s_waitcnt(0);   // also retires the Q loads
     __syncthreads();
-    if (tail_tile(0)) zero_tail(vring, 0);
+    if (tail_tile(T0)) zero_tail(vring, T0);
     s_mfma(kring, sa);
-    if (needs_mask(0)) mask_tile(sa, 0);
+    if (needs_mask(T0)) mask_tile(sa, T0);
     update_max(row_max(sa));
     __syncthreads();
   }
-  // Iteration j.  The last iteration also computes S for tile n_tiles: its
+  // Iteration j (tile T0 + j of the query tile's key tiles).  The last
+  // iteration also computes S for the tile after this split's last one: its
   // K buffer holds a re-read of the last tile and every score of it is
-  // masked (its keys lie past the last key any row of the workgroup may
-  // see), so it changes nothing and the loop body has a single form.
+  // masked, so it changes nothing and the loop body has a single form.
   // r0, r1, r2 = j % 3, (j + 1) % 3, (j + 2) % 3.
   int r0 = 0, r1 = 1, r2 = 2;
   auto iteration = [&](int j, const f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int vcur = NVB == 3 ? r0 : (j & 1);  // ring buffer of V(j)
     const int vnext = NVB == 3 ? r1 : (vcur ^ 1);  // of V(j+1)
     if constexpr (NVB == 3) {
-      issue_k(kring + r0 * TILE, min(j + 3, n_tiles - 1), blk_k);
-      issue_v(vring + r2 * TILE, min(j + 2, n_tiles - 1), blk_v);
+      issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
+      issue_v(vring + r2 * TILE, T0 + min(j + 2, n_tiles - 1), blk_v);
     } else {
-      issue_v(vring + vnext * TILE, min(j + 1, n_tiles - 1), blk_v);
-      issue_k(kring + r0 * TILE, min(j + 3, n_tiles - 1), blk_k);
+      issue_v(vring + vnext * TILE, T0 + min(j + 1, n_tiles - 1), blk_v);
+      issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
     }
     if constexpr (PAGED) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) blk_v[i] = blk_k[i];
-      tile_blocks(min(j + 4, n_tiles - 1), blk_k);
+      tile_blocks(T0 + min(j + 4, n_tiles - 1), blk_k);
     }
     phase_a(kring + r1 * TILE, sc, sn);
-    if (needs_mask(j + 1)) mask_tile(sn, j + 1);
+    if (needs_mask(T0 + j + 1)) mask_tile(sn, T0 + j + 1);
     float tmax = -INFINITY;
     phase_b(vring + vcur * TILE, sn, tmax);
     update_max(fmaxf(tmax, xor32(tmax)));
     tile_barrier();
-    if (tail_tile(j + 1)) {
-      zero_tail(vring + vnext * TILE, j + 1);
+    if (tail_tile(T0 + j + 1)) {
+      zero_tail(vring + vnext * TILE, T0 + j + 1);
       __syncthreads();
     }
     const int t = r0;
@@ -521,26 +562,122 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
   }
 
-  // ---- epilogue: O = O / l, optional LSE (natural log)
+  // ---- epilogue: O = O / l, optional LSE (natural log); with several
+  // splits the unnormalised O, the max (log2 units) and the row sum go to
+  // the workspace for prefill_merge_kernel
   const float l_tot = l_run + xor32(l_run);
   if (qi < tq) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    __bf16* orow = o_base + (int64_t)qi * o_stride_t;
+    if (nsplit > 1) {
+      const int64_t row = PAGED ? (q_row0 + qi) * a.hq + h : ((int64_t)b * tq + qi) * a.hq + h;
+      const int64_t slot = (int64_t)split * a.ws_rows + row;
+      float* wo = a.ws_o + slot * D;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = dt * 32 + 8 * rg + 4 * hh;
-        const u32x2 w = {pack_bf16x2(oacc[dt][4 * rg + 0] * inv, oacc[dt][4 * rg + 1] * inv),
-                         pack_bf16x2(oacc[dt][4 * rg + 2] * inv, oacc[dt][4 * rg + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + d0) = w;
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = dt * 32 + 8 * rg + 4 * hh;
+          *reinterpret_cast<f32x4*>(wo + d0) =
+              f32x4{oacc[dt][4 * rg + 0], oacc[dt][4 * rg + 1], oacc[dt][4 * rg + 2], oacc[dt][4 * rg + 3]};
+        }
+      if (hh == 0) {
+        a.ws_ml[slot * 2 + 0] = m_run * c2;
+        a.ws_ml[slot * 2 + 1] = l_tot;
       }
-    if (!PAGED && a.lse != nullptr && hh == 0) {
-      const float lse = l_tot > 0.f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
-      a.lse[((int64_t)b * a.hq + h) * tq + qi] = lse;
+    } else {
+      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+      __bf16* orow = o_base + (int64_t)qi * o_stride_t;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          const int d0 = dt * 32 + 8 * rg + 4 * hh;
+          const u32x2 w = {pack_bf16x2(oacc[dt][4 * rg + 0] * inv, oacc[dt][4 * rg + 1] * inv),
+                           pack_bf16x2(oacc[dt][4 * rg + 2] * inv, oacc[dt][4 * rg + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + d0) = w;
+        }
+      if (!PAGED && a.lse != nullptr && hh == 0) {
+        const float lse = l_tot > 0.f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+        a.lse[((int64_t)b * a.hq + h) * tq + qi] = lse;
+      }
     }
   }
 }
+
+// ---------------------------------------------------------------------------
+// Merge of the split-KV partials of one query tile (the same geometry as the
+// attention kernel): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with
+// M = max_s m_s, the exact recombination of softmax statistics, taken here
+// as one online pass over the shares (their loads do not depend on each
+// other).  Thread = (head, query row, four channels); a query tile's items
+// are spread over MERGE_PARTS workgroups of 256 threads.
+template <int D, int HPW, int WPH>
+constexpr int merge_parts() { return HPW * 32 * WPH * (D / 4) / 256; }
+
+template <int D, bool PAGED, int HPW, int WPH>
+__global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a) {
+  constexpr int BM = 32 * WPH;
+  constexpr int PARTS = merge_parts<D, HPW, WPH>();
+  const uint32_t id = blockIdx.x / PARTS;
+  const int it = (int)(blockIdx.x % PARTS) * 256 + (int)threadIdx.x;
+  const int hgroups = a.hq / HPW;
+  const uint32_t per_tile = (uint32_t)hgroups * (uint32_t)a.batch;
+  const int mt = a.num_m_tiles - 1 - (int)(id / per_tile);
+  const uint32_t rem = id % per_tile;
+  const int b = (int)(rem / hgroups);
+  const int h0 = (int)(rem % hgroups) * HPW;
+  int32_t tq, tk;
+  int64_t q_row0 = 0;
+  if constexpr (PAGED) {
+    const int32_t c0 = a.cu_seqlens_q[b];
+    tq = max(0, min(a.cu_seqlens_q[b + 1], a.total_q) - max(c0, 0));
+    tk = min(a.context_lens[b], a.bt_stride * kBlockSize);
+    q_row0 = max(c0, 0);
+  } else {
+    tq = a.tq;
+    tk = a.tk;
+  }
+  const int m0 = mt * BM;
+  if (m0 >= tq) return;
+  int n_all = (tk + BN - 1) / BN;
+  if (a.causal) {
+    const int q_hi = min(m0 + BM, tq) - 1;
+    const int kmax = min(tk - 1, q_hi + tk - tq);
+    n_all = kmax < 0 ? 0 : kmax / BN + 1;
+  }
+  const int L = split_len(n_all, a);
+  const int nsplit = max(1, (n_all + L - 1) / L);
+  if (nsplit <= 1) return;  // that query tile wrote its output itself
+  const int hl = it / (BM * (D / 4));
+  const int r = (it / (D / 4)) % BM;
+  const int d0 = 4 * (it % (D / 4));
+  const int qi = m0 + r;
+  if (qi >= tq) return;
+  const int h = h0 + hl;
+  const int64_t row = PAGED ? (q_row0 + qi) * a.hq + h : ((int64_t)b * tq + qi) * a.hq + h;
+  float mx = -INFINITY, lsum = 0.f;
+  f32x4 acc = f32x4{};
+#pragma unroll 4
+  for (int sp = 0; sp < nsplit; ++sp) {
+    const int64_t slot = (int64_t)sp * a.ws_rows + row;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + slot * 2);
+    const f32x4 ov = *reinterpret_cast<const f32x4*>(a.ws_o + slot * D + d0);
+    const float mn = fmaxf(mx, ml[0]);
+    const float mu = mn == -INFINITY ? 0.f : mn;
+    const float f_old = __builtin_amdgcn_exp2f(mx - mu);    // 0 while mx is -inf
+    const float f_new = __builtin_amdgcn_exp2f(ml[0] - mu);
+    lsum = lsum * f_old + f_new * ml[1];
+    acc = acc * f_old + f_new * ov;
+    mx = mn;
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  __bf16* op = static_cast<__bf16*>(a.o);
+  __bf16* orow = PAGED ? op + ((q_row0 + qi) * a.hq + h) * D : op + b * a.os_b + (int64_t)qi * a.os_t + h * a.os_h;
+  *reinterpret_cast<u32x2*>(orow + d0) = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv),
+                                               pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (!PAGED && a.lse != nullptr && d0 == 0)
+    a.lse[((int64_t)b * a.hq + h) * tq + qi] = lsum > 0.f ? (mx + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
 // ---------------------------------------------------------------------------
 // f32 VALU kernel: LPQ = D / 64 lanes per query, each holding 64 channels.
 template <int D>
@@ -636,13 +773,22 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
 
 }  // namespace
 
+
+template <int D, bool PAGED, int HPW, int WPH>
+static void launch_one(const PrefillArgs& a, hipStream_t s) {
+  dim3 grid(a.num_wg * (uint32_t)a.num_splits);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, HPW, WPH>), grid, dim3(64 * HPW * WPH), 0, s, a);
+  if (a.num_splits > 1)
+    hipLaunchKernelGGL((prefill_merge_kernel<D, PAGED, HPW, WPH>), dim3(a.num_wg * merge_parts<D, HPW, WPH>()),
+                       dim3(256), 0, s, a);
+}
+
 template <int D, bool PAGED>
 static void launch_cfg(const PrefillArgs& a, int hpw, int wph, hipStream_t s) {
-  dim3 grid(a.num_wg);
-  if (hpw == 2 && wph == 4) hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 2, 4>), grid, dim3(512), 0, s, a);
-  else if (hpw == 2 && wph == 2) hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 2, 2>), grid, dim3(256), 0, s, a);
-  else if (hpw == 1 && wph == 4) hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 1, 4>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, 1, 2>), grid, dim3(128), 0, s, a);
+  if (hpw == 2 && wph == 4) launch_one<D, PAGED, 2, 4>(a, s);
+  else if (hpw == 2 && wph == 2) launch_one<D, PAGED, 2, 2>(a, s);
+  else if (hpw == 1 && wph == 4) launch_one<D, PAGED, 1, 4>(a, s);
+  else launch_one<D, PAGED, 1, 2>(a, s);
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, hipStream_t s) {

@@ -17,7 +17,7 @@ import numpy as np
 import torch
 
 from . import (Pool, attn_decode_paged, attn_decode_paged_workspace_size, attn_kv_cache_write_rope,
-               attn_prefill_paged)
+               attn_prefill_paged, attn_prefill_paged_workspace_size)
 
 
 class MixedStep:
@@ -62,6 +62,11 @@ class MixedStep:
         self.o_decode = torch.empty(S, case.hq, d, dtype=dt, device=device)
         need = attn_decode_paged_workspace_size(S, case.hq, hkv, d, self.max_dec_ctx, partition_size)
         self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        # split-KV workspace of the chunked prefill (its own: the two run at once)
+        self.max_pre_ctx = int((case.cached + case.chunk).max()) if R else 1
+        need = attn_prefill_paged_workspace_size(R, max(self.n_prefill, 1), case.chunk, self.max_pre_ctx, case.hq,
+                                                 hkv, d) if R else 0
+        self.pre_workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
         # side stream (default priority) and the event that orders it after the write
         self.side = torch.cuda.Stream(device=device)
         self.written = torch.cuda.Event()
@@ -74,7 +79,7 @@ class MixedStep:
         R = self.R
         attn_prefill_paged(self.q[: self.n_prefill], self.k_cache, self.v_cache, self.tables[:R],
                            self.cu_seqlens_q, self.context_lens[:R], self.case.chunk, o=self.o_prefill,
-                           causal=True)
+                           causal=True, max_context_len=self.max_pre_ctx, workspace=self.pre_workspace)
 
     def decode(self):
         R = self.R
