@@ -147,6 +147,24 @@ def test_mixed_step_small():
     assert not used & set(case.foreign.tolist())
 
 
+def test_concurrent_step_equals_serial():
+    """The two-stream schedule (decode tokens written and decoded on a second
+    stream beside the chunk write and prefill) gives the serial order's
+    outputs, rotated queries and caches bit for bit."""
+    say("case: concurrent vs serial step")
+    case = mixed_case(78, num_req=3, chunk=200, cached_max=900, num_dec=20, dec_lo=1, dec_hi=5000)
+    steps = []
+    for conc in (False, True):
+        st = MixedStep(case, assign_blocks, DEV, scatter=scatter_to_pool, concurrent=conc)
+        st.run()
+        torch.cuda.synchronize()
+        steps.append(st)
+    a, b = steps
+    for name in ("o_prefill", "o_decode", "q", "k_cache", "v_cache"):
+        x, y = getattr(a, name), getattr(b, name)
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16)), name
+
+
 def test_c5_mixed_step():
     """8 chunks of 512 new tokens on 0-2048 cached tokens + 128 decode
     sequences with context log-U[16, 32768], RoPE base 10000, fragmented pool
