@@ -60,13 +60,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 // completion is ordered by the explicit vmcnt waits before the barriers that
 // publish a tile, and the LDS ring buffers can then live in one array
 // addressed by a uniform buffer offset.
-__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_dst);
+// `lds` is the LDS byte address (uniform).
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
 }
 // the same from a uniform (scalar) base plus a 32-bit per-lane byte offset
-__device__ __forceinline__ void dma16s(const void* base, uint32_t off, const void* lds_dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)lds_dst);
+__device__ __forceinline__ void dma16s(const void* base, uint32_t off, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);
   const uint64_t p = (uint64_t)(uintptr_t)base;
   // readfirstlane returns int: widen through uint32_t (no sign extension)
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
@@ -215,14 +216,26 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // chunk); the offset fits in 32 bits for token strides below 2^28
   // elements, which attn_prefill requires
   uint32_t koff[LPW], voff[LPW];  // bytes
+  // Scalar parts, formed once: the (batch, kv head) bases, and the element
+  // offset of each DMA slot's first row within a tile, so a tile's DMA costs
+  // one scalar multiply plus a 64-bit add per slot.
+  const __bf16* const kb0 = kbase + b * a.ks_b + g * a.ks_h;
+  const __bf16* const vb0 = vbase + b * a.vs_b + g * a.vs_h;
+  int64_t krow[LPW], vrow[LPW];
   if constexpr (!PAGED) {
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int r = (wave * LPW + i) * RPI + lane / CH;
       koff[i] = 2u * (uint32_t)((lane / CH) * (int32_t)a.ks_t + 8 * ((lane % CH) ^ k_swz<D>(r)));
       voff[i] = 2u * (uint32_t)((lane / CH) * (int32_t)a.vs_t + 8 * ((lane % CH) ^ v_swz<D>(r)));
+      krow[i] = (int64_t)((wave * LPW + i) * RPI) * a.ks_t;
+      vrow[i] = (int64_t)((wave * LPW + i) * RPI) * a.vs_t;
     }
   }
+  // LDS byte address of the ring array (the one generic-to-LDS conversion);
+  // a DMA destination is this plus a uniform byte offset
+  const uint32_t sm_lds = (uint32_t)(uintptr_t)(lds_void*)sm;
+  auto lds_of = [&](const __bf16* p) { return sm_lds + 2u * (uint32_t)(p - sm); };
   // Paged rows past the context read a valid slot of the last block (the
   // table entries are clamped to it); their scores are masked and their
   // values zeroed, so only the address has to stay inside the pool.
@@ -235,14 +248,13 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         const int r = ii * RPI + lane / CH;  // the RPI rows of one DMA share a block
         const int32_t bk = pick4(blk, (ii * RPI) >> 4);
         dma16(kbase + (((int64_t)bk * a.hkv + g) * kBlockSize + (r & 15)) * D + 8 * ((lane % CH) ^ k_swz<D>(r)),
-              dk + ii * 512);
+              lds_of(dk) + ii * 1024);
       }
     } else if (n0 + BN <= tk) {
+      const __bf16* tb = kb0 + (int64_t)n0 * a.ks_t;
+      const uint32_t l0 = lds_of(dk) + wave * LPW * 1024;
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int ii = wave * LPW + i;
-        dma16s(kbase + b * a.ks_b + g * a.ks_h + (int64_t)(n0 + ii * RPI) * a.ks_t, koff[i], dk + ii * 512);
-      }
+      for (int i = 0; i < LPW; ++i) dma16s(tb + krow[i], koff[i], l0 + i * 1024);
     } else {
       // last partial tile: rows past the keys re-read the last key
 #pragma unroll
@@ -251,7 +263,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         const int r = ii * RPI + lane / CH;
         const int key = min(n0 + r, tk - 1);
         dma16(kbase + b * a.ks_b + (int64_t)key * a.ks_t + g * a.ks_h + 8 * ((lane % CH) ^ k_swz<D>(r)),
-              dk + ii * 512);
+              lds_of(dk) + ii * 1024);
       }
     }
   };
@@ -266,14 +278,13 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         const int d = ii * 8 + lane / 8;
         const int c = (lane % 8) ^ vt_swz(d);
         const int32_t bk = pick4(blk, c >> 1);
-        dma16(vbase + (((int64_t)bk * a.hkv + g) * D + d) * kBlockSize + 8 * (c & 1), dv + ii * 512);
+        dma16(vbase + (((int64_t)bk * a.hkv + g) * D + d) * kBlockSize + 8 * (c & 1), lds_of(dv) + ii * 1024);
       }
     } else if (n0 + BN <= tk) {
+      const __bf16* tb = vb0 + (int64_t)n0 * a.vs_t;
+      const uint32_t l0 = lds_of(dv) + wave * LPW * 1024;
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int ii = wave * LPW + i;
-        dma16s(vbase + b * a.vs_b + g * a.vs_h + (int64_t)(n0 + ii * RPI) * a.vs_t, voff[i], dv + ii * 512);
-      }
+      for (int i = 0; i < LPW; ++i) dma16s(tb + vrow[i], voff[i], l0 + i * 1024);
     } else {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
@@ -281,7 +292,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         const int r = ii * RPI + lane / CH;
         const int key = min(n0 + r, tk - 1);
         dma16(vbase + b * a.vs_b + (int64_t)key * a.vs_t + g * a.vs_h + 8 * ((lane % CH) ^ v_swz<D>(r)),
-              dv + ii * 512);
+              lds_of(dv) + ii * 1024);
       }
     }
   };
