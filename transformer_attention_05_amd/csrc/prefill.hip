@@ -527,6 +527,13 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     update_max(row_max(sa));
     __syncthreads();
   }
+  // Q^T is in registers by now (the wait above retired its loads), but the
+  // compiler's wait insertion keeps them pending and would put a vmcnt(0) in
+  // front of the loop's first use of Q^T, which would also wait for the tile
+  // DMAs just issued.  Passing the registers through an empty asm makes them
+  // the asm's results; any wait it adds sits here, before the loop.
+#pragma unroll
+  for (int c = 0; c < D / 16; ++c) asm volatile("" : "+v"(qreg[c]));
   // Iteration j (tile T0 + j of the query tile's key tiles).  The last
   // iteration also computes S for the tile after this split's last one: its
   // K buffer holds a re-read of the last tile and every score of it is
