@@ -74,17 +74,17 @@ def test_chunk_equals_rows_of_contiguous_prefill():
     assert torch.equal(full[0, c:], o)
 
 
-@pytest.mark.parametrize("ctx_hint", [0, 3200, 1100])
-def test_split_kv_chunked_prefill(ctx_hint):
+@pytest.mark.parametrize("ctx_hint,d", [(0, 128), (3200, 128), (1100, 128), (3200, 64)])
+def test_split_kv_chunked_prefill(ctx_hint, d):
     """Split-KV shares + merge = one pass per query tile = the oracle, for a
     context bound from the block table (0), the exact longest context, and a
     bound below it (the kernel lengthens the shares to cover every key)."""
     cached, new = [3000, 100], [200, 50]
-    say(f"case: paged split-KV, max_context_len hint {ctx_hint}")
+    say(f"case: paged split-KV, max_context_len hint {ctx_hint}, D {d}")
     s, tot, mq = len(new), sum(new), max(new)
     bound = ctx_hint or 3200
-    assert mi.attn_prefill_paged_workspace_size(s, tot, mq, bound, 12, 2, 128) > 0   # the plan splits
-    qs, ks, vs, bt, kc, vc, total = paged_setup(90, cached, new)
+    assert mi.attn_prefill_paged_workspace_size(s, tot, mq, bound, 12, 2, d) > 0   # the plan splits
+    qs, ks, vs, bt, kc, vc, total = paged_setup(90, cached, new, d=d)
     o_split, _ = run_paged(qs, bt, kc, vc, total, max_context_len=ctx_hint)
     o_one, _ = run_paged(qs, bt, kc, vc, total, workspace=False)
     refs = np.concatenate(oracle.chunked_prefill([to_f64(q) for q in qs], [to_f64(k) for k in ks],

@@ -16,15 +16,34 @@ pytestmark = [pytest.mark.gpu,
 SENTINEL = -1  # int16 0xFFFF: a NaN bit pattern in bf16
 
 
-def setup(seed, n, hq, hkv, d, nb, dtype):
+def setup(seed, n, hq, hkv, d, nb, dtype, layout="perm"):
+    """layout "perm": slots a random permutation of the pool (a 16-token
+    workgroup's tokens land in unrelated blocks), every 7th skipped; "runs":
+    runs of consecutive slots starting mid-block, as a chunk's tokens."""
     g = rng(seed)
     q = normal(g, (n, hq, d), dtype)
     k = normal(g, (n, hkv, d), dtype)
     v = normal(g, (n, hkv, d), dtype)
     pos = g.integers(0, 32768, n).astype(np.int32)
-    slots = g.permutation(nb * BLOCK_SIZE)[:n].astype(np.int32)
-    slots[::7] = -1
+    if layout == "perm":
+        slots = g.permutation(nb * BLOCK_SIZE)[:n].astype(np.int32)
+        slots[::7] = -1
+    else:
+        starts = g.permutation(nb // 4)[: (n + 49) // 50] * 4 * BLOCK_SIZE + 5
+        slots = np.concatenate([s0 + np.arange(50) for s0 in starts])[:n].astype(np.int32)
     return q, k, v, pos, slots
+
+
+# (n, hq, hkv, d, nb, layout): the serving shape, more heads than one pass of
+# a workgroup holds (three q/k passes, four value passes), one kv head per
+# query head at D 64, and consecutive slots
+WRITE_SHAPES = [
+    (300, 12, 2, 128, 40, "perm"),
+    (150, 32, 8, 128, 40, "perm"),
+    (200, 8, 8, 64, 40, "perm"),
+    (333, 12, 2, 128, 120, "runs"),
+]
+WRITE_IDS = [f"n{c[0]}_h{c[1]}x{c[2]}_d{c[3]}_{c[5]}" for c in WRITE_SHAPES]
 
 
 def caches(nb, hkv, d, dtype):
@@ -37,11 +56,12 @@ def caches(nb, hkv, d, dtype):
     return kc, vc
 
 
+@pytest.mark.parametrize("shape", WRITE_SHAPES, ids=WRITE_IDS)
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_plain_copy_is_bit_exact(dtype):
-    say(f"case: cache write copy {dtype}")
-    n, hq, hkv, d, nb = 300, 12, 2, 128, 40
-    q, k, v, pos, slots = setup(60, n, hq, hkv, d, nb, dtype)
+def test_plain_copy_is_bit_exact(dtype, shape):
+    say(f"case: cache write copy {dtype} {shape}")
+    n, hq, hkv, d, nb, layout = shape
+    q, k, v, pos, slots = setup(60, n, hq, hkv, d, nb, dtype, layout)
     kc, vc = caches(nb, hkv, d, dtype)
     kc0, vc0 = kc.clone(), vc.clone()
     qd = q.to(DEV)
@@ -63,11 +83,12 @@ def test_plain_copy_is_bit_exact(dtype):
         assert np.array_equal(f64(kc), ek) and np.array_equal(f64(vc), ev)
 
 
+@pytest.mark.parametrize("shape", WRITE_SHAPES, ids=WRITE_IDS)
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-def test_rope_write(dtype):
-    say(f"case: rope write {dtype}")
-    n, hq, hkv, d, nb = 500, 12, 2, 128, 64
-    q, k, v, pos, slots = setup(61, n, hq, hkv, d, nb, dtype)
+def test_rope_write(dtype, shape):
+    say(f"case: rope write {dtype} {shape}")
+    n, hq, hkv, d, nb, layout = shape
+    q, k, v, pos, slots = setup(61, n, hq, hkv, d, nb, dtype, layout)
     kc, vc = caches(nb, hkv, d, dtype)
     kc0, vc0 = kc.clone(), vc.clone()
     qd = q.to(DEV)
