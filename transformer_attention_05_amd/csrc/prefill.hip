@@ -601,22 +601,38 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         a.ws_ml[slot * 2 + 0] = m_run * c2;
         a.ws_ml[slot * 2 + 1] = l_tot;
       }
-    } else {
-      const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-      __bf16* orow = o_base + (int64_t)qi * o_stride_t;
+    } else if (!PAGED && a.lse != nullptr && hh == 0) {
+      const float lse = l_tot > 0.f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+      a.lse[((int64_t)b * a.hq + h) * tq + qi] = lse;
+    }
+  }
+  if (nsplit <= 1) {
+    // O through LDS, so that global stores cover whole rows: the wave writes
+    // its 32 x D tile (row = query, 16-byte chunks XOR-swizzled by row, free
+    // of bank conflicts both ways) into its own slice of the ring array, then
+    // reads it back 16 bytes per lane in row order.  The barrier first lets
+    // every wave finish with the K/V rings.
+    __syncthreads();
+    constexpr int CPRW = D / 8;         // 16-byte chunks per row
+    constexpr int RPS = 64 / CPRW;      // rows per store instruction
+    __bf16* st = sm + wave * 32 * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+    for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const int d0 = dt * 32 + 8 * rg + 4 * hh;
-          const u32x2 w = {pack_bf16x2(oacc[dt][4 * rg + 0] * inv, oacc[dt][4 * rg + 1] * inv),
-                           pack_bf16x2(oacc[dt][4 * rg + 2] * inv, oacc[dt][4 * rg + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + d0) = w;
-        }
-      if (!PAGED && a.lse != nullptr && hh == 0) {
-        const float lse = l_tot > 0.f ? (m_run * c2 + __log2f(l_tot)) * kLn2 : -INFINITY;
-        a.lse[((int64_t)b * a.hq + h) * tq + qi] = lse;
+      for (int rg = 0; rg < 4; ++rg) {
+        const int c = 4 * dt + rg;  // chunk of channels dt*32 + 8*rg .. +7; this lane has half hh
+        const u32x2 w = {pack_bf16x2(oacc[dt][4 * rg + 0] * inv, oacc[dt][4 * rg + 1] * inv),
+                         pack_bf16x2(oacc[dt][4 * rg + 2] * inv, oacc[dt][4 * rg + 3] * inv)};
+        *reinterpret_cast<u32x2*>(st + lq * D + 8 * (c ^ (lq & (CPRW - 1))) + 4 * hh) = w;
       }
+#pragma unroll
+    for (int it = 0; it < 32 / RPS; ++it) {
+      const int row = it * RPS + lane / CPRW;
+      const int c = lane % CPRW;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + row * D + 8 * (c ^ (row & (CPRW - 1))));
+      const int q = wq0 + row;
+      if (q < tq) *reinterpret_cast<u32x4*>(o_base + (int64_t)q * o_stride_t + 8 * c) = v;
     }
   }
 }
