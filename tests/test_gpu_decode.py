@@ -52,6 +52,17 @@ def test_split_kv_partition_sizes(part):
     check(f64(o), oracle_decode(case), torch.bfloat16, f"partition {part}")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_merge_of_many_partitions(d):
+    """Long contexts cut into 128-token partitions (up to 157 per sequence):
+    the merge walks the partials in several passes of its partition groups."""
+    say(f"case: many partitions, D {d}")
+    case = decode_case(32, 5, 1, 1, d=d, lengths=np.array([20000, 9000, 8193, 16, 129]))
+    kc, vc = build_decode_pool(case, DEV)
+    o = run_decode(case, kc, vc, partition_size=128)
+    check(f64(o), oracle_decode(case), torch.bfloat16, f"157 partitions, D {d}")
+
+
 def test_block_order_invariance_and_worked_table(golden_dir):
     """Identity, reversed and random block tables give bit-identical outputs
     (paging does not change the logical K/V), and the tutorial's worked table

@@ -253,67 +253,86 @@ __global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeA
   }
 }
 
-// Merge kernel: workgroup = (query head, sequence), thread = channel.
-// O = sum_p f_p O_p / sum_p f_p l_p with f_p = exp(m_p - max m); the
-// partition weights are computed once, in parallel, into LDS.
+// Merge kernel: workgroup = (query head, sequence).
+// O = sum_p f_p O_p / sum_p f_p l_p with f_p = exp(m_p - max m).  Thread =
+// (four channels, partition group): it takes every MPG-th partition, so the
+// partials' loads of up to MK partitions per thread, and the (m, l) loads,
+// are all in flight at once (the merge is bound by load latency); the
+// partition groups are then summed through LDS.
+constexpr int kMergeThreads = 256;
 template <int D>
-__global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const DecodeArgs a) {
+  constexpr int CG = D / 4;                  // channel groups (four channels each)
+  constexpr int MPG = kMergeThreads / CG;    // partition groups
+  constexpr int MK = 8;                      // partitions per thread and pass
   const int h = blockIdx.x;
   const int s = blockIdx.y;
   const int ctx = min(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize));
   const int nparts = (ctx + a.part_size - 1) / a.part_size;
   if (nparts <= 1) return;
-  extern __shared__ float sm_w[];  // [max_parts]
-  __shared__ float sm_red[2][2];
+  __shared__ float sm_red[kMergeThreads / 64];
+  __shared__ f32x4 sm_acc[MPG][CG];
+  __shared__ float sm_l[MPG];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int cg = tid % CG, pg = tid / CG;
   const int64_t row = (int64_t)s * a.hq + h;
   const float* ml = a.ws_ml + row * a.max_parts * 2;
+  const f32x4* po = reinterpret_cast<const f32x4*>(a.ws_o + row * a.max_parts * D) + cg;
   const float c2 = a.scale_log2;
 
+  // this thread's partitions of the first pass, and every (m) for the max
+  f32x4 ov[MK];
+  f32x2 mlv[MK];
+#pragma unroll
+  for (int k = 0; k < MK; ++k) {
+    const int p = pg + k * MPG;
+    ov[k] = p < nparts ? po[(int64_t)p * CG] : f32x4{};
+    mlv[k] = p < nparts ? *reinterpret_cast<const f32x2*>(ml + 2 * p) : f32x2{-INFINITY, 0.f};
+  }
   float mx = -INFINITY;
-  for (int i = tid; i < nparts; i += 128) mx = fmaxf(mx, ml[2 * i]);
+  for (int i = tid; i < nparts; i += kMergeThreads) mx = fmaxf(mx, ml[2 * i]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) sm_red[0][wave] = mx;
+  if (lane == 0) sm_red[wave] = mx;
   __syncthreads();
-  mx = fmaxf(sm_red[0][0], sm_red[0][1]);
+  mx = sm_red[0];
+#pragma unroll
+  for (int w = 1; w < kMergeThreads / 64; ++w) mx = fmaxf(mx, sm_red[w]);
   const float mu = (mx == -INFINITY) ? 0.f : mx;
+
+  f32x4 acc = f32x4{};
   float lsum = 0.f;
-  for (int i = tid; i < nparts; i += 128) {
-    const float f = __builtin_amdgcn_exp2f((ml[2 * i] - mu) * c2);
-    sm_w[i] = f;
-    lsum = fmaf(f, ml[2 * i + 1], lsum);
+  for (int base = 0;; base += MK * MPG) {
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      const float f = __builtin_amdgcn_exp2f((mlv[k][0] - mu) * c2);  // 0 past nparts (m = -inf)
+      acc += f * ov[k];
+      lsum = fmaf(f, mlv[k][1], lsum);
+    }
+    if (base + MK * MPG >= nparts) break;
+    // more partitions than one pass holds (small partitions of a long context)
+#pragma unroll
+    for (int k = 0; k < MK; ++k) {
+      const int p = base + MK * MPG + pg + k * MPG;
+      ov[k] = p < nparts ? po[(int64_t)p * CG] : f32x4{};
+      mlv[k] = p < nparts ? *reinterpret_cast<const f32x2*>(ml + 2 * p) : f32x2{-INFINITY, 0.f};
+    }
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lsum += __shfl_xor(lsum, o);
-  if (lane == 0) sm_red[1][wave] = lsum;
+  sm_acc[pg][cg] = acc;
+  if (cg == 0) sm_l[pg] = lsum;
   __syncthreads();
-  lsum = sm_red[1][0] + sm_red[1][1];
-  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-  if (tid < D) {
-    // eight partitions per step: their loads are independent and in flight
-    // together (the merge is bound by load latency, not bandwidth)
-    const float* po = a.ws_o + row * a.max_parts * D + tid;
-    float acc[8] = {};
-    int i = 0;
-    for (; i + 8 <= nparts; i += 8) {
-      float x[8];
+  if (pg == 0) {
+    f32x4 o = sm_acc[0][cg];
+    float l = sm_l[0];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = po[(int64_t)(i + u) * D];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc[u] = fmaf(sm_w[i + u], x[u], acc[u]);
+    for (int g = 1; g < MPG; ++g) {
+      o += sm_acc[g][cg];
+      l += sm_l[g];
     }
-    {
-      float x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = i + u < nparts ? po[(int64_t)(i + u) * D] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (i + u < nparts) acc[u] = fmaf(sm_w[i + u], x[u], acc[u]);
-    }
-    const float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-    static_cast<__bf16*>(a.o)[row * D + tid] = static_cast<__bf16>(sum * inv);
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + row * D + 4 * cg) =
+        u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
   }
 }
 
@@ -322,17 +341,16 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(const DecodeArgs a) {
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t st) {
   dim3 grid1(a.max_parts | 1, a.hkv * a.head_groups, a.num_seqs);
   dim3 grid2(a.hq, a.num_seqs);
-  const size_t merge_smem = sizeof(float) * (size_t)a.max_parts;
   if (head_dim == 128) {
     hipLaunchKernelGGL(decode_partition_kernel<128>, grid1, dim3(64 * DW), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.max_parts > 1) hipLaunchKernelGGL(decode_merge_kernel<128>, grid2, dim3(128), merge_smem, st, a);
+    if (a.max_parts > 1) hipLaunchKernelGGL(decode_merge_kernel<128>, grid2, dim3(kMergeThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL(decode_partition_kernel<64>, grid1, dim3(64 * DW), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.max_parts > 1) hipLaunchKernelGGL(decode_merge_kernel<64>, grid2, dim3(128), merge_smem, st, a);
+    if (a.max_parts > 1) hipLaunchKernelGGL(decode_merge_kernel<64>, grid2, dim3(kMergeThreads), 0, st, a);
   }
   return hipGetLastError();
 }
