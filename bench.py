@@ -233,13 +233,14 @@ def main():
         ws = torch.empty(max(256, mi.attn_decode_paged_workspace_size(64, HQ, HKV, D, mx)), dtype=torch.uint8,
                          device=dev)
         o = torch.empty_like(qd)
+        plan = torch.from_numpy(mi.attn_decode_paged_plan(dc.lengths, HKV, mx)).to(dev)
         for i in range(max(3, args.warmup)):
-            mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws)
+            mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws, plan=plan)
         torch.cuda.synchronize()
         td = EventTimer(torch)
         n = max(9, args.steps)
         for i in range(n):
-            e = td.start(); mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws); td.stop(e)
+            e = td.start(); mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws, plan=plan); td.stop(e)
         torch.cuda.synchronize()
         by = decode_bytes(dc.lengths)
         out["decode_c3"] = dict(ms=td.mean_ms(), bytes=by, part=mi.attn_decode_paged_auto_partition(64, HKV, mx))

@@ -166,6 +166,15 @@ ATTN_API int attn_prefill_paged(const void* q, const void* k_cache, const void* 
  *                token included)
  *   o            device bf16 [num_seqs][num_q_heads][head_dim], written
  *   partition_size: 0 = automatic, else a multiple of 128, at most 1024.
+ *   plan         optional device int32 [plan_items][2]: the (sequence,
+ *                partition) pairs that attn_decode_paged_plan lists for the
+ *                same context lengths, max_context_len, num_kv_heads and
+ *                partition_size.  With a plan only those partitions are
+ *                dispatched; NULL (plan_items 0): a padded grid of every
+ *                sequence x the longest context's partitions, where the empty
+ *                ones exit at once.  Entries out of range are skipped; a plan
+ *                that omits a real partition leaves that part of the output
+ *                unset.
  *   workspace    device scratch of at least
  *                attn_decode_paged_workspace_size(...) bytes (same arguments)
  * ---------------------------------------------------------------------- */
@@ -178,7 +187,19 @@ ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v
                       int32_t head_dim, int32_t block_size, int32_t num_blocks,
                       int32_t max_blocks_per_seq, int32_t max_context_len,
                       int32_t partition_size, float scale, attn_dtype dtype,
+                      const int32_t* plan, int32_t plan_items,
                       void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+/* Host-side plan of a decode launch (host memory only, no HIP call): the
+ * (sequence, partition) pairs of the sequences' contexts, longest sequences
+ * first, partitions in order, with the partition size attn_decode_paged
+ * uses for the same arguments.  context_lens: host int32 [num_seqs] (clamped
+ * to max_context_len).  Returns the number of pairs; writes them to items
+ * (int32 [count][2]) only when items is non-NULL and capacity (in pairs)
+ * holds them all.  Negative attn_status on bad arguments. */
+ATTN_API int64_t attn_decode_paged_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                               int32_t max_context_len, int32_t partition_size, int32_t* items,
+                               int64_t capacity);
 
 /* Partition size that attn_decode_paged uses when partition_size is 0. */
 ATTN_API int32_t attn_decode_paged_auto_partition(int32_t num_seqs, int32_t num_kv_heads,

@@ -29,7 +29,7 @@ def declared_symbols():
 
 def test_header_declares_entry_points():
     syms = declared_symbols()
-    for name in ("attn_prefill", "attn_prefill_paged", "attn_prefill_workspace_size",
+    for name in ("attn_prefill", "attn_prefill_paged", "attn_prefill_workspace_size", "attn_decode_paged_plan",
                  "attn_prefill_paged_workspace_size", "attn_decode_paged", "attn_decode_paged_workspace_size",
                  "attn_kv_cache_write_rope", "attn_pool_create", "attn_pool_alloc", "attn_pool_free",
                  "attn_pool_retain", "attn_seq_reserve", "attn_last_error"):
@@ -124,11 +124,11 @@ def test_prefill_empty_is_ok_without_launch(lib):
 
 def decode(lib, **kw):
     a = dict(q=P, kc=P, vc=P, bt=P, cl=P, o=P, S=4, hq=12, hkv=2, d=128, bs=16, nb=100, maxb=8, maxctx=128,
-             part=0, scale=0.0, dtype=ATTN_BF16, ws=P, wsb=1 << 30)
+             part=0, scale=0.0, dtype=ATTN_BF16, plan=None, nplan=0, ws=P, wsb=1 << 30)
     a.update(kw)
     return lib.attn_decode_paged(a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["o"], a["S"], a["hq"], a["hkv"],
                                  a["d"], a["bs"], a["nb"], a["maxb"], a["maxctx"], a["part"], a["scale"],
-                                 a["dtype"], a["ws"], a["wsb"], None)
+                                 a["dtype"], a["plan"], a["nplan"], a["ws"], a["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -145,6 +145,10 @@ def decode(lib, **kw):
     (dict(maxctx=4096, maxb=256, part=128, wsb=16), ATTN_E_NOMEM),
     (dict(maxctx=4096, maxb=256, part=128, ws=P + 16), ATTN_E_INVALID),
     (dict(hq=12, hkv=5), ATTN_E_INVALID),
+    (dict(plan=None, nplan=3), ATTN_E_INVALID),       # items without a plan
+    (dict(plan=P, nplan=-1), ATTN_E_INVALID),
+    (dict(plan=P + 2, nplan=1), ATTN_E_INVALID),      # misaligned
+    (dict(plan=P, nplan=4 * 1 + 1), ATTN_E_INVALID),  # more items than sequences x partitions
 ])
 def test_decode_rejects(lib, kw, status):
     assert decode(lib, **kw) == status
@@ -158,6 +162,26 @@ def test_decode_workspace_size(lib):
     assert n == ((rows * 128 * 4 + 255) // 256) * 256 + rows * 8
     p = lib.attn_decode_paged_auto_partition(64, 2, 4096)
     assert p % 128 == 0 and 128 <= p <= 1024
+
+
+def test_decode_plan():
+    """The plan lists each sequence's ceil(ctx / P) partitions, longest
+    sequences first, partitions in order, P as the decode launch picks it."""
+    lens = np.array([1000, 5, 0, 3000, 1000, 769], dtype=np.int32)
+    P = 256
+    items = mi.attn_decode_paged_plan(lens, 2, 3000, P)
+    counts = -(-lens // P)
+    assert items.shape == (counts.sum(), 2)
+    order = sorted(range(len(lens)), key=lambda s: -counts[s])   # stable: ties keep their order
+    expect = [(s, p) for s in order for p in range(counts[s])]
+    assert [tuple(x) for x in items] == expect
+    # automatic partition size: the decode's choice for the same arguments
+    auto = mi.attn_decode_paged_auto_partition(len(lens), 2, 3000)
+    assert len(mi.attn_decode_paged_plan(lens, 2, 3000)) == int((-(-lens // auto)).sum())
+    # lengths beyond max_context_len are clamped, as the kernel clamps them
+    assert len(mi.attn_decode_paged_plan(np.array([5000], np.int32), 2, 1024, 512)) == 2
+    with pytest.raises(mi.AttnError):
+        mi.attn_decode_paged_plan(lens, 2, 3000, 100)   # not a multiple of 128
 
 
 def test_paged_prefill_and_write_reject(lib):

@@ -52,6 +52,30 @@ def test_split_kv_partition_sizes(part):
     check(f64(o), oracle_decode(case), torch.bfloat16, f"partition {part}")
 
 
+@pytest.mark.parametrize("part", [0, 128])
+def test_planned_grid_equals_padded(part):
+    """The planned launch (only the real partitions, longest sequences first)
+    gives the padded grid's output bit for bit; plan entries out of range are
+    skipped."""
+    say(f"case: planned decode, partition {part}")
+    case = decode_case(33, 40, 1, 9000, dist="loguniform")
+    kc, vc = build_decode_pool(case, DEV)
+    q = case.q.to(DEV)
+    bt = torch.from_numpy(case.block_tables).to(DEV)
+    cl = torch.from_numpy(case.lengths.astype(np.int32)).to(DEV)
+    mx = int(case.lengths.max())
+    o_pad = mi.attn_decode_paged(q, kc, vc, bt, cl, mx, partition_size=part)
+    items = mi.attn_decode_paged_plan(case.lengths, case.hkv, mx, part)
+    o_plan = mi.attn_decode_paged(q, kc, vc, bt, cl, mx, partition_size=part,
+                                  plan=torch.from_numpy(items).to(DEV))
+    junk = np.concatenate([items, np.array([[-1, 0], [0, 99999], [len(case.lengths), 0], [3, -2]], np.int32)])
+    o_junk = mi.attn_decode_paged(q, kc, vc, bt, cl, mx, partition_size=part, plan=torch.from_numpy(junk).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(o_plan.view(torch.int16), o_pad.view(torch.int16))
+    assert torch.equal(o_junk.view(torch.int16), o_pad.view(torch.int16))
+    check(f64(o_plan), oracle_decode(case), torch.bfloat16, "planned")
+
+
 @pytest.mark.parametrize("d", [128, 64])
 def test_merge_of_many_partitions(d):
     """Long contexts cut into 128-token partitions (up to 157 per sequence):

@@ -20,6 +20,7 @@ __all__ = [
     "Pool",
     "attn_decode_paged",
     "attn_decode_paged_auto_partition",
+    "attn_decode_paged_plan",
     "attn_decode_paged_workspace_size",
     "attn_kv_cache_write_rope",
     "attn_last_error",
@@ -56,8 +57,9 @@ _SIGNATURES = {
     "attn_decode_paged_workspace_size": (ctypes.c_size_t, [_c_i32] * 6),
     "attn_decode_paged_auto_partition": (_c_i32, [_c_i32] * 3),
     "attn_decode_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
-                                         _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp,
-                                         ctypes.c_size_t, _vp]),
+                                         _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp, _c_i32,
+                                         _vp, ctypes.c_size_t, _vp]),
+    "attn_decode_paged_plan": (ctypes.c_int64, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32p, ctypes.c_int64]),
     "attn_kv_cache_write_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                                 _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp]),
     "attn_pool_create": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_vp)]),
@@ -220,12 +222,31 @@ def attn_decode_paged_auto_partition(num_seqs, num_kv_heads, max_context_len) ->
     return int(load().attn_decode_paged_auto_partition(num_seqs, num_kv_heads, max_context_len))
 
 
+def attn_decode_paged_plan(context_lens, num_kv_heads, max_context_len, partition_size=0):
+    """Host-side plan: int32 numpy array [n, 2] of (sequence, partition)
+    pairs, longest sequences first; move it to the GPU for attn_decode_paged."""
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    lib = load()
+    ptr = cl.ctypes.data_as(_c_i32p)
+    n = int(lib.attn_decode_paged_plan(ptr, cl.shape[0], num_kv_heads, int(max_context_len), int(partition_size),
+                                       None, 0))
+    if n < 0:
+        raise AttnError(n, attn_last_error())
+    items = np.zeros((max(n, 1), 2), dtype=np.int32)
+    m = int(lib.attn_decode_paged_plan(ptr, cl.shape[0], num_kv_heads, int(max_context_len), int(partition_size),
+                                       items.ctypes.data_as(_c_i32p), n))
+    _check(0 if m == n else ATTN_E_INVALID)
+    return items[:n]
+
+
 def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_context_len, o=None,
-                      partition_size=0, scale=0.0, workspace=None):
+                      partition_size=0, scale=0.0, workspace=None, plan=None):
     """Decode: q [S, Hq, D], one query per sequence, over the paged caches.
 
     ``workspace`` is a uint8 GPU tensor of at least
-    attn_decode_paged_workspace_size(...) bytes; allocated here if None."""
+    attn_decode_paged_workspace_size(...) bytes; allocated here if None.
+    ``plan``: optional int32 GPU tensor [n, 2] from attn_decode_paged_plan
+    (same lengths and arguments)."""
     if o is None:
         o = torch.empty_like(q)
     s, hq, d = q.shape
@@ -238,7 +259,9 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
     st = load().attn_decode_paged(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
         _dev(context_lens, "context_lens"), _dev(o, "o"), s, hq, hkv, d, bs, nb, block_table.shape[1],
-        int(max_context_len), int(partition_size), float(scale), _dtype_code(q), ws_ptr, ws_bytes, _stream(q))
+        int(max_context_len), int(partition_size), float(scale), _dtype_code(q),
+        _dev(plan, "plan") if plan is not None else None, int(plan.shape[0]) if plan is not None else 0,
+        ws_ptr, ws_bytes, _stream(q))
     _check(st)
     return o
 

@@ -13,6 +13,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <vector>
 
 #include "kernels.h"
 #include "mi_attn.h"
@@ -350,12 +351,49 @@ extern "C" size_t attn_decode_paged_workspace_size(int32_t num_seqs, int32_t num
   return gm.o_bytes + gm.ml_bytes;
 }
 
+extern "C" int64_t attn_decode_paged_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                          int32_t max_context_len, int32_t partition_size, int32_t* items,
+                                          int64_t capacity) {
+  static const char* fn = "attn_decode_paged_plan";
+  if (num_seqs < 0 || num_kv_heads < 1 || max_context_len < 1 || capacity < 0 || (num_seqs > 0 && !context_lens))
+    return fail(ATTN_E_INVALID, "%s: bad argument", fn);
+  if (partition_size < 0 || partition_size % 128 != 0 || partition_size > 1024)
+    return fail(ATTN_E_INVALID, "%s: partition_size must be 0 or a multiple of 128 up to 1024", fn);
+  const int32_t part = partition_size > 0 ? partition_size
+                                          : attn_decode_paged_auto_partition(num_seqs, num_kv_heads, max_context_len);
+  // the kernel's own view of a context: clamped to max_context_len
+  auto parts_of = [&](int32_t s) {
+    const int64_t ctx = std::min<int64_t>(std::max(context_lens[s], 0), max_context_len);
+    return (ctx + part - 1) / part;
+  };
+  int64_t count = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) count += parts_of(s);
+  if (items == nullptr || capacity < count) {
+    ok();
+    return count;
+  }
+  // longest sequences first: their partitions start together
+  std::vector<int32_t> order(num_seqs);
+  for (int32_t s = 0; s < num_seqs; ++s) order[s] = s;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return parts_of(x) > parts_of(y); });
+  int64_t k = 0;
+  for (int32_t s : order)
+    for (int64_t p = 0; p < parts_of(s); ++p) {
+      items[2 * k] = s;
+      items[2 * k + 1] = (int32_t)p;
+      ++k;
+    }
+  ok();
+  return count;
+}
+
 extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
                                  const int32_t* block_table, const int32_t* context_lens, void* o,
                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                  int32_t max_blocks_per_seq, int32_t max_context_len,
                                  int32_t partition_size, float scale, attn_dtype dtype,
+                                 const int32_t* plan, int32_t plan_items,
                                  void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   static const char* fn = "attn_decode_paged";
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !o)
@@ -377,9 +415,13 @@ extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void*
   const void* ptrs[] = {q, k_cache, v_cache, o};
   for (const void* p : ptrs)
     if (!aligned(p, 16)) return fail(ATTN_E_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
-  if (!aligned(block_table, 4) || !aligned(context_lens, 4))
+  if (!aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(plan, 4))
     return fail(ATTN_E_INVALID, "%s: int32 arrays must be 4-byte aligned", fn);
+  if (plan_items < 0 || (plan == nullptr && plan_items != 0))
+    return fail(ATTN_E_INVALID, "%s: plan_items must be >= 0, and 0 without a plan", fn);
   DecodeGeom gm = decode_geom(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
+  if (plan != nullptr && (int64_t)plan_items > (int64_t)num_seqs * gm.max_parts)
+    return fail(ATTN_E_INVALID, "%s: plan_items %d exceeds num_seqs x partitions", fn, plan_items);
   const size_t need = gm.o_bytes + gm.ml_bytes;
   if (need > 0) {
     if (!workspace) return fail(ATTN_E_INVALID, "%s: workspace of %zu bytes required", fn, need);
@@ -400,6 +442,10 @@ extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void*
   a.part_size = gm.part; a.max_parts = gm.max_parts;
   a.num_blocks = num_blocks;
   a.scale_log2 = scale_log2;
+  a.plan = plan;
+  a.plan_items = plan_items;
+  if ((int64_t)plan_items * num_kv_heads * a.head_groups > INT32_MAX)
+    return fail(ATTN_E_UNSUPPORTED, "%s: plan too large for one launch", fn);
   if ((int64_t)num_kv_heads * a.head_groups > 65535 || num_seqs > 65535)
     return fail(ATTN_E_UNSUPPORTED, "%s: at most 65535 sequences (and kv head slices) per call", fn);
   return launched(launch_decode(a, head_dim, reinterpret_cast<hipStream_t>(stream)), fn);

@@ -9,7 +9,8 @@
 // merged exactly by rescaling each partition with exp(m_p - max m).
 //
 // Partition kernel: one workgroup of 4 wavefronts per (partition, kv head
-// [x 16-head slice], sequence).  Each wavefront takes every fourth 16-token
+// [x 16-head slice], sequence), over a padded grid or a host-built list of
+// the real (sequence, partition) items.  Each wavefront takes every fourth 16-token
 // block of the partition and keeps two blocks' loads in flight while it
 // consumes a third; the block-table entries of the partition come in with one
 // lane-parallel load.  Per block:
@@ -64,17 +65,15 @@ __device__ __forceinline__ void load_block(BlockRegs<D>& r, const __bf16* kb, co
 // XCDs round-robin in dispatch order; the partition dimension is padded to an
 // odd size so that partition p lands on a different XCD for each sequence
 // (with a multiple of 8, short contexts would load only a few XCDs).
-template <int D>
-__global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeArgs a) {
-  const int p = blockIdx.x;
-  const int s = blockIdx.z;
+template <int D, int DWT>
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, const int yy, const int s, char* lds) {
   // the grid and the block table bound what a malformed length can reach
   const int ctx = min(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize));
   const int nparts = (ctx + a.part_size - 1) / a.part_size;
   if (p >= nparts) return;
 
-  const int kvh = blockIdx.y / a.head_groups;
-  const int hgi = blockIdx.y % a.head_groups;
+  const int kvh = yy / a.head_groups;
+  const int hgi = yy % a.head_groups;
   const int head0 = kvh * a.group + hgi * 16;
   const int nh = min(16, a.group - hgi * 16);
 
@@ -176,7 +175,7 @@ __global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeA
     for (int dt = 0; dt < D / 16; ++dt) oacc[dt] = mfma16k16(__builtin_bit_cast(v4i16, r.v[dt]), pbi, oacc[dt]);
   };
 
-  // ---- this wavefront's blocks: blk_begin + wave, + DW, ...; three register
+  // ---- this wavefront's blocks: blk_begin + wave, + DWT, ...; three register
   // buffers keep two blocks in flight while one is consumed
   // (the scheduling barriers pin the issue order of the load groups, which
   // the wait counters rely on: loads retire in issue order)
@@ -186,30 +185,30 @@ __global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeA
   block_ptrs(first, kb, vb);
   load_block<D>(r0, kb, vb);
   __builtin_amdgcn_sched_barrier(0);
-  block_ptrs(first + DW, kb, vb);
+  block_ptrs(first + DWT, kb, vb);
   load_block<D>(r1, kb, vb);
   __builtin_amdgcn_sched_barrier(0);
-  for (int blk = first; blk < blk_end; blk += 3 * DW) {
-    block_ptrs(blk + 2 * DW, kb, vb);
+  for (int blk = first; blk < blk_end; blk += 3 * DWT) {
+    block_ptrs(blk + 2 * DWT, kb, vb);
     load_block<D>(r2, kb, vb);
     __builtin_amdgcn_sched_barrier(0);
     consume(r0, blk);
-    if (blk + DW >= blk_end) break;
-    block_ptrs(blk + 3 * DW, kb, vb);
+    if (blk + DWT >= blk_end) break;
+    block_ptrs(blk + 3 * DWT, kb, vb);
     load_block<D>(r0, kb, vb);
     __builtin_amdgcn_sched_barrier(0);
-    consume(r1, blk + DW);
-    if (blk + 2 * DW >= blk_end) break;
-    block_ptrs(blk + 4 * DW, kb, vb);
+    consume(r1, blk + DWT);
+    if (blk + 2 * DWT >= blk_end) break;
+    block_ptrs(blk + 4 * DWT, kb, vb);
     load_block<D>(r1, kb, vb);
     __builtin_amdgcn_sched_barrier(0);
-    consume(r2, blk + 2 * DW);
+    consume(r2, blk + 2 * DWT);
   }
 
   // ---- combine the wavefronts (lane holds head `col`, channels 16dt + 4*g4 .. +3)
-  __shared__ float sm_m[DW][16];
-  __shared__ float sm_l[DW][16];
-  __shared__ f32x4 sm_o[DW][D / 16][4][17];  // [wave][dt][g4][head], padded
+  float (*sm_m)[16] = reinterpret_cast<float (*)[16]>(lds);
+  float (*sm_l)[16] = reinterpret_cast<float (*)[16]>(lds + DWT * 16 * 4);
+  f32x4 (*sm_o)[D / 16][4][17] = reinterpret_cast<f32x4 (*)[D / 16][4][17]>(lds + DWT * 16 * 8);
   float l_all = l_run + xor16(l_run);
   l_all += xor32(l_all);
   if (g4 == 0) {
@@ -222,17 +221,17 @@ __global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeA
 
   // thread = (head, 4 channels)
   const bool single = nparts == 1;
-  for (int t = tid; t < nh * (D / 4); t += 64 * DW) {
+  for (int t = tid; t < nh * (D / 4); t += 64 * DWT) {
     const int hl = t / (D / 4), d4 = t % (D / 4);
     const int dt = d4 >> 2, gg = d4 & 3;
     float mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < DW; ++w) mx = fmaxf(mx, sm_m[w][hl]);
+    for (int w = 0; w < DWT; ++w) mx = fmaxf(mx, sm_m[w][hl]);
     const float mu = (mx == -INFINITY) ? 0.f : mx;
     float lsum = 0.f;
     f32x4 osum = f32x4{};
 #pragma unroll
-    for (int w = 0; w < DW; ++w) {
+    for (int w = 0; w < DWT; ++w) {
       const float f = __builtin_amdgcn_exp2f((sm_m[w][hl] - mu) * c2);
       lsum = fmaf(f, sm_l[w][hl], lsum);
       osum += f * sm_o[w][dt][gg][hl];
@@ -251,6 +250,35 @@ __global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeA
       }
     }
   }
+}
+
+// LDS of a DWT-wavefront workgroup's combine: per wave 16 maxima, 16 sums and
+// a padded (dt, g4, head) block of partial outputs
+template <int D, int DWT>
+constexpr int decode_lds_bytes() { return DWT * 16 * 8 + DWT * (D / 16) * 4 * 17 * 16; }
+
+// Padded grid (partition, kv slice, sequence): partitions past a sequence's
+// context exit at once.
+template <int D>
+__global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[decode_lds_bytes<D, DW>()];
+  decode_body<D, DW>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+}
+
+// Planned grid: workgroup = (item, kv slice), item = (sequence, partition)
+// from a list built on the host (attn_decode_paged_plan), longest sequences
+// first.  Only real partitions are dispatched: the padded grid's empty
+// workgroups (most of it for a batch of mixed lengths) each take a CU slot
+// on their way out.  Entries out of range are skipped.
+template <int D>
+__global__ __launch_bounds__(64 * DW) void decode_planned_kernel(const DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) char lds[decode_lds_bytes<D, DW>()];
+  const int Y = a.hkv * a.head_groups;
+  const int yy = (int)(blockIdx.x % (uint32_t)Y);
+  const int it = (int)(blockIdx.x / (uint32_t)Y);
+  const int s = a.plan[2 * it], p = a.plan[2 * it + 1];
+  if (s < 0 || s >= a.num_seqs || p < 0 || p >= a.max_parts) return;
+  decode_body<D, DW>(a, p, yy, s, lds);
 }
 
 // Merge kernel: workgroup = (query head, sequence).
@@ -341,6 +369,20 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const Decod
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t st) {
   dim3 grid1(a.max_parts | 1, a.hkv * a.head_groups, a.num_seqs);
   dim3 grid2(a.hq, a.num_seqs);
+  if (a.plan != nullptr) {
+    const dim3 gp((uint32_t)a.plan_items * (uint32_t)(a.hkv * a.head_groups));
+    if (a.plan_items > 0) {
+      if (head_dim == 128) hipLaunchKernelGGL(decode_planned_kernel<128>, gp, dim3(64 * DW), 0, st, a);
+      else hipLaunchKernelGGL(decode_planned_kernel<64>, gp, dim3(64 * DW), 0, st, a);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    if (a.max_parts > 1) {
+      if (head_dim == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid2, dim3(kMergeThreads), 0, st, a);
+      else hipLaunchKernelGGL(decode_merge_kernel<64>, grid2, dim3(kMergeThreads), 0, st, a);
+    }
+    return hipGetLastError();
+  }
   if (head_dim == 128) {
     hipLaunchKernelGGL(decode_partition_kernel<128>, grid1, dim3(64 * DW), 0, st, a);
     hipError_t e = hipGetLastError();

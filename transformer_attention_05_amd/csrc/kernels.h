@@ -56,6 +56,8 @@ struct DecodeArgs {
   int32_t part_size, max_parts;
   int32_t num_blocks;  // pool size; out-of-range table entries read as zeros
   float scale_log2;
+  const int32_t* plan;  // [plan_items][2] (sequence, partition), or null: padded grid
+  int32_t plan_items;
 };
 
 struct RopeWriteArgs {

@@ -24,8 +24,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (Pool, attn_decode_paged, attn_decode_paged_workspace_size, attn_kv_cache_write_rope,
-               attn_prefill_paged, attn_prefill_paged_workspace_size)
+from . import (Pool, attn_decode_paged, attn_decode_paged_plan, attn_decode_paged_workspace_size,
+               attn_kv_cache_write_rope, attn_prefill_paged, attn_prefill_paged_workspace_size)
 
 
 class MixedStep:
@@ -70,6 +70,10 @@ class MixedStep:
         self.o_decode = torch.empty(S, case.hq, d, dtype=dt, device=device)
         need = attn_decode_paged_workspace_size(S, case.hq, hkv, d, self.max_dec_ctx, partition_size)
         self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        # decode plan: the real (sequence, partition) pairs, built on the host
+        # from the host copy of the lengths, as the block tables are
+        self.plan = (torch.from_numpy(attn_decode_paged_plan(case.dec_lengths, hkv, self.max_dec_ctx,
+                                                             partition_size)).to(device) if S else None)
         # split-KV workspace of the chunked prefill (its own: the two run at once)
         self.max_pre_ctx = int((case.cached + case.chunk).max()) if R else 1
         need = attn_prefill_paged_workspace_size(R, max(self.n_prefill, 1), case.chunk, self.max_pre_ctx, case.hq,
@@ -96,7 +100,7 @@ class MixedStep:
         R = self.R
         attn_decode_paged(self.q[self.n_prefill:], self.k_cache, self.v_cache, self.tables[R:],
                           self.context_lens[R:], self.max_dec_ctx, o=self.o_decode,
-                          partition_size=self.partition_size, workspace=self.workspace)
+                          partition_size=self.partition_size, workspace=self.workspace, plan=self.plan)
 
     def run(self):
         if self.concurrent and self.R and self.S:
