@@ -155,10 +155,11 @@ ATTN_API int attn_prefill_paged(const void* q, const void* k_cache, const void* 
  * §FlashAttention-Style Kernels: decode has one new query per request and is
  * dominated by reading the growing KV cache; §Paged Attention Kernels: the
  * kernel follows the block table.  Each sequence's context is cut into
- * partitions of `partition_size` tokens.  One pass computes, per partition,
- * the partition's running max m, sum l and unnormalised output; a merge pass
- * combines the partitions exactly (each rescaled by exp(m_p - max_p m_p)).
- * A sequence with one partition is finished by the first pass.
+ * partitions of `partition_size` tokens.  One workgroup per partition (and
+ * kv head slice) computes the partition's running max m, sum l and
+ * unnormalised output; the last of a sequence's workgroups to finish combines
+ * the partitions exactly (each rescaled by exp(m_p - max_p m_p)).  A sequence
+ * with one partition needs no combination.  One kernel launch per call.
  *
  *   q            device bf16 [num_seqs][num_q_heads][head_dim]
  *   block_table  device int32 [num_seqs][max_blocks_per_seq]
@@ -175,8 +176,15 @@ ATTN_API int attn_prefill_paged(const void* q, const void* k_cache, const void* 
  *                ones exit at once.  Entries out of range are skipped; a plan
  *                that omits a real partition leaves that part of the output
  *                unset.
- *   workspace    device scratch of at least
- *                attn_decode_paged_workspace_size(...) bytes (same arguments)
+ *   workspace    device scratch (256-byte aligned) of at least
+ *                attn_decode_paged_workspace_size(...) bytes (same arguments),
+ *                needed when that size is non-zero.  It begins with arrival
+ *                counters that must be ZERO before the first call that uses
+ *                the workspace (fill it with zeros once after allocating);
+ *                every completed call leaves them zero again, so the same
+ *                workspace serves later calls of any shape that fits.  Calls
+ *                that overlap on one workspace race; a plan that lists a
+ *                partition twice corrupts the counters.
  * ---------------------------------------------------------------------- */
 ATTN_API size_t attn_decode_paged_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t max_context_len,

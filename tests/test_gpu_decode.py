@@ -1,5 +1,6 @@
-"""Parity of the paged decode (attn_decode_paged: partition kernel + merge)
-with the fp64 oracle, plus the paging and split-KV invariants."""
+"""Parity of the paged decode (attn_decode_paged: partitions, merged by the
+last workgroup of each sequence in the same launch) with the fp64 oracle,
+plus the paging and split-KV invariants."""
 
 import numpy as np
 import pytest
@@ -50,6 +51,35 @@ def test_split_kv_partition_sizes(part):
     kc, vc = build_decode_pool(case, DEV)
     o = run_decode(case, kc, vc, partition_size=part)
     check(f64(o), oracle_decode(case), torch.bfloat16, f"partition {part}")
+
+
+def test_workspace_counters_reset_and_reuse():
+    """The arrival counters at the head of the decode workspace are zero after
+    every call, so one workspace serves consecutive calls of different shapes:
+    a long batch, then a smaller one with shorter contexts, then the first
+    again, each equal to the oracle (and the repeat bit-identical)."""
+    say("case: decode workspace reuse")
+    big = decode_case(41, 20, 1, 3000)
+    small = decode_case(42, 7, 1, 700)
+    part = 128
+    need = mi.attn_decode_paged_workspace_size(20, 12, 2, 128, int(big.lengths.max()), part)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    outs = []
+    for case in (big, small, big):
+        kc, vc = build_decode_pool(case, DEV)
+        q = case.q.to(DEV)
+        bt = torch.from_numpy(case.block_tables).to(DEV)
+        cl = torch.from_numpy(case.lengths.astype(np.int32)).to(DEV)
+        mx = int(case.lengths.max())
+        assert mi.attn_decode_paged_workspace_size(len(case.lengths), 12, 2, 128, mx, part) <= need
+        plan = torch.from_numpy(mi.attn_decode_paged_plan(case.lengths, 2, mx, part)).to(DEV)
+        o = mi.attn_decode_paged(q, kc, vc, bt, cl, mx, partition_size=part, workspace=ws, plan=plan)
+        torch.cuda.synchronize()
+        # counters: one int32 per (sequence, kv head) at the start of the workspace
+        assert int(ws[:20 * 2 * 4].view(torch.int32).abs().sum().item()) == 0
+        check(f64(o.cpu()), oracle_decode(case), torch.bfloat16, f"reuse {len(case.lengths)} seqs, max {mx}")
+        outs.append(o.cpu())
+    assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
 
 
 @pytest.mark.parametrize("part", [0, 128])

@@ -244,7 +244,9 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
     """Decode: q [S, Hq, D], one query per sequence, over the paged caches.
 
     ``workspace`` is a uint8 GPU tensor of at least
-    attn_decode_paged_workspace_size(...) bytes; allocated here if None.
+    attn_decode_paged_workspace_size(...) bytes, zero-filled before its first
+    use (every completed call leaves its counters zero again); allocated here,
+    zeroed, if None.
     ``plan``: optional int32 GPU tensor [n, 2] from attn_decode_paged_plan
     (same lengths and arguments)."""
     if o is None:
@@ -253,7 +255,7 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
     nb, hkv, bs, _ = k_cache.shape
     need = attn_decode_paged_workspace_size(s, hq, hkv, d, int(max_context_len), int(partition_size))
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().attn_decode_paged(

@@ -323,9 +323,13 @@ extern "C" int32_t attn_decode_paged_auto_partition(int32_t num_seqs, int32_t nu
 }
 
 namespace {
+// Decode workspace, used only when a context can span several partitions:
+// the arrival counters (one int32 per sequence and kv head slice, zero
+// between calls), then the partial outputs, then the (m, l) pairs.
 struct DecodeGeom {
   int32_t part, max_parts;
-  size_t o_bytes, ml_bytes;
+  size_t cnt_bytes, o_bytes, ml_bytes;
+  size_t total() const { return cnt_bytes + o_bytes + ml_bytes; }
 };
 
 DecodeGeom decode_geom(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int32_t max_ctx, int32_t part) {
@@ -333,6 +337,8 @@ DecodeGeom decode_geom(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int
   gm.part = part > 0 ? part : attn_decode_paged_auto_partition(num_seqs, hkv, max_ctx);
   gm.max_parts = ceil_div(max_ctx, gm.part);
   if (gm.max_parts > 1) {
+    const size_t slices = (size_t)hkv * ceil_div(hq / hkv, 16);
+    gm.cnt_bytes = ((size_t)num_seqs * slices * sizeof(int32_t) + 255) / 256 * 256;
     const size_t rows = (size_t)num_seqs * hq * gm.max_parts;
     gm.o_bytes = (rows * d * sizeof(float) + 255) / 256 * 256;
     gm.ml_bytes = rows * 2 * sizeof(float);
@@ -348,7 +354,7 @@ extern "C" size_t attn_decode_paged_workspace_size(int32_t num_seqs, int32_t num
       partition_size < 0)
     return 0;
   DecodeGeom gm = decode_geom(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
-  return gm.o_bytes + gm.ml_bytes;
+  return gm.total();
 }
 
 extern "C" int64_t attn_decode_paged_plan(const int32_t* context_lens, int32_t num_seqs, int32_t num_kv_heads,
@@ -422,7 +428,7 @@ extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void*
   DecodeGeom gm = decode_geom(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
   if (plan != nullptr && (int64_t)plan_items > (int64_t)num_seqs * gm.max_parts)
     return fail(ATTN_E_INVALID, "%s: plan_items %d exceeds num_seqs x partitions", fn, plan_items);
-  const size_t need = gm.o_bytes + gm.ml_bytes;
+  const size_t need = gm.total();
   if (need > 0) {
     if (!workspace) return fail(ATTN_E_INVALID, "%s: workspace of %zu bytes required", fn, need);
     if (!aligned(workspace, 256)) return fail(ATTN_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
@@ -435,8 +441,10 @@ extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void*
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
   a.block_table = block_table; a.bt_stride = max_blocks_per_seq;
   a.context_lens = context_lens; a.o = o;
-  a.ws_o = need ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + gm.o_bytes) : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.counters = need ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  a.ws_o = need ? reinterpret_cast<float*>(ws + gm.cnt_bytes) : nullptr;
+  a.ws_ml = need ? reinterpret_cast<float*>(ws + gm.cnt_bytes + gm.o_bytes) : nullptr;
   a.num_seqs = num_seqs; a.hq = num_q_heads; a.hkv = num_kv_heads;
   a.group = group; a.head_groups = ceil_div(group, 16);
   a.part_size = gm.part; a.max_parts = gm.max_parts;

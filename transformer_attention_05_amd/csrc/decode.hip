@@ -1,5 +1,5 @@
 // Paged decode for gfx950: one query token per sequence against its paged
-// KV cache, split into partitions of the context plus a merge pass.
+// KV cache, split into partitions of the context that are merged in the same launch.
 //
 // "Fast Attention Kernels and Operator Fusion": decode has one or a few new
 // queries per request and is dominated by reading the growing KV cache
@@ -24,9 +24,10 @@
 //     4 tokens) is one 8-byte load, and P passes from the S accumulator to
 //     the B operand without any data movement.
 // The wavefronts are combined through LDS.  A sequence with a single
-// partition writes its output directly; otherwise
-// the (m, l, O) partials go to the workspace and the merge kernel combines
-// them.
+// partition writes its output directly; otherwise the (m, l, O) partials go
+// to the workspace, and the last workgroup of the sequence's kv slice to
+// finish (an arrival counter in the workspace) merges them, so the decode is
+// one launch.
 
 #include <math.h>
 
@@ -58,6 +59,75 @@ __device__ __forceinline__ void load_block(BlockRegs<D>& r, const __bf16* kb, co
   for (int c = 0; c < D / 32; ++c) r.k[c] = *reinterpret_cast<const bf16x8*>(kb + 32 * c);
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) r.v[dt] = *reinterpret_cast<const u32x2*>(vb + 16 * dt * kBlockSize);
+}
+
+// The partials cross workgroups (and XCDs, whose L2 caches are not coherent
+// with each other) inside one launch.  They are written and read as
+// device-scope relaxed atomics, which go to the device's coherence point
+// instead of the XCD's L2, so no cache writeback or invalidation is needed:
+// a workgroup's partial stores are complete (vmcnt 0) before its arrival is
+// counted, and the merging workgroup reads them after the count.
+__device__ __forceinline__ void store_coherent(float* p, float x, float y) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, f32x2{x, y}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 load_coherent(const float* p) {
+  return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Merge of one sequence's partitions for the query heads head0 .. head0+nh-1:
+// O = sum_p f_p O_p / sum_p f_p l_p with f_p = exp(m_p - max m), taken as one
+// online pass over batches of MK partitions whose loads are all in flight at
+// once (the merge is bound by load latency).  Thread = (head, four channels).
+template <int D>
+__device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int head0, int nh, int nparts,
+                                               int tid, int nthreads) {
+  constexpr int CG = D / 4;  // four-channel groups per head
+  constexpr int MK = 8;
+  const float c2 = a.scale_log2;
+  for (int t = tid; t < nh * CG; t += nthreads) {
+    const int hl = t / CG, cg = t % CG;
+    const int64_t row = (int64_t)s * a.hq + head0 + hl;
+    const float* ml = a.ws_ml + row * a.max_parts * 2;
+    const float* po = a.ws_o + row * a.max_parts * D + 4 * cg;
+    float mx = -INFINITY, lsum = 0.f;
+    f32x4 acc = f32x4{};
+    for (int p0 = 0; p0 < nparts; p0 += MK) {
+      f32x4 ov[MK];
+      f32x2 mlv[MK];
+#pragma unroll
+      for (int k = 0; k < MK; ++k) {
+        const int p = p0 + k;
+        if (p < nparts) {
+          const f32x2 lo = load_coherent(po + (int64_t)p * D), hi = load_coherent(po + (int64_t)p * D + 2);
+          ov[k] = f32x4{lo[0], lo[1], hi[0], hi[1]};
+          mlv[k] = load_coherent(ml + 2 * p);
+        } else {
+          ov[k] = f32x4{};
+          mlv[k] = f32x2{-INFINITY, 0.f};
+        }
+      }
+      float bm = mlv[0][0];
+#pragma unroll
+      for (int k = 1; k < MK; ++k) bm = fmaxf(bm, mlv[k][0]);
+      const float mn = fmaxf(mx, bm);
+      const float mu = mn == -INFINITY ? 0.f : mn;
+      const float f_old = __builtin_amdgcn_exp2f((mx - mu) * c2);  // 0 while mx is -inf
+      lsum *= f_old;
+      acc *= f_old;
+#pragma unroll
+      for (int k = 0; k < MK; ++k) {
+        const float f = __builtin_amdgcn_exp2f((mlv[k][0] - mu) * c2);  // 0 past nparts (m = -inf)
+        acc += f * ov[k];
+        lsum = fmaf(f, mlv[k][1], lsum);
+      }
+      mx = mn;
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + row * D + 4 * cg) =
+        u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  }
 }
 
 // Grid (partition, kv head x head slice, sequence), partitions fastest so a
@@ -243,13 +313,30 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, co
       *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + row * D + 4 * d4) = w2;
     } else {
       const int64_t slot = row * a.max_parts + p;
-      *reinterpret_cast<f32x4*>(a.ws_o + slot * D + 4 * d4) = osum;
-      if (d4 == 0) {
-        a.ws_ml[slot * 2 + 0] = mx;
-        a.ws_ml[slot * 2 + 1] = lsum;
-      }
+      store_coherent(a.ws_o + slot * D + 4 * d4, osum[0], osum[1]);
+      store_coherent(a.ws_o + slot * D + 4 * d4 + 2, osum[2], osum[3]);
+      if (d4 == 0) store_coherent(a.ws_ml + slot * 2, mx, lsum);
     }
   }
+  if (single) return;
+
+  // ---- arrival: every partial store of the workgroup has completed before
+  // the count; the workgroup that brings the count to nparts merges, then
+  // restores the counter to its value before the call (zero), for the next
+  // call
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // every thread's partials, and the combine's LDS reads, are done
+  int* sm_last = reinterpret_cast<int*>(lds);
+  if (tid == 0) {
+    int* cnt = a.counters + (int64_t)s * (a.hkv * a.head_groups) + yy;
+    const int prev = atomicAdd(cnt, 1);
+    const int last = prev == nparts - 1;
+    if (last) atomicSub(cnt, nparts);
+    *sm_last = last;
+  }
+  __syncthreads();
+  if (*sm_last == 0) return;
+  merge_partials<D>(a, s, head0, nh, nparts, tid, 64 * DWT);
 }
 
 // LDS of a DWT-wavefront workgroup's combine: per wave 16 maxima, 16 sums and
@@ -281,119 +368,20 @@ __global__ __launch_bounds__(64 * DW) void decode_planned_kernel(const DecodeArg
   decode_body<D, DW>(a, p, yy, s, lds);
 }
 
-// Merge kernel: workgroup = (query head, sequence).
-// O = sum_p f_p O_p / sum_p f_p l_p with f_p = exp(m_p - max m).  Thread =
-// (four channels, partition group): it takes every MPG-th partition, so the
-// partials' loads of up to MK partitions per thread, and the (m, l) loads,
-// are all in flight at once (the merge is bound by load latency); the
-// partition groups are then summed through LDS.
-constexpr int kMergeThreads = 256;
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const DecodeArgs a) {
-  constexpr int CG = D / 4;                  // channel groups (four channels each)
-  constexpr int MPG = kMergeThreads / CG;    // partition groups
-  constexpr int MK = 8;                      // partitions per thread and pass
-  const int h = blockIdx.x;
-  const int s = blockIdx.y;
-  const int ctx = min(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize));
-  const int nparts = (ctx + a.part_size - 1) / a.part_size;
-  if (nparts <= 1) return;
-  __shared__ float sm_red[kMergeThreads / 64];
-  __shared__ f32x4 sm_acc[MPG][CG];
-  __shared__ float sm_l[MPG];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int cg = tid % CG, pg = tid / CG;
-  const int64_t row = (int64_t)s * a.hq + h;
-  const float* ml = a.ws_ml + row * a.max_parts * 2;
-  const f32x4* po = reinterpret_cast<const f32x4*>(a.ws_o + row * a.max_parts * D) + cg;
-  const float c2 = a.scale_log2;
-
-  // this thread's partitions of the first pass, and every (m) for the max
-  f32x4 ov[MK];
-  f32x2 mlv[MK];
-#pragma unroll
-  for (int k = 0; k < MK; ++k) {
-    const int p = pg + k * MPG;
-    ov[k] = p < nparts ? po[(int64_t)p * CG] : f32x4{};
-    mlv[k] = p < nparts ? *reinterpret_cast<const f32x2*>(ml + 2 * p) : f32x2{-INFINITY, 0.f};
-  }
-  float mx = -INFINITY;
-  for (int i = tid; i < nparts; i += kMergeThreads) mx = fmaxf(mx, ml[2 * i]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-  if (lane == 0) sm_red[wave] = mx;
-  __syncthreads();
-  mx = sm_red[0];
-#pragma unroll
-  for (int w = 1; w < kMergeThreads / 64; ++w) mx = fmaxf(mx, sm_red[w]);
-  const float mu = (mx == -INFINITY) ? 0.f : mx;
-
-  f32x4 acc = f32x4{};
-  float lsum = 0.f;
-  for (int base = 0;; base += MK * MPG) {
-#pragma unroll
-    for (int k = 0; k < MK; ++k) {
-      const float f = __builtin_amdgcn_exp2f((mlv[k][0] - mu) * c2);  // 0 past nparts (m = -inf)
-      acc += f * ov[k];
-      lsum = fmaf(f, mlv[k][1], lsum);
-    }
-    if (base + MK * MPG >= nparts) break;
-    // more partitions than one pass holds (small partitions of a long context)
-#pragma unroll
-    for (int k = 0; k < MK; ++k) {
-      const int p = base + MK * MPG + pg + k * MPG;
-      ov[k] = p < nparts ? po[(int64_t)p * CG] : f32x4{};
-      mlv[k] = p < nparts ? *reinterpret_cast<const f32x2*>(ml + 2 * p) : f32x2{-INFINITY, 0.f};
-    }
-  }
-  sm_acc[pg][cg] = acc;
-  if (cg == 0) sm_l[pg] = lsum;
-  __syncthreads();
-  if (pg == 0) {
-    f32x4 o = sm_acc[0][cg];
-    float l = sm_l[0];
-#pragma unroll
-    for (int g = 1; g < MPG; ++g) {
-      o += sm_acc[g][cg];
-      l += sm_l[g];
-    }
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + row * D + 4 * cg) =
-        u32x2{pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv)};
-  }
-}
-
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t st) {
-  dim3 grid1(a.max_parts | 1, a.hkv * a.head_groups, a.num_seqs);
-  dim3 grid2(a.hq, a.num_seqs);
   if (a.plan != nullptr) {
     const dim3 gp((uint32_t)a.plan_items * (uint32_t)(a.hkv * a.head_groups));
     if (a.plan_items > 0) {
       if (head_dim == 128) hipLaunchKernelGGL(decode_planned_kernel<128>, gp, dim3(64 * DW), 0, st, a);
       else hipLaunchKernelGGL(decode_planned_kernel<64>, gp, dim3(64 * DW), 0, st, a);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
-    }
-    if (a.max_parts > 1) {
-      if (head_dim == 128) hipLaunchKernelGGL(decode_merge_kernel<128>, grid2, dim3(kMergeThreads), 0, st, a);
-      else hipLaunchKernelGGL(decode_merge_kernel<64>, grid2, dim3(kMergeThreads), 0, st, a);
     }
     return hipGetLastError();
   }
-  if (head_dim == 128) {
-    hipLaunchKernelGGL(decode_partition_kernel<128>, grid1, dim3(64 * DW), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.max_parts > 1) hipLaunchKernelGGL(decode_merge_kernel<128>, grid2, dim3(kMergeThreads), 0, st, a);
-  } else {
-    hipLaunchKernelGGL(decode_partition_kernel<64>, grid1, dim3(64 * DW), 0, st, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (a.max_parts > 1) hipLaunchKernelGGL(decode_merge_kernel<64>, grid2, dim3(kMergeThreads), 0, st, a);
-  }
+  const dim3 grid(a.max_parts | 1, a.hkv * a.head_groups, a.num_seqs);
+  if (head_dim == 128) hipLaunchKernelGGL(decode_partition_kernel<128>, grid, dim3(64 * DW), 0, st, a);
+  else hipLaunchKernelGGL(decode_partition_kernel<64>, grid, dim3(64 * DW), 0, st, a);
   return hipGetLastError();
 }
 

@@ -52,6 +52,7 @@ struct DecodeArgs {
   void* o;              // [S][Hq][D]
   float* ws_ml;         // [S][Hq][max_parts][2]  (running max, running sum)
   float* ws_o;          // [S][Hq][max_parts][D]  (unnormalised output)
+  int32_t* counters;    // [S][Hkv * head_groups] partitions finished (zero between calls)
   int32_t num_seqs, hq, hkv, group, head_groups;
   int32_t part_size, max_parts;
   int32_t num_blocks;  // pool size; out-of-range table entries read as zeros

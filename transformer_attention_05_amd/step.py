@@ -69,7 +69,8 @@ class MixedStep:
         self.o_prefill = torch.empty(self.n_prefill, case.hq, d, dtype=dt, device=device)
         self.o_decode = torch.empty(S, case.hq, d, dtype=dt, device=device)
         need = attn_decode_paged_workspace_size(S, case.hq, hkv, d, self.max_dec_ctx, partition_size)
-        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        # zeroed once: the decode's arrival counters start at zero and every call leaves them so
+        self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
         # decode plan: the real (sequence, partition) pairs, built on the host
         # from the host copy of the lengths, as the block tables are
         self.plan = (torch.from_numpy(attn_decode_paged_plan(case.dec_lengths, hkv, self.max_dec_ctx,
