@@ -1,11 +1,14 @@
 """Benchmark of the attention hot path on one MI355X.
 
 A step is one serving step over a shared paged KV cache, the workload that
-touches every stage of the path: the fused RoPE + paged cache write for all
+touches every stage of the path: the fused RoPE + paged cache write of all
 new tokens, chunked prefill of 8 requests (512 new tokens each on 0-2048
 cached tokens) and decode of 128 sequences (context log-uniform in
-[16, 32768]), partitions and merge in one launch; 12 query / 2 kv heads, head_dim 128,
-bf16, 16-token blocks, RoPE base 10000, pool pre-fragmented (seed 1004).
+[16, 32768]), partitions and merge in one launch; 12 query / 2 kv heads,
+head_dim 128, bf16, 16-token blocks, RoPE base 10000, pool pre-fragmented
+(seed 1004).  The decode-only step of the 64-sequence workload is also
+timed both ways: RoPE write then decode, and the decode launch that writes
+its own tokens.
 Inputs are synthetic and already resident in HBM when timing starts.
 
 value = percent of the step's roofline time reached:
@@ -247,6 +250,38 @@ def main():
         by = decode_bytes(dc.lengths)
         out["decode_c3"] = dict(ms=td.mean_ms(), bytes=by, part=mi.attn_decode_paged_auto_partition(64, HKV, mx))
         log(f"bench: decode C3 {td.mean_ms() * 1e3:.1f} us  {by / td.mean_ms() / 1e6:.0f} GB/s")
+        # a decode-only serving step: each sequence's new token (the last of
+        # its context) rotated and written into its slot, then the decode;
+        # as two launches, and as the one decode launch that writes it
+        last = dc.lengths - 1
+        slots_np = (dc.block_tables[np.arange(64), last // 16].astype(np.int64) * 16 + last % 16).astype(np.int32)
+        slots = torch.from_numpy(slots_np).to(dev)
+        pos = torch.from_numpy(last.astype(np.int32)).to(dev)
+        k_new = torch.stack([k[-1] for k in dc.k]).to(dev)
+        v_new = torch.stack([v[-1] for v in dc.v]).to(dev)
+        q_rot = torch.empty_like(qd)
+        q_w = qd.clone()
+
+        def two_launches(i):
+            mi.attn_kv_cache_write_rope(q_w, k_new, v_new, pos, slots, *pools[i % 3])
+            mi.attn_decode_paged(q_w, *pools[i % 3], bt, cl, mx, o=o, workspace=ws, plan=plan)
+
+        def one_launch(i):
+            mi.attn_decode_paged_rope(qd, k_new, v_new, pos, slots, *pools[i % 3], bt, cl, mx, o=o, q_rot_out=q_rot,
+                                      workspace=ws, plan=plan)
+        step_ms = {}
+        for name, fn in (("write_then_decode", two_launches), ("fused", one_launch)):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            tm = EventTimer(torch)
+            for i in range(n):
+                e = tm.start(); fn(i); tm.stop(e)
+            torch.cuda.synchronize()
+            step_ms[name] = tm.mean_ms()
+        out["decode_step_c3"] = dict(bytes=by + write_bytes(64), **step_ms)
+        log(f"bench: decode-only step C3: write + decode {step_ms['write_then_decode'] * 1e3:.1f} us, "
+            f"fused {step_ms['fused'] * 1e3:.1f} us")
         del pools
 
     # ------------------------------------------------------------------ CPU baseline (oracle)
@@ -330,7 +365,8 @@ def emit(args, out, cpu):
                                      "Hq 12 / Hkv 2, D 128, bf16, block 16, fragmented pool, seed 1004",
                          "new_tokens": m["n_new"], "decode_context_tokens": m["dec_tokens"],
                          "pool_blocks": m["pool_blocks"], "decode_partition": m["part"],
-                         "schedule": "write; then chunked prefill and decode on two streams",
+                         "schedule": "chunk tokens' RoPE write then chunked prefill on one stream, beside the "
+                                     "decode tokens' RoPE write then the decode on a second",
                          "parallelism": "single GPU"}
         dec_s = m["ms_decode"] / 1e3
         gbps = m["B_dec"] / dec_s / 1e9
@@ -360,6 +396,14 @@ def emit(args, out, cpu):
         gb = d["bytes"] / (d["ms"] / 1e3) / 1e9
         comps["decode_64seq_U128_4096"] = {"us": round(d["ms"] * 1e3, 2), "GB/s": round(gb, 1),
                                            "frac_of_hbm_peak": round(gb * 1e9 / PEAK_HBM, 4), "partition": d["part"]}
+    if "decode_step_c3" in out:
+        d = out["decode_step_c3"]
+        comps["decode_only_step_64seq"] = {
+            "bytes": d["bytes"],
+            "write_then_decode_us": round(d["write_then_decode"] * 1e3, 2),
+            "fused_us": round(d["fused"] * 1e3, 2),
+            "fused_GB/s": round(d["bytes"] / (d["fused"] / 1e3) / 1e9, 1),
+            "fused_frac_of_hbm_peak": round(d["bytes"] / (d["fused"] / 1e3) / PEAK_HBM, 4)}
     res["components"] = comps
     if "value" not in res:
         res["value"] = None

@@ -198,6 +198,43 @@ ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v
                       const int32_t* plan, int32_t plan_items,
                       void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/* -------------------------------------------------------------------------
+ * attn_decode_paged_rope -- the decode above, with each sequence's new token
+ * rotated and written into the cache by the same launch.
+ *
+ * §Operator Fusion names "applying rotary position embeddings to queries and
+ * keys" and "updating the KV cache while transforming key and value tensors"
+ * as fusions; here they are fused into the decode itself.  Equivalent to
+ * attn_kv_cache_write_rope(q, k_new, v_new, positions, slot_mapping, ...)
+ * (one token per sequence) followed by attn_decode_paged on the rotated q,
+ * with the same rotation arithmetic bit for bit, except that q is not
+ * modified: the rotated queries go to q_rot_out when it is non-NULL.
+ *
+ *   q_rot_out    device bf16 [num_seqs][num_q_heads][head_dim] or NULL; must
+ *                not alias q (other workgroups of a sequence still read q)
+ *   q            device bf16 [num_seqs][num_q_heads][head_dim], NOT rotated
+ *   k_new, v_new device bf16 [num_seqs][num_kv_heads][head_dim]: the new
+ *                token's key (not rotated) and value
+ *   positions    device int32 [num_seqs]: the new token's position (the
+ *                rotation angle); the attention itself follows context_lens
+ *   slot_mapping device int32 [num_seqs]: the new token's slot, which must be
+ *                the slot of logical position context_lens[s] - 1 under the
+ *                sequence's block table; -1 (or a slot outside the pool)
+ *                skips the write, and the cache's current contents are read
+ *   rope_base    0 = no rotation (the write is a plain copy), else > 1
+ *   all other arguments, the workspace contract and the errors as for
+ *   attn_decode_paged; k_cache and v_cache are written.
+ * ---------------------------------------------------------------------- */
+ATTN_API int attn_decode_paged_rope(void* q_rot_out, const void* q, const void* k_new, const void* v_new,
+                           const int32_t* positions, const int32_t* slot_mapping, float rope_base,
+                           void* k_cache, void* v_cache, const int32_t* block_table,
+                           const int32_t* context_lens, void* o, int32_t num_seqs, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                           int32_t partition_size, float scale, attn_dtype dtype, const int32_t* plan,
+                           int32_t plan_items, void* workspace, size_t workspace_bytes,
+                           attn_stream_t stream);
+
 /* Host-side plan of a decode launch (host memory only, no HIP call): the
  * (sequence, partition) pairs of the sequences' contexts, longest sequences
  * first, partitions in order, with the partition size attn_decode_paged

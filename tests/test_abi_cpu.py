@@ -31,6 +31,7 @@ def test_header_declares_entry_points():
     syms = declared_symbols()
     for name in ("attn_prefill", "attn_prefill_paged", "attn_prefill_workspace_size", "attn_decode_paged_plan",
                  "attn_prefill_paged_workspace_size", "attn_decode_paged", "attn_decode_paged_workspace_size",
+                 "attn_decode_paged_rope",
                  "attn_kv_cache_write_rope", "attn_pool_create", "attn_pool_alloc", "attn_pool_free",
                  "attn_pool_retain", "attn_seq_reserve", "attn_last_error"):
         assert name in syms
@@ -152,6 +153,38 @@ def decode(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def decode_rope(lib, **kw):
+    a = dict(qr=None, q=P, kn=P, vn=P, pos=P, slots=P, base=10000.0, kc=P, vc=P, bt=P, cl=P, o=P, S=4, hq=12,
+             hkv=2, d=128, bs=16, nb=100, maxb=8, maxctx=128, part=0, scale=0.0, dtype=ATTN_BF16, plan=None,
+             nplan=0, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.attn_decode_paged_rope(a["qr"], a["q"], a["kn"], a["vn"], a["pos"], a["slots"], a["base"], a["kc"],
+                                      a["vc"], a["bt"], a["cl"], a["o"], a["S"], a["hq"], a["hkv"], a["d"], a["bs"],
+                                      a["nb"], a["maxb"], a["maxctx"], a["part"], a["scale"], a["dtype"], a["plan"],
+                                      a["nplan"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), ATTN_E_INVALID),
+    (dict(vn=None), ATTN_E_INVALID),
+    (dict(pos=None), ATTN_E_INVALID),
+    (dict(slots=None), ATTN_E_INVALID),
+    (dict(base=1.0), ATTN_E_INVALID),
+    (dict(base=-2.0), ATTN_E_INVALID),
+    (dict(base=float("inf")), ATTN_E_INVALID),
+    (dict(kn=P + 2), ATTN_E_INVALID),           # misaligned
+    (dict(pos=P + 2), ATTN_E_INVALID),
+    (dict(qr=P), ATTN_E_INVALID),               # rotated queries may not overwrite q
+    (dict(q=None), ATTN_E_INVALID),             # and the decode's own checks still apply
+    (dict(dtype=ATTN_F32), ATTN_E_UNSUPPORTED),
+    (dict(maxb=7), ATTN_E_INVALID),
+    (dict(maxctx=4096, maxb=256, part=128, wsb=16), ATTN_E_NOMEM),
+])
+def test_decode_rope_rejects(lib, kw, status):
+    assert decode_rope(lib, **kw) == status
+    assert "attn_decode_paged_rope" in mi.attn_last_error()
 
 
 def test_decode_workspace_size(lib):

@@ -138,7 +138,7 @@ def test_mixed_step_small():
     case = mixed_case(77, num_req=3, chunk=100, cached_max=300, num_dec=9, dec_lo=1, dec_hi=3000)
     step = run_mixed(case, partition_size=256)
     pre, dec, _ = mixed_reference(case)
-    check_stored(f64(step.q), oracle.rope(to_f64(case.q_new), case.positions, case.rope_base), torch.bfloat16,
+    check_stored(f64(step.rotated_q()), oracle.rope(to_f64(case.q_new), case.positions, case.rope_base), torch.bfloat16,
                  "rotated q")
     check(f64(step.o_prefill), pre, torch.bfloat16, "mixed prefill")
     check(f64(step.o_decode), dec, torch.bfloat16, "mixed decode")
@@ -147,21 +147,26 @@ def test_mixed_step_small():
     assert not used & set(case.foreign.tolist())
 
 
-def test_concurrent_step_equals_serial():
-    """The two-stream schedule (decode tokens written and decoded on a second
-    stream beside the chunk write and prefill) gives the serial order's
-    outputs, rotated queries and caches bit for bit."""
-    say("case: concurrent vs serial step")
+@pytest.mark.parametrize("fused", [False, True])
+def test_concurrent_step_equals_serial(fused):
+    """The two-stream schedule (the decode tokens written and decoded on a
+    second stream beside the chunk write and prefill, or with the decode
+    writing its own tokens) gives the serial order's outputs, rotated queries
+    and caches bit for bit."""
+    say(f"case: concurrent vs serial step, fused decode write {fused}")
     case = mixed_case(78, num_req=3, chunk=200, cached_max=900, num_dec=20, dec_lo=1, dec_hi=5000)
     steps = []
     for conc in (False, True):
-        st = MixedStep(case, assign_blocks, DEV, scatter=scatter_to_pool, concurrent=conc)
+        st = MixedStep(case, assign_blocks, DEV, scatter=scatter_to_pool, concurrent=conc,
+                       fuse_decode_write=fused)
         st.run()
         torch.cuda.synchronize()
         steps.append(st)
     a, b = steps
-    for name in ("o_prefill", "o_decode", "q", "k_cache", "v_cache"):
+    for name in ("o_prefill", "o_decode", "rotated_q", "k_cache", "v_cache"):
         x, y = getattr(a, name), getattr(b, name)
+        if callable(x):
+            x, y = x(), y()
         assert torch.equal(x.view(torch.int16), y.view(torch.int16)), name
 
 

@@ -20,6 +20,7 @@ __all__ = [
     "Pool",
     "attn_decode_paged",
     "attn_decode_paged_auto_partition",
+    "attn_decode_paged_rope",
     "attn_decode_paged_plan",
     "attn_decode_paged_workspace_size",
     "attn_kv_cache_write_rope",
@@ -59,6 +60,10 @@ _SIGNATURES = {
     "attn_decode_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp, _c_i32,
                                          _vp, ctypes.c_size_t, _vp]),
+    "attn_decode_paged_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                              _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                              _c_i32, ctypes.c_float, ctypes.c_int, _vp, _c_i32, _vp,
+                                              ctypes.c_size_t, _vp]),
     "attn_decode_paged_plan": (ctypes.c_int64, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32p, ctypes.c_int64]),
     "attn_kv_cache_write_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                                 _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp]),
@@ -260,6 +265,35 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().attn_decode_paged(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        _dev(context_lens, "context_lens"), _dev(o, "o"), s, hq, hkv, d, bs, nb, block_table.shape[1],
+        int(max_context_len), int(partition_size), float(scale), _dtype_code(q),
+        _dev(plan, "plan") if plan is not None else None, int(plan.shape[0]) if plan is not None else 0,
+        ws_ptr, ws_bytes, _stream(q))
+    _check(st)
+    return o
+
+
+def attn_decode_paged_rope(q, k_new, v_new, positions, slot_mapping, k_cache, v_cache, block_table, context_lens,
+                           max_context_len, o=None, q_rot_out=None, rope_base=10000.0, partition_size=0, scale=0.0,
+                           workspace=None, plan=None):
+    """Decode with the new token of each sequence rotated and written into
+    the cache by the same launch: q [S, Hq, D] (not rotated, left unchanged),
+    k_new / v_new [S, Hkv, D], positions / slot_mapping [S] int32.  The
+    rotated queries go to ``q_rot_out`` when given.  ``workspace`` and
+    ``plan`` as for attn_decode_paged."""
+    if o is None:
+        o = torch.empty_like(q)
+    s, hq, d = q.shape
+    nb, hkv, bs, _ = k_cache.shape
+    need = attn_decode_paged_workspace_size(s, hq, hkv, d, int(max_context_len), int(partition_size))
+    if workspace is None and need > 0:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().attn_decode_paged_rope(
+        _dev(q_rot_out, "q_rot_out") if q_rot_out is not None else None, _dev(q, "q"), _dev(k_new, "k_new"),
+        _dev(v_new, "v_new"), _dev(positions, "positions"), _dev(slot_mapping, "slot_mapping"), float(rope_base),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
         _dev(context_lens, "context_lens"), _dev(o, "o"), s, hq, hkv, d, bs, nb, block_table.shape[1],
         int(max_context_len), int(partition_size), float(scale), _dtype_code(q),
         _dev(plan, "plan") if plan is not None else None, int(plan.shape[0]) if plan is not None else 0,

@@ -61,6 +61,14 @@ int launched(hipError_t e, const char* fn) {
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
+// theta_i = base^(-2i/D) for the D/2 rotation pairs, in double
+RopeFreqs rope_freqs(float base, int32_t head_dim) {
+  RopeFreqs f{};
+  for (int i = 0; i < head_dim / 2 && i < kMaxRopePairs; ++i)
+    f.theta[i] = std::pow((double)base, -2.0 * (double)i / (double)head_dim);
+  return f;
+}
+
 // Tile shape of the bf16 prefill kernel: two query heads of one kv group per
 // workgroup (each K/V tile serves both) and 128-query tiles unless that
 // leaves most CUs idle.  The
@@ -393,15 +401,24 @@ extern "C" int64_t attn_decode_paged_plan(const int32_t* context_lens, int32_t n
   return count;
 }
 
-extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                                 const int32_t* block_table, const int32_t* context_lens, void* o,
-                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                 int32_t max_blocks_per_seq, int32_t max_context_len,
-                                 int32_t partition_size, float scale, attn_dtype dtype,
-                                 const int32_t* plan, int32_t plan_items,
-                                 void* workspace, size_t workspace_bytes, attn_stream_t stream) {
-  static const char* fn = "attn_decode_paged";
+namespace {
+// The new token of each sequence, rotated and written by the decode launch
+// itself (attn_decode_paged_rope); null for attn_decode_paged.
+struct DecodeWrite {
+  void* q_rot_out;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  float rope_base;
+};
+
+int decode_common(const char* fn, const DecodeWrite* w, const void* q, const void* k_cache, const void* v_cache,
+                  const int32_t* block_table, const int32_t* context_lens, void* o, int32_t num_seqs,
+                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                  int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                  int32_t partition_size, float scale, attn_dtype dtype, const int32_t* plan,
+                  int32_t plan_items, void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !o)
     return fail(ATTN_E_INVALID, "%s: pointer arguments must be non-NULL", fn);
   if (num_seqs < 0 || num_blocks < 1 || max_context_len < 1)
@@ -456,7 +473,58 @@ extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void*
     return fail(ATTN_E_UNSUPPORTED, "%s: plan too large for one launch", fn);
   if ((int64_t)num_kv_heads * a.head_groups > 65535 || num_seqs > 65535)
     return fail(ATTN_E_UNSUPPORTED, "%s: at most 65535 sequences (and kv head slices) per call", fn);
-  return launched(launch_decode(a, head_dim, reinterpret_cast<hipStream_t>(stream)), fn);
+  if (w != nullptr) {
+    a.q_rot_out = w->q_rot_out;
+    a.k_new = w->k_new;
+    a.v_new = w->v_new;
+    a.positions = w->positions;
+    a.slot_mapping = w->slot_mapping;
+    a.rope = w->rope_base > 0.f;
+    if (a.rope) a.freqs = rope_freqs(w->rope_base, head_dim);
+  }
+  return launched(launch_decode(a, head_dim, w != nullptr, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+}  // namespace
+
+extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* block_table, const int32_t* context_lens, void* o,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len,
+                                 int32_t partition_size, float scale, attn_dtype dtype,
+                                 const int32_t* plan, int32_t plan_items,
+                                 void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  return decode_common("attn_decode_paged", nullptr, q, k_cache, v_cache, block_table, context_lens, o, num_seqs,
+                       num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, partition_size, scale, dtype, plan, plan_items, workspace, workspace_bytes,
+                       stream);
+}
+
+extern "C" int attn_decode_paged_rope(void* q_rot_out, const void* q, const void* k_new, const void* v_new,
+                                      const int32_t* positions, const int32_t* slot_mapping, float rope_base,
+                                      void* k_cache, void* v_cache, const int32_t* block_table,
+                                      const int32_t* context_lens, void* o, int32_t num_seqs, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                                      int32_t partition_size, float scale, attn_dtype dtype, const int32_t* plan,
+                                      int32_t plan_items, void* workspace, size_t workspace_bytes,
+                                      attn_stream_t stream) {
+  static const char* fn = "attn_decode_paged_rope";
+  if (!k_new || !v_new || !positions || !slot_mapping)
+    return fail(ATTN_E_INVALID, "%s: k_new, v_new, positions and slot_mapping must be non-NULL", fn);
+  if (!std::isfinite(rope_base) || rope_base < 0.f || (rope_base > 0.f && rope_base <= 1.f))
+    return fail(ATTN_E_INVALID, "%s: rope_base must be 0 (no rotation) or > 1", fn);
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || (q_rot_out && !aligned(q_rot_out, 16)))
+    return fail(ATTN_E_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (!aligned(positions, 4) || !aligned(slot_mapping, 4))
+    return fail(ATTN_E_INVALID, "%s: int32 arrays must be 4-byte aligned", fn);
+  if (q_rot_out != nullptr && q_rot_out == q)
+    return fail(ATTN_E_INVALID, "%s: q_rot_out must not alias q (other workgroups still read q)", fn);
+  if ((int64_t)num_blocks * kBlockSizeHost > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: pool too large", fn);
+  const DecodeWrite w{q_rot_out, k_new, v_new, positions, slot_mapping, rope_base};
+  return decode_common(fn, &w, q, k_cache, v_cache, block_table, context_lens, o, num_seqs, num_q_heads,
+                       num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq, max_context_len,
+                       partition_size, scale, dtype, plan, plan_items, workspace, workspace_bytes, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -489,6 +557,7 @@ extern "C" int attn_kv_cache_write_rope(void* q, const void* k, const void* v, c
   a.k_cache = k_cache; a.v_cache = v_cache;
   a.num_tokens = num_tokens; a.hq = num_q_heads; a.hkv = num_kv_heads;
   a.num_blocks = num_blocks;
-  a.rope_base = (double)rope_base;
+  a.rope = rope_base > 0.f;
+  if (a.rope) a.freqs = rope_freqs(rope_base, head_dim);
   return launched(launch_rope_write(a, head_dim, dtype == ATTN_BF16, reinterpret_cast<hipStream_t>(stream)), fn);
 }

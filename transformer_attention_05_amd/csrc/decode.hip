@@ -135,7 +135,7 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
 // XCDs round-robin in dispatch order; the partition dimension is padded to an
 // odd size so that partition p lands on a different XCD for each sequence
 // (with a multiple of 8, short contexts would load only a few XCDs).
-template <int D, int DWT>
+template <int D, int DWT, bool FUSED>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, const int yy, const int s, char* lds) {
   // the grid and the block table bound what a malformed length can reach
   const int ctx = min(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize));
@@ -186,9 +186,64 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, co
       qreg[c] = col < nh ? *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g4) : bf16x8{};
   }
 
+  // fused RoPE: this lane's cos and sin for pair index `lane` (D/2 pairs)
+  float rc = 1.f, rs = 0.f;
+  if constexpr (FUSED) {
+    if (a.rope) rope_cos_sin(a.positions[s], a.freqs.theta[lane & (D / 2 - 1)], rc, rs);
+  }
+
   // the table and Q^T must be in registers before the block pipeline starts:
   // waiting here keeps the loop's waits to the blocks themselves
   __builtin_amdgcn_s_waitcnt(0);
+
+  if constexpr (FUSED) {
+    // rotate Q^T: the pair (channel i, i + D/2) sits in qreg[c][e] and
+    // qreg[c + D/64][e] of the same lane, i = 32c + 8*g4 + e
+    if (a.rope) {
+#pragma unroll
+      for (int c = 0; c < D / 64; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int src = 32 * c + 8 * g4 + e;
+          const float cc = __shfl(rc, src), ss = __shfl(rs, src);
+          float y1, y2;
+          rope_rotate((float)qreg[c][e], (float)qreg[c + D / 64][e], cc, ss, y1, y2);
+          qreg[c][e] = static_cast<__bf16>(y1);
+          qreg[c + D / 64][e] = static_cast<__bf16>(y2);
+        }
+    }
+    // The new token (position ctx - 1, in the last partition): the
+    // workgroups of that partition write its rotated key and its value into
+    // the slot before they read the partition's blocks; the other
+    // partitions never read that block.  Wave 0, lane i: pair (i, i + D/2).
+    const int32_t slot = a.slot_mapping[s];
+    if (p == nparts - 1 && slot >= 0 && slot < a.num_blocks * kBlockSize) {
+      if (wave == 0 && lane < D / 2) {
+        const int64_t src = ((int64_t)s * a.hkv + kvh) * D;
+        const float x1 = (float)static_cast<const __bf16*>(a.k_new)[src + lane];
+        const float x2 = (float)static_cast<const __bf16*>(a.k_new)[src + lane + D / 2];
+        const __bf16 v1 = static_cast<const __bf16*>(a.v_new)[src + lane];
+        const __bf16 v2 = static_cast<const __bf16*>(a.v_new)[src + lane + D / 2];
+        float y1 = x1, y2 = x2;
+        if (a.rope) rope_rotate(x1, x2, rc, rs, y1, y2);
+        const int64_t base = ((int64_t)(slot / kBlockSize) * a.hkv + kvh) * (kBlockSize * D);
+        const int off = slot % kBlockSize;
+        __bf16* kd = static_cast<__bf16*>(const_cast<void*>(a.k_cache)) + base + off * D;
+        __bf16* vd = static_cast<__bf16*>(const_cast<void*>(a.v_cache)) + base + off;
+        kd[lane] = static_cast<__bf16>(y1);
+        kd[lane + D / 2] = static_cast<__bf16>(y2);
+        vd[lane * kBlockSize] = v1;
+        vd[(lane + D / 2) * kBlockSize] = v2;
+        __builtin_amdgcn_s_waitcnt(0);  // the stores have reached the cache hierarchy
+      }
+      __syncthreads();
+    }
+    if (a.q_rot_out != nullptr && p == 0 && col < nh) {
+      __bf16* qo = static_cast<__bf16*>(a.q_rot_out) + ((int64_t)s * a.hq + head0 + col) * D;
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) *reinterpret_cast<bf16x8*>(qo + 32 * c + 8 * g4) = qreg[c];
+    }
+  }
 
   const float c2 = a.scale_log2;
   const float tau_raw = kLazyTau / c2;
@@ -346,10 +401,10 @@ constexpr int decode_lds_bytes() { return DWT * 16 * 8 + DWT * (D / 16) * 4 * 17
 
 // Padded grid (partition, kv slice, sequence): partitions past a sequence's
 // context exit at once.
-template <int D>
+template <int D, bool FUSED>
 __global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[decode_lds_bytes<D, DW>()];
-  decode_body<D, DW>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
+  decode_body<D, DW, FUSED>(a, blockIdx.x, blockIdx.y, blockIdx.z, lds);
 }
 
 // Planned grid: workgroup = (item, kv slice), item = (sequence, partition)
@@ -357,7 +412,7 @@ __global__ __launch_bounds__(64 * DW) void decode_partition_kernel(const DecodeA
 // first.  Only real partitions are dispatched: the padded grid's empty
 // workgroups (most of it for a batch of mixed lengths) each take a CU slot
 // on their way out.  Entries out of range are skipped.
-template <int D>
+template <int D, bool FUSED>
 __global__ __launch_bounds__(64 * DW) void decode_planned_kernel(const DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) char lds[decode_lds_bytes<D, DW>()];
   const int Y = a.hkv * a.head_groups;
@@ -365,23 +420,30 @@ __global__ __launch_bounds__(64 * DW) void decode_planned_kernel(const DecodeArg
   const int it = (int)(blockIdx.x / (uint32_t)Y);
   const int s = a.plan[2 * it], p = a.plan[2 * it + 1];
   if (s < 0 || s >= a.num_seqs || p < 0 || p >= a.max_parts) return;
-  decode_body<D, DW>(a, p, yy, s, lds);
+  decode_body<D, DW, FUSED>(a, p, yy, s, lds);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t st) {
+template <int D, bool FUSED>
+static void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   if (a.plan != nullptr) {
     const dim3 gp((uint32_t)a.plan_items * (uint32_t)(a.hkv * a.head_groups));
-    if (a.plan_items > 0) {
-      if (head_dim == 128) hipLaunchKernelGGL(decode_planned_kernel<128>, gp, dim3(64 * DW), 0, st, a);
-      else hipLaunchKernelGGL(decode_planned_kernel<64>, gp, dim3(64 * DW), 0, st, a);
-    }
-    return hipGetLastError();
+    if (a.plan_items > 0) hipLaunchKernelGGL((decode_planned_kernel<D, FUSED>), gp, dim3(64 * DW), 0, st, a);
+    return;
   }
   const dim3 grid(a.max_parts | 1, a.hkv * a.head_groups, a.num_seqs);
-  if (head_dim == 128) hipLaunchKernelGGL(decode_partition_kernel<128>, grid, dim3(64 * DW), 0, st, a);
-  else hipLaunchKernelGGL(decode_partition_kernel<64>, grid, dim3(64 * DW), 0, st, a);
+  hipLaunchKernelGGL((decode_partition_kernel<D, FUSED>), grid, dim3(64 * DW), 0, st, a);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStream_t st) {
+  if (head_dim == 128) {
+    if (fused) launch_decode_t<128, true>(a, st);
+    else launch_decode_t<128, false>(a, st);
+  } else {
+    if (fused) launch_decode_t<64, true>(a, st);
+    else launch_decode_t<64, false>(a, st);
+  }
   return hipGetLastError();
 }
 

@@ -67,6 +67,28 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // exactly the rounded weights).
 __device__ __forceinline__ float round_bf16(float f) { return __uint_as_float(f2bf_bits(f) << 16); }
 
+// Rotary embedding, shared by every kernel that rotates so that they all
+// round identically.  cos and sin of the angle pos * theta: positions reach
+// tens of thousands of radians, where a float angle is off by ~1e-3 rad, so
+// the angle is formed and reduced modulo 2*pi in double precision (two-part
+// 2*pi, Cody-Waite); sine and cosine of the reduced angle (|r| <= pi) are then
+// taken in float, accurate to about one float ulp.
+__device__ __forceinline__ void rope_cos_sin(int32_t pos, double theta, float& c, float& s) {
+  constexpr double kTwoPiHi = 6.283185307179586;       // 2*pi rounded to double
+  constexpr double kTwoPiLo = 2.4492935982947064e-16;  // 2*pi - kTwoPiHi
+  constexpr double kInvTwoPi = 0.15915494309189535;
+  const double ang = (double)pos * theta;
+  const double k = rint(ang * kInvTwoPi);
+  const double r = fma(-k, kTwoPiLo, fma(-k, kTwoPiHi, ang));
+  sincosf((float)r, &s, &c);
+}
+// Rotation of the pair (x1, x2) = (x[i], x[i + D/2]) by that angle, with an
+// explicit order of roundings (no contraction left to the compiler).
+__device__ __forceinline__ void rope_rotate(float x1, float x2, float c, float s, float& y1, float& y2) {
+  y1 = fmaf(x1, c, -__fmul_rn(x2, s));
+  y2 = fmaf(x2, c, __fmul_rn(x1, s));
+}
+
 // A block-table entry outside the pool is replaced by block 0 so that a
 // corrupt table can never address memory outside the cache.
 __device__ __forceinline__ int32_t safe_block(int32_t blk, int32_t num_blocks) {

@@ -7,6 +7,14 @@
 
 namespace mi_attn {
 
+// RoPE frequencies theta_i = base^(-2i/D), i < D/2, computed once on the host
+// in double and passed by value, so every kernel that rotates uses the same
+// values.
+constexpr int kMaxRopePairs = 64;
+struct RopeFreqs {
+  double theta[kMaxRopePairs];
+};
+
 struct PrefillArgs {
   const void* q;
   const void* k;
@@ -59,6 +67,15 @@ struct DecodeArgs {
   float scale_log2;
   const int32_t* plan;  // [plan_items][2] (sequence, partition), or null: padded grid
   int32_t plan_items;
+  // fused RoPE + cache write of each sequence's new token (decode kernels
+  // built with the fused flag only)
+  const void* k_new;            // [S][Hkv][D], the new token's key (not rotated)
+  const void* v_new;            // [S][Hkv][D]
+  const int32_t* positions;     // [S], the new token's position
+  const int32_t* slot_mapping;  // [S], its cache slot; -1 or outside the pool: not written
+  void* q_rot_out;              // [S][Hq][D] rotated queries, or null
+  int32_t rope;                 // 0: no rotation (the write is a plain copy)
+  RopeFreqs freqs;
 };
 
 struct RopeWriteArgs {
@@ -71,7 +88,8 @@ struct RopeWriteArgs {
   void* v_cache;
   int32_t num_tokens, hq, hkv;
   int32_t num_blocks;  // slots at or past num_blocks * 16 are skipped
-  double rope_base;    // 0 = no rotation
+  int32_t rope;        // 0 = no rotation
+  RopeFreqs freqs;
 };
 
 // Launchers return the launch status (hipSuccess or the error).
@@ -79,7 +97,7 @@ struct RopeWriteArgs {
 // queries per head (4 or 2).  Query tile = 32 * wph rows.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStream_t s);
 hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hipStream_t s);
 
 // Tile geometry of the bf16 prefill kernel, used to size its grid.

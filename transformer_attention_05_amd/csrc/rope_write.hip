@@ -7,12 +7,10 @@
 // and the value into the token's paged slot.
 //
 // Rotation (half-split pairs): for i < D/2 the pair (x[i], x[i + D/2]) turns
-// by angle pos * base^(-2i/D).  Positions reach tens of thousands of radians,
-// where a float angle is off by ~1e-3 rad, so the angle is formed and reduced
-// modulo 2*pi in double precision (two-part 2*pi, Cody-Waite); sine and cosine
-// of the reduced angle (|r| <= pi) are then taken in float, accurate to about
-// one float ulp.  The rotation itself is float arithmetic; bf16 outputs are
-// rounded to nearest even.
+// by angle pos * base^(-2i/D) (frequencies from the host, in double; the
+// angle, its reduction and the rotation by rope_cos_sin and rope_rotate, the
+// same code as the decode's fused write).  bf16 outputs are rounded to
+// nearest even.
 //
 // Workgroup = kTok tokens, 512 threads.  A q or k item is four channel pairs
 // of one row (8-byte accesses for bf16; consecutive lanes cover consecutive
@@ -76,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void rope_write_kernel(const RopeWriteArg
   const int n0 = blockIdx.x * kTok;
   const int tid = threadIdx.x;
   const int ntok = min(kTok, a.num_tokens - n0);
-  const bool rot = a.rope_base != 0.0;
+  const bool rot = a.rope != 0;
 
   // round trip 1: slots and positions (the frequencies meanwhile)
   if (tid < kTok) {
@@ -86,7 +84,7 @@ __global__ __launch_bounds__(kThreads) void rope_write_kernel(const RopeWriteArg
     pos_sm[tid] = tid < ntok ? a.positions[n0 + tid] : 0;
   }
   if (rot)
-    for (int i = tid; i < H2; i += kThreads) theta[i] = pow(a.rope_base, -2.0 * (double)i / (double)D);
+    for (int i = tid; i < H2; i += kThreads) theta[i] = a.freqs.theta[i];
   __syncthreads();
 
   T* q = static_cast<T*>(a.q);
@@ -136,9 +134,10 @@ __global__ __launch_bounds__(kThreads) void rope_write_kernel(const RopeWriteArg
     if (rot) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float c = cs[it.t][it.i0 + e], s = sn[it.t][it.i0 + e];
-        y1[e] = x1[e] * c - x2[e] * s;
-        y2[e] = x2[e] * c + x1[e] * s;
+        float r1, r2;
+        rope_rotate(x1[e], x2[e], cs[it.t][it.i0 + e], sn[it.t][it.i0 + e], r1, r2);
+        y1[e] = r1;
+        y2[e] = r2;
       }
     }
     Vec4<T>::store(it.dst, y1);
@@ -177,18 +176,9 @@ __global__ __launch_bounds__(kThreads) void rope_write_kernel(const RopeWriteArg
 #pragma unroll
   for (int u = 0; u < kVItems; ++u) load_vitem(tid + u * kThreads, vitems[u]);
   if (rot) {
-    constexpr double kTwoPiHi = 6.283185307179586;        // 2*pi rounded to double
-    constexpr double kTwoPiLo = 2.4492935982947064e-16;   // 2*pi - kTwoPiHi
-    constexpr double kInvTwoPi = 0.15915494309189535;
     for (int e = tid; e < ntok * H2; e += kThreads) {
       const int t = e / H2, i = e % H2;
-      const double ang = (double)pos_sm[t] * theta[i];
-      const double kk = rint(ang * kInvTwoPi);
-      const double r = fma(-kk, kTwoPiLo, fma(-kk, kTwoPiHi, ang));
-      float sv, cv;
-      sincosf((float)r, &sv, &cv);
-      cs[t][i] = cv;
-      sn[t][i] = sv;
+      rope_cos_sin(pos_sm[t], theta[i], cs[t][i], sn[t][i]);
     }
   }
   __syncthreads();

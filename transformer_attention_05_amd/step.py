@@ -1,13 +1,16 @@
 """One serving step over a shared paged cache: fused RoPE + cache write for
 every new token, chunked prefill for the prefill requests, decode for the
-decode sequences (partition pass + merge), with no host synchronisation in
-between.  The chunked prefill (bound by the matrix cores) and the decode
-(bound by HBM) do not depend on each other, and each needs only its own new
-tokens rotated and written (the two sets of tokens and of cache slots are
-disjoint).  So with ``concurrent`` the write is split in two launches: the
-caller's stream writes the chunk tokens and runs the prefill, a second
-stream writes the decode tokens and runs the decode, and the caller's
-stream then waits for the second one.  Nothing waits on the other stream
+decode sequences (one launch: partitions and their merge), with no host
+synchronisation in between.  The chunked prefill (bound by the matrix cores)
+and the decode (bound by HBM) do not depend on each other, and each needs
+only its own new tokens rotated and written (the two sets of tokens and of
+cache slots are disjoint).  So with ``concurrent`` the write is split in two
+launches: the caller's stream writes the chunk tokens and runs the prefill,
+a second stream writes the decode tokens and runs the decode, and the
+caller's stream then waits for the second one.  With ``fuse_decode_write``
+the second stream instead runs one decode launch that rotates and writes its
+own tokens (attn_decode_paged_rope; rotated queries in ``q_dec_rot``), after
+waiting for the chunk write (see below).  Nothing waits on the other stream
 mid-step.  The prefill is enqueued first: each of its workgroups needs a
 whole CU's registers, so it must be placed before the decode's thousands of
 small workgroups spread over every CU (enqueued the other way round, the
@@ -24,8 +27,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (Pool, attn_decode_paged, attn_decode_paged_plan, attn_decode_paged_workspace_size,
-               attn_kv_cache_write_rope, attn_prefill_paged, attn_prefill_paged_workspace_size)
+from . import (Pool, attn_decode_paged, attn_decode_paged_plan, attn_decode_paged_rope,
+               attn_decode_paged_workspace_size, attn_kv_cache_write_rope, attn_prefill_paged,
+               attn_prefill_paged_workspace_size)
 
 
 class MixedStep:
@@ -37,9 +41,11 @@ class MixedStep:
     ``case.tables`` and ``case.slots`` through the pool.
     """
 
-    def __init__(self, case, assign, device="cuda", partition_size=0, scatter=None, concurrent=True):
+    def __init__(self, case, assign, device="cuda", partition_size=0, scatter=None, concurrent=True,
+                 fuse_decode_write=False):
         self.case = case
         self.concurrent = concurrent
+        self.fuse_decode_write = fuse_decode_write
         self.device = device
         self.pool = Pool(case.num_blocks)
         assign(case, self.pool)
@@ -68,6 +74,8 @@ class MixedStep:
         self.partition_size = partition_size
         self.o_prefill = torch.empty(self.n_prefill, case.hq, d, dtype=dt, device=device)
         self.o_decode = torch.empty(S, case.hq, d, dtype=dt, device=device)
+        # rotated decode queries of the fused decode (the concurrent schedule)
+        self.q_dec_rot = torch.empty(S, case.hq, d, dtype=dt, device=device)
         need = attn_decode_paged_workspace_size(S, case.hq, hkv, d, self.max_dec_ctx, partition_size)
         # zeroed once: the decode's arrival counters start at zero and every call leaves them so
         self.workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
@@ -98,12 +106,47 @@ class MixedStep:
                            causal=True, max_context_len=self.max_pre_ctx, workspace=self.pre_workspace)
 
     def decode(self):
+        """Decode over the cache, whose decode tokens are already written."""
         R = self.R
         attn_decode_paged(self.q[self.n_prefill:], self.k_cache, self.v_cache, self.tables[R:],
                           self.context_lens[R:], self.max_dec_ctx, o=self.o_decode,
                           partition_size=self.partition_size, workspace=self.workspace, plan=self.plan)
 
+    def decode_fused(self):
+        """Decode that rotates and writes the decode tokens itself (q left
+        unrotated; rotated queries in q_dec_rot)."""
+        R, n = self.R, self.n_prefill
+        attn_decode_paged_rope(self.q[n:], self.k[n:], self.v[n:], self.positions[n:], self.slots[n:],
+                               self.k_cache, self.v_cache, self.tables[R:], self.context_lens[R:],
+                               self.max_dec_ctx, o=self.o_decode, q_rot_out=self.q_dec_rot,
+                               rope_base=self.case.rope_base, partition_size=self.partition_size,
+                               workspace=self.workspace, plan=self.plan)
+
+    def _fused(self):
+        return self.concurrent and self.fuse_decode_write and self.R and self.S
+
+    def rotated_q(self):
+        """Rotated queries of every new token after run()."""
+        if self._fused():
+            return torch.cat([self.q[: self.n_prefill], self.q_dec_rot])
+        return self.q
+
     def run(self):
+        if self._fused():
+            main = torch.cuda.current_stream()
+            self.side.wait_stream(main)      # the step's inputs come from the caller's stream
+            self.write(0, self.n_prefill)    # the chunk tokens
+            # the decode is released with the prefill, when the chunk write
+            # ends: started at once, its workgroups would take every CU
+            # before the prefill's (MI355X: 234 us per step instead of 207)
+            after_write = torch.cuda.Event()
+            after_write.record(main)
+            self.prefill()
+            with torch.cuda.stream(self.side):
+                self.side.wait_event(after_write)
+                self.decode_fused()          # writes the decode tokens itself
+            main.wait_stream(self.side)
+            return
         if self.concurrent and self.R and self.S:
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)      # the step's inputs come from the caller's stream
