@@ -61,21 +61,6 @@ __device__ __forceinline__ void load_block(BlockRegs<D>& r, const __bf16* kb, co
   for (int dt = 0; dt < D / 16; ++dt) r.v[dt] = *reinterpret_cast<const u32x2*>(vb + 16 * dt * kBlockSize);
 }
 
-// The partials cross workgroups (and XCDs, whose L2 caches are not coherent
-// with each other) inside one launch.  They are written and read as
-// device-scope relaxed atomics, which go to the device's coherence point
-// instead of the XCD's L2, so no cache writeback or invalidation is needed:
-// a workgroup's partial stores are complete (vmcnt 0) before its arrival is
-// counted, and the merging workgroup reads them after the count.
-__device__ __forceinline__ void store_coherent(float* p, float x, float y) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, f32x2{x, y}), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ f32x2 load_coherent(const float* p) {
-  return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT));
-}
-
 // Merge of one sequence's partitions for the query heads head0 .. head0+nh-1:
 // O = sum_p f_p O_p / sum_p f_p l_p with f_p = exp(m_p - max m), taken as one
 // online pass over batches of MK partitions whose loads are all in flight at
@@ -380,17 +365,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, co
   // restores the counter to its value before the call (zero), for the next
   // call
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // every thread's partials, and the combine's LDS reads, are done
-  int* sm_last = reinterpret_cast<int*>(lds);
-  if (tid == 0) {
-    int* cnt = a.counters + (int64_t)s * (a.hkv * a.head_groups) + yy;
-    const int prev = atomicAdd(cnt, 1);
-    const int last = prev == nparts - 1;
-    if (last) atomicSub(cnt, nparts);
-    *sm_last = last;
-  }
-  __syncthreads();
-  if (*sm_last == 0) return;
+  // (the barrier in arrive_last also ends the combine's LDS reads)
+  if (!arrive_last(a.counters + (int64_t)s * (a.hkv * a.head_groups) + yy, nparts, reinterpret_cast<int*>(lds)))
+    return;
   merge_partials<D>(a, s, head0, nh, nparts, tid, 64 * DWT);
 }
 

@@ -89,6 +89,38 @@ __device__ __forceinline__ void rope_rotate(float x1, float x2, float c, float s
   y2 = fmaf(x2, c, __fmul_rn(x1, s));
 }
 
+// Partials that cross workgroups (and XCDs, whose L2 caches are not
+// coherent with each other) inside one launch are written and read as
+// device-scope relaxed atomics: they go to the device's coherence point
+// instead of the XCD's L2, so no cache writeback or invalidation is needed.
+// A workgroup's partial stores are complete (vmcnt 0) before it counts its
+// arrival, and the merging workgroup reads them after the count.
+__device__ __forceinline__ void store_coherent(float* p, float x, float y) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, f32x2{x, y}), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 load_coherent(const float* p) {
+  return __builtin_bit_cast(f32x2, __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Arrival of one of `n` workgroups that share a merge: returns true (to
+// every thread) in the last to arrive, which then restores the counter to
+// its value before the launch (zero).  Every thread's partial stores must be
+// complete (vmcnt 0) before the call; `flag` is one int of LDS that no wave
+// still uses.
+__device__ __forceinline__ bool arrive_last(int32_t* counter, int n, int* flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(counter, 1);
+    const int last = prev == n - 1;
+    if (last) atomicSub(counter, n);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
 // A block-table entry outside the pool is replaced by block 0 so that a
 // corrupt table can never address memory outside the cache.
 __device__ __forceinline__ int32_t safe_block(int32_t blk, int32_t num_blocks) {
