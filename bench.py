@@ -178,6 +178,18 @@ def main():
             torch.cuda.synchronize()
             stage_ms.append(tm.mean_ms())
         ms_wr, ms_pre, ms_dec = stage_ms
+        # the same step captured in a HIP graph, replays back to back
+        graph_s = None
+        if not args.no_components:
+            step.capture()
+            for _ in range(3):
+                step.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                step.replay()
+            torch.cuda.synchronize()
+            graph_s = (time.perf_counter() - t0) / args.steps
         # prefill and decode overlap (two streams), so the step's bound is the
         # larger of its total HBM bytes and its total matrix-core flops
         B_pre = prefill_io_bytes(case)
@@ -185,7 +197,8 @@ def main():
         out["mixed"] = dict(wall_s=wall, ms_write=ms_wr, ms_prefill=ms_pre, ms_decode=ms_dec, F=F, B_dec=B_dec,
                             B_wr=B_wr, B_pre=B_pre, t_roof=t_roof, n_new=n_new, part=mi.attn_decode_paged_auto_partition(
                                 len(case.dec_lengths), HKV, int(case.dec_lengths.max())),
-                            dec_tokens=int(case.dec_lengths.sum()), pool_blocks=case.num_blocks)
+                            dec_tokens=int(case.dec_lengths.sum()), pool_blocks=case.num_blocks,
+                            graph_s=graph_s)
         log(f"bench: mixed step wall {wall * 1e3:.3f} ms | write {ms_wr:.3f} prefill {ms_pre:.3f} "
             f"decode {ms_dec:.3f} ms")
         del step
@@ -381,6 +394,8 @@ def emit(args, out, cpu):
         comps["step_decode"] = {"us": round(m["ms_decode"] * 1e3, 2), "GB/s": round(gbps, 1),
                                 "frac_of_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4)}
         comps["step_roofline_us"] = round(m["t_roof"] * 1e6, 2)
+        if m.get("graph_s"):
+            comps["step_graph_replay_us"] = round(m["graph_s"] * 1e6, 2)
     if "prefill_c4" in out:
         p = out["prefill_c4"]
         tf = p["flops"] / (p["ms"] / 1e3) / 1e12

@@ -170,6 +170,34 @@ def test_concurrent_step_equals_serial(fused):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16)), name
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replay_equals_eager(fused):
+    """The step captured in a HIP graph and replayed three times, with eager
+    work (restoring the unrotated queries) and synchronisations between the
+    replays, gives the eager step's outputs, rotated queries and caches bit
+    for bit every time."""
+    say(f"case: graph-captured step, fused decode write {fused}")
+    case = mixed_case(79, num_req=3, chunk=150, cached_max=700, num_dec=17, dec_lo=1, dec_hi=6000)
+    st = MixedStep(case, assign_blocks, DEV, scatter=scatter_to_pool, fuse_decode_write=fused)
+    q0 = st.q.clone()
+    st.run()
+    torch.cuda.synchronize()
+    names = ("o_prefill", "o_decode", "k_cache", "v_cache")
+    eager = {n: getattr(st, n).clone() for n in names}
+    eager["rotated_q"] = st.rotated_q().clone()
+    st.capture()
+    for rep in range(3):
+        st.q.copy_(q0)
+        st.o_prefill.zero_()
+        st.o_decode.zero_()
+        torch.cuda.synchronize()
+        st.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            assert torch.equal(getattr(st, n).view(torch.int16), eager[n].view(torch.int16)), (rep, n)
+        assert torch.equal(st.rotated_q().view(torch.int16), eager["rotated_q"].view(torch.int16)), rep
+
+
 def test_c5_mixed_step():
     """8 chunks of 512 new tokens on 0-2048 cached tokens + 128 decode
     sequences with context log-U[16, 32768], RoPE base 10000, fragmented pool

@@ -122,6 +122,24 @@ class MixedStep:
                                rope_base=self.case.rope_base, partition_size=self.partition_size,
                                workspace=self.workspace, plan=self.plan)
 
+    def capture(self):
+        """Record run() into a HIP graph (torch.cuda.CUDAGraph) for replay().
+
+        The launches allocate nothing, issue no memset and read no length on
+        the host, so the step captures as it is; both streams join the
+        capture through the events run() records.  A replay re-runs the same
+        launches on the same buffers: the RoPE write rotates q in place, so
+        the caller restores q (or writes new tokens) between replays, as it
+        would between eager steps."""
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run()
+        torch.cuda.synchronize()
+
+    def replay(self):
+        self.graph.replay()
+
     def _fused(self):
         return self.concurrent and self.fuse_decode_write and self.R and self.S
 
