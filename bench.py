@@ -130,7 +130,8 @@ def main():
     import torch
     import transformer_attention_05_amd as mi
     from transformer_attention_05_amd.step import MixedStep
-    from workloads import assign_blocks, build_decode_pool, decode_case, mixed_case, prefill_case, scatter_to_pool
+    from workloads import (additive_mask, assign_blocks, build_decode_pool, decode_case, mixed_case, prefill_case,
+                           scatter_to_pool)
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
@@ -237,7 +238,20 @@ def main():
         fl = 4 * D * HQ * 2048 * 2049 // 2
         out["prefill_c2"] = dict(ms=tp.mean_ms(), flops=fl)
         log(f"bench: prefill C2 {tp.mean_ms() * 1e3:.1f} us  {fl / tp.mean_ms() / 1e9:.1f} TFLOP/s")
-        del qd, kd, vd, o, ws
+        # the same shape with a general additive mask (one fp32 [T, T] mask for
+        # every head, no causal structure): every (query, key) pair is computed
+        mask = additive_mask(1006, (2048, 2048), amp=1.0, p_masked=0.1).to(dev)
+        for _ in range(3):
+            mi.attn_prefill_masked(qd, kd, vd, mask, o=o)
+        torch.cuda.synchronize()
+        tp = EventTimer(torch)
+        for _ in range(max(10, args.steps)):
+            e = tp.start(); mi.attn_prefill_masked(qd, kd, vd, mask, o=o); tp.stop(e)
+        torch.cuda.synchronize()
+        fl = 4 * D * HQ * 2048 * 2048
+        out["prefill_masked"] = dict(ms=tp.mean_ms(), flops=fl)
+        log(f"bench: masked prefill T 2048 {tp.mean_ms() * 1e3:.1f} us  {fl / tp.mean_ms() / 1e9:.1f} TFLOP/s")
+        del qd, kd, vd, o, ws, mask
 
     # ------------------------------------------------------------------ uniform decode
     if not args.no_components and args.only in (None, "decode"):
@@ -406,6 +420,11 @@ def emit(args, out, cpu):
         tf = p["flops"] / (p["ms"] / 1e3) / 1e12
         comps["prefill_T2048"] = {"us": round(p["ms"] * 1e3, 1), "TFLOP/s": round(tf, 1),
                                   "frac_of_bf16_peak": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)}
+    if "prefill_masked" in out:
+        p = out["prefill_masked"]
+        tf = p["flops"] / (p["ms"] / 1e3) / 1e12
+        comps["prefill_T2048_additive_mask"] = {"us": round(p["ms"] * 1e3, 1), "TFLOP/s": round(tf, 1),
+                                                "frac_of_bf16_peak": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)}
     if "decode_c3" in out:
         d = out["decode_c3"]
         gb = d["bytes"] / (d["ms"] / 1e3) / 1e9

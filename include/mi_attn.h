@@ -109,6 +109,29 @@ ATTN_API int attn_prefill(const void* q, const void* k, const void* v, void* o, 
                  void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* -------------------------------------------------------------------------
+ * attn_prefill_masked -- attn_prefill with a general additive mask.
+ *
+ * §FlashAttention-Style Kernels writes attention as softmax(Q K^T / sqrt(d)
+ * + M) V with an additive mask M; attn_prefill covers M = 0 and the causal
+ * M.  Here M is given: element (b, h, i, j) (batch, query head, query row,
+ * key) is mask[b*mask_strides[0] + h*mask_strides[1] + i*mask_strides[2] + j],
+ * fp32, keys contiguous; a stride of 0 broadcasts that dimension (one
+ * [Tq][Tk] mask for every batch and head, say).  Entries are finite or
+ * -infinity; `causal` applies on top.  A row whose every key is masked
+ * yields O = 0 (and LSE = -infinity).  Single pass (no workspace).
+ *
+ *   mask         device fp32, 16-byte aligned; strides >= 0 and multiples of
+ *                4 elements
+ *   every other argument as for attn_prefill.
+ * ---------------------------------------------------------------------- */
+ATTN_API int attn_prefill_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const float* mask, const int64_t mask_strides[3], int32_t batch,
+                        int32_t seqlen_q, int32_t seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, const int64_t q_strides[3], const int64_t k_strides[3],
+                        const int64_t v_strides[3], const int64_t o_strides[3], float scale,
+                        int32_t causal, attn_dtype dtype, attn_stream_t stream);
+
+/* -------------------------------------------------------------------------
  * attn_prefill_paged -- prefill of new query chunks over a paged KV cache.
  *
  * The same computation as attn_prefill, with keys and values read through

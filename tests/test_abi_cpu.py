@@ -31,7 +31,7 @@ def test_header_declares_entry_points():
     syms = declared_symbols()
     for name in ("attn_prefill", "attn_prefill_paged", "attn_prefill_workspace_size", "attn_decode_paged_plan",
                  "attn_prefill_paged_workspace_size", "attn_decode_paged", "attn_decode_paged_workspace_size",
-                 "attn_decode_paged_rope",
+                 "attn_decode_paged_rope", "attn_prefill_masked",
                  "attn_kv_cache_write_rope", "attn_pool_create", "attn_pool_alloc", "attn_pool_free",
                  "attn_pool_retain", "attn_seq_reserve", "attn_last_error"):
         assert name in syms
@@ -82,6 +82,37 @@ def prefill(lib, **kw):
 def test_prefill_rejects(lib, kw, status):
     assert prefill(lib, **kw) == status
     assert lib.attn_last_error().decode().startswith("attn_prefill")
+
+
+M3 = (ctypes.c_int64 * 3)(0, 0, 64)
+
+
+def prefill_masked(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=None, mask=P, ms=M3, batch=1, tq=64, tk=64, hq=1, hkv=1, d=64,
+             qs=S3, ks=S3, vs=S3, os_=S3, scale=0.0, causal=0, dtype=ATTN_F32)
+    a.update(kw)
+    return lib.attn_prefill_masked(a["q"], a["k"], a["v"], a["o"], a["lse"], a["mask"], a["ms"], a["batch"],
+                                   a["tq"], a["tk"], a["hq"], a["hkv"], a["d"], a["qs"], a["ks"], a["vs"],
+                                   a["os_"], a["scale"], a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(mask=None), ATTN_E_INVALID),
+    (dict(ms=None), ATTN_E_INVALID),
+    (dict(mask=P + 4), ATTN_E_INVALID),                               # not 16-byte aligned
+    (dict(ms=(ctypes.c_int64 * 3)(0, 0, 66)), ATTN_E_INVALID),        # row stride not a multiple of 4
+    (dict(ms=(ctypes.c_int64 * 3)(-64, 0, 64)), ATTN_E_INVALID),
+    (dict(d=96), ATTN_E_UNSUPPORTED),                                 # the prefill's own checks
+    (dict(q=None), ATTN_E_INVALID),
+    (dict(tq=65, tk=64, causal=1), ATTN_E_INVALID),
+])
+def test_prefill_masked_rejects(lib, kw, status):
+    assert prefill_masked(lib, **kw) == status
+    assert lib.attn_last_error().decode().startswith("attn_prefill_masked")
+
+
+def test_prefill_masked_empty_is_ok_without_launch(lib):
+    assert prefill_masked(lib, batch=0) == 0
 
 
 # batch 1, T 2048, 12/2 heads, D 128: too few query tiles to fill the GPU, so

@@ -17,9 +17,13 @@ pytestmark = [pytest.mark.gpu,
 
 
 # LSE bar.  bf16 path: the row sum accumulates the bf16-rounded weights that
-# feed the PV product (each within a relative 2**-9 of exact), so
-# |LSE - exact| <= ln(1 + 2**-9) ~ 1.95e-3 plus fp32 rounding.  fp32 path: 1e-5.
-LSE_BF16 = 2.0e-3
+# feed the PV product.  bf16 carries 8 significant bits, so rounding to
+# nearest moves a weight by at most half an ulp, a relative 2**-8 at the
+# bottom of a binade; hence |LSE - exact| <= ln(1 + 2**-8) ~ 3.9e-3 plus fp32
+# rounding.  (Averaged over many keys the errors mostly cancel; a row that
+# sees only a few keys, as under a strong mask, can come close to the bound.)
+# fp32 path: 1e-5.
+LSE_BF16 = 4.0e-3
 LSE_F32 = 1e-5
 
 

@@ -26,6 +26,7 @@ __all__ = [
     "attn_kv_cache_write_rope",
     "attn_last_error",
     "attn_prefill",
+    "attn_prefill_masked",
     "attn_prefill_paged",
     "attn_prefill_paged_workspace_size",
     "attn_prefill_workspace_size",
@@ -51,6 +52,9 @@ _SIGNATURES = {
     "attn_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                     _c_i64p, _c_i64p, _c_i64p, _c_i64p, ctypes.c_float, _c_i32, ctypes.c_int,
                                     _vp, ctypes.c_size_t, _vp]),
+    "attn_prefill_masked": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i64p, _c_i32, _c_i32, _c_i32, _c_i32,
+                                           _c_i32, _c_i32, _c_i64p, _c_i64p, _c_i64p, _c_i64p, ctypes.c_float, _c_i32,
+                                           ctypes.c_int, _vp]),
     "attn_prefill_paged_workspace_size": (ctypes.c_size_t, [_c_i32] * 7),
     "attn_prefill_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
@@ -184,6 +188,31 @@ def attn_prefill(q, k, v, o=None, lse=None, causal=True, scale=0.0, workspace=No
         b, tq, tk, hq, hkv, d,
         _bth_strides(q, "q"), _bth_strides(k, "k"), _bth_strides(v, "v"), _bth_strides(o, "o"),
         float(scale), 1 if causal else 0, _dtype_code(q), ws_ptr, ws_bytes, _stream(q))
+    _check(st)
+    return o
+
+
+def attn_prefill_masked(q, k, v, mask, o=None, lse=None, causal=False, scale=0.0):
+    """Contiguous attention with an additive fp32 mask: ``mask`` is a GPU
+    float32 tensor broadcastable to [B, Hq, Tq, Tk] (a [Tq, Tk] mask serves
+    every batch and head) with contiguous keys; `causal` applies on top."""
+    if o is None:
+        o = torch.empty_like(q)
+    b, tq, hq, d = q.shape
+    _, tk, hkv, _ = k.shape
+    if mask.dtype != torch.float32:
+        raise ValueError("mask must be float32")
+    m = mask
+    while m.dim() < 4:
+        m = m.unsqueeze(0)
+    m = m.expand(b, hq, tq, tk)
+    if m.stride(3) != 1:
+        raise ValueError("mask: keys must be contiguous")
+    st = load().attn_prefill_masked(
+        _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o"), _dev(lse, "lse") if lse is not None else None,
+        _dev(m, "mask"), _i64x3(m.stride()[:3]), b, tq, tk, hq, hkv, d,
+        _bth_strides(q, "q"), _bth_strides(k, "k"), _bth_strides(v, "v"), _bth_strides(o, "o"),
+        float(scale), 1 if causal else 0, _dtype_code(q), _stream(q))
     _check(st)
     return o
 

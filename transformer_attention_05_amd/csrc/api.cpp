@@ -61,6 +61,8 @@ int launched(hipError_t e, const char* fn) {
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 
+constexpr double kLog2eHost = 1.4426950408889634;
+
 // theta_i = base^(-2i/D) for the D/2 rotation pairs, in double
 RopeFreqs rope_freqs(float base, int32_t head_dim) {
   RopeFreqs f{};
@@ -199,14 +201,13 @@ extern "C" size_t attn_prefill_paged_workspace_size(int32_t num_seqs, int32_t to
 }
 
 // ---------------------------------------------------------------------------
-extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
-                            int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
-                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                            const int64_t q_strides[3], const int64_t k_strides[3],
-                            const int64_t v_strides[3], const int64_t o_strides[3],
-                            float scale, int32_t causal, attn_dtype dtype,
-                            void* workspace, size_t workspace_bytes, attn_stream_t stream) {
-  static const char* fn = "attn_prefill";
+namespace {
+int prefill_common(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse,
+                   const float* mask, const int64_t* mask_strides, int32_t batch, int32_t seqlen_q,
+                   int32_t seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                   const int64_t q_strides[3], const int64_t k_strides[3], const int64_t v_strides[3],
+                   const int64_t o_strides[3], float scale, int32_t causal, attn_dtype dtype, void* workspace,
+                   size_t workspace_bytes, attn_stream_t stream) {
   if (!q || !k || !v || !o) return fail(ATTN_E_INVALID, "%s: q, k, v and o must be non-NULL", fn);
   if (!q_strides || !k_strides || !v_strides || !o_strides)
     return fail(ATTN_E_INVALID, "%s: stride arrays must be non-NULL", fn);
@@ -233,6 +234,13 @@ extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o
   // byte offset from a row base: up to 7 token strides of 2 bytes
   if (dtype == ATTN_BF16 && (k_strides[1] >= (int64_t(1) << 28) || v_strides[1] >= (int64_t(1) << 28)))
     return fail(ATTN_E_UNSUPPORTED, "%s: key/value token strides must be below 2^28 elements", fn);
+  if (mask != nullptr) {
+    // the kernels read four consecutive mask floats with one 16-byte load
+    if (!aligned(mask, 16)) return fail(ATTN_E_INVALID, "%s: mask must be 16-byte aligned", fn);
+    for (int i = 0; i < 3; ++i)
+      if (mask_strides[i] < 0 || mask_strides[i] % 4 != 0)
+        return fail(ATTN_E_INVALID, "%s: mask strides must be >= 0 and multiples of 4 elements", fn);
+  }
   if (batch == 0 || seqlen_q == 0) return ok();
 
   PrefillArgs a{};
@@ -245,10 +253,22 @@ extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o
   a.hq = num_q_heads; a.hkv = num_kv_heads; a.group = num_q_heads / num_kv_heads;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = scale_log2;
+  if (mask != nullptr) {
+    a.mask = mask;
+    a.ms_b = mask_strides[0]; a.ms_h = mask_strides[1]; a.ms_q = mask_strides[2];
+    a.mask_scale = (float)((double)kLog2eHost / (double)scale_log2);  // 1 / scale
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (dtype == ATTN_BF16) {
     PrefillPlan p = plan_prefill(seqlen_q, seqlen_k, num_q_heads, a.group, batch, head_dim, false,
                                  (int64_t)batch * seqlen_q * num_q_heads);
+    if (mask != nullptr) {
+      // one pass on the default tile (the masked kernel's only shapes)
+      p.t = PrefillTile{a.group % 2 == 0 ? 2 : 1, a.group % 2 == 0 ? 2 : 4};
+      p.num_m_tiles = ceil_div(seqlen_q, 32 * p.t.wph);
+      p.num_wg = (int64_t)p.num_m_tiles * (num_q_heads / p.t.hpw) * batch;
+      p.num_splits = 1;
+    }
     if ((st = use_workspace(p, workspace, workspace_bytes, a, fn)) != ATTN_OK) return st;
     a.num_m_tiles = p.num_m_tiles;
     if (p.num_wg * a.num_splits > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
@@ -261,6 +281,32 @@ extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o
   if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
   a.num_wg = (uint32_t)nwg;
   return launched(launch_prefill_f32(a, head_dim, s), fn);
+}
+}  // namespace
+
+extern "C" int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int32_t batch, int32_t seqlen_q, int32_t seqlen_k,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            const int64_t q_strides[3], const int64_t k_strides[3],
+                            const int64_t v_strides[3], const int64_t o_strides[3],
+                            float scale, int32_t causal, attn_dtype dtype,
+                            void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  return prefill_common("attn_prefill", q, k, v, o, lse, nullptr, nullptr, batch, seqlen_q, seqlen_k,
+                        num_q_heads, num_kv_heads, head_dim, q_strides, k_strides, v_strides, o_strides, scale,
+                        causal, dtype, workspace, workspace_bytes, stream);
+}
+
+extern "C" int attn_prefill_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const float* mask, const int64_t mask_strides[3], int32_t batch,
+                                   int32_t seqlen_q, int32_t seqlen_k, int32_t num_q_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, const int64_t q_strides[3], const int64_t k_strides[3],
+                                   const int64_t v_strides[3], const int64_t o_strides[3], float scale,
+                                   int32_t causal, attn_dtype dtype, attn_stream_t stream) {
+  static const char* fn = "attn_prefill_masked";
+  if (!mask || !mask_strides) return fail(ATTN_E_INVALID, "%s: mask and mask_strides must be non-NULL", fn);
+  return prefill_common(fn, q, k, v, o, lse, mask, mask_strides, batch, seqlen_q, seqlen_k, num_q_heads,
+                        num_kv_heads, head_dim, q_strides, k_strides, v_strides, o_strides, scale, causal, dtype,
+                        nullptr, 0, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -48,6 +48,11 @@ struct PrefillArgs {
   int64_t ws_rows;      // partial rows per split: (query row, head) pairs
   float* ws_o;          // [num_splits][ws_rows][D], unnormalised output
   float* ws_ml;         // [num_splits][ws_rows][2]: max (log2 units), row sum
+  // additive mask (contiguous prefill): fp32, element (b, h, i, j) at
+  // mask[b*ms_b + h*ms_h + i*ms_q + j]; null: none.  mask_scale = 1 / scale.
+  const float* mask;
+  int64_t ms_b, ms_h, ms_q;
+  float mask_scale;
 };
 
 struct DecodeArgs {

@@ -100,8 +100,9 @@ __device__ __forceinline__ int vt_swz(int d) {   // V^T rows (paged, 64 keys = 8
 }
 
 // Tile geometry: HPW query heads share every K/V tile (same kv head under
-// GQA); each head has WPH wavefronts of 32 queries.
-template <int D, bool PAGED, int HPW, int WPH>
+// GQA); each head has WPH wavefronts of 32 queries.  MASKED adds the caller's
+// additive mask M to every score (contiguous layout only).
+template <int D, bool PAGED, int HPW, int WPH, bool MASKED = false>
 __global__ __launch_bounds__(64 * HPW * WPH) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NW = HPW * WPH;
@@ -453,6 +454,31 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     return (t + 1) * BN > key_end || (a.causal && (t + 1) * BN - 1 > wq0 + off);
   };
   auto mask_tile = [&](f32x16 (&s)[2], int t) {
+    if constexpr (MASKED) {
+      // the additive mask M (natural-log units) enters the raw scores as
+      // M / scale, so the exponent becomes (s + M / scale) * scale * log2 e;
+      // lane keys t*BN + 32kt + 8g + 4hh + j, j < 4, are four consecutive
+      // floats of the mask row (rows past the queries read the last row,
+      // keys past the keys read nothing: both are discarded or masked)
+      const float* mrow = a.mask + b * a.ms_b + h * a.ms_h + (int64_t)min(qi, tq - 1) * a.ms_q;
+      f32x4 mv[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int key0 = t * BN + kt * 32 + 8 * g4 + 4 * hh;
+          if (key0 + 4 <= tk) {
+            mv[kt][g4] = *reinterpret_cast<const f32x4*>(mrow + key0);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mv[kt][g4][j] = key0 + j < tk ? mrow[key0 + j] : 0.f;
+          }
+        }
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = fmaf(mv[kt][r >> 2][r & 3], a.mask_scale, s[kt][r]);
+    }
     const int lim = a.causal ? min(key_end - 1, qi + off) : key_end - 1;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -523,7 +549,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     __syncthreads();
     if (tail_tile(T0)) zero_tail(vring, T0);
     s_mfma(kring, sa);
-    if (needs_mask(T0)) mask_tile(sa, T0);
+    if (MASKED || needs_mask(T0)) mask_tile(sa, T0);
     update_max(row_max(sa));
     __syncthreads();
   }
@@ -556,7 +582,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       tile_blocks(T0 + min(j + 4, n_tiles - 1), blk_k);
     }
     phase_a(kring + r1 * TILE, sc, sn);
-    if (needs_mask(T0 + j + 1)) mask_tile(sn, T0 + j + 1);
+    if (MASKED || needs_mask(T0 + j + 1)) mask_tile(sn, T0 + j + 1);
     float tmax = -INFINITY;
     phase_b(vring + vcur * TILE, sn, tmax);
     update_max(fmaxf(tmax, xor32(tmax)));
@@ -740,6 +766,8 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
   const float* kp = static_cast<const float*>(a.k) + b * a.ks_b + g * a.ks_h;
   const float* vp = static_cast<const float*>(a.v) + b * a.vs_b + g * a.vs_h;
   float* op = static_cast<float*>(a.o) + b * a.os_b + h * a.os_h;
+  // additive mask row of this query (rows past the queries read the last row)
+  const float* mrow = a.mask ? a.mask + b * a.ms_b + h * a.ms_h + (int64_t)min(qi, tq - 1) * a.ms_q : nullptr;
 
   float qr[64];
 #pragma unroll
@@ -778,6 +806,7 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
       // scores are kept in log2 units (scale * log2 e folded in once), so the
       // exponent below is a plain difference of stored values and the row
       // maximum gets weight exactly 1
+      if (mrow != nullptr && n0 + j <= lim) dot = fmaf(mrow[n0 + j], a.mask_scale, dot);
       s[j] = (n0 + j <= lim) ? dot * c2 : -INFINITY;
       tmax = fmaxf(tmax, s[j]);
     }
@@ -811,6 +840,14 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
 template <int D, bool PAGED, int HPW, int WPH>
 static void launch_one(const PrefillArgs& a, hipStream_t s) {
   dim3 grid(a.num_wg * (uint32_t)a.num_splits);
+  if constexpr (!PAGED && ((HPW == 2 && WPH == 2) || (HPW == 1 && WPH == 4))) {
+    // the masked variant exists for the default contiguous tiles only (the
+    // host picks one of them and never splits a masked launch)
+    if (a.mask != nullptr) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, HPW, WPH, true>), grid, dim3(64 * HPW * WPH), 0, s, a);
+      return;
+    }
+  }
   hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, HPW, WPH>), grid, dim3(64 * HPW * WPH), 0, s, a);
   if (a.num_splits > 1)
     hipLaunchKernelGGL((prefill_merge_kernel<D, PAGED, HPW, WPH>), dim3(a.num_wg * merge_parts<D, HPW, WPH>()),

@@ -52,6 +52,18 @@ def prefill_case(seed, batch, seqlen, hq, hkv, d, dtype, seqlen_k=None):
     return q, k, v
 
 
+def additive_mask(seed, shape, amp=3.0, p_masked=0.25, masked_rows=()):
+    """fp32 additive mask: amp * N(0,1) with a fraction p_masked of the entries
+    set to -inf, and the rows listed in masked_rows (indices on the second to
+    last axis) wholly -inf."""
+    g = rng(seed)
+    m = (amp * g.standard_normal(shape)).astype(np.float32)
+    m[g.random(shape) < p_masked] = -np.inf
+    for r in masked_rows:
+        m[..., r, :] = -np.inf
+    return torch.from_numpy(m)
+
+
 # --------------------------------------------------------------------------
 # paged decode
 # --------------------------------------------------------------------------
