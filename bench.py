@@ -310,6 +310,25 @@ def main():
         log(f"bench: decode-only step C3: write + decode {step_ms['write_then_decode'] * 1e3:.1f} us, "
             f"fused {step_ms['fused'] * 1e3:.1f} us")
         del pools
+        # copy on write of prefix sharing: 4096 whole blocks (both pools, 2 kv
+        # heads, D 128, bf16: 8 KiB per block and pool) copied in one launch;
+        # three disjoint pair sets in rotation (400 MB touched) so the 256 MB
+        # MALL cannot hold the sources
+        kc = torch.zeros(30000, HKV, 16, D, dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros(30000, HKV, D, 16, dtype=torch.bfloat16, device=dev)
+        perm = np.random.default_rng(1007).permutation(30000)
+        sets = [torch.from_numpy(np.stack([perm[i * 8192:i * 8192 + 4096], perm[i * 8192 + 4096:(i + 1) * 8192]],
+                                          1).astype(np.int32)).to(dev) for i in range(3)]
+        for i in range(3):
+            mi.attn_copy_blocks(kc, vc, sets[i])
+        torch.cuda.synchronize()
+        tc = EventTimer(torch)
+        for i in range(max(12, args.steps)):
+            e = tc.start(); mi.attn_copy_blocks(kc, vc, sets[i % 3]); tc.stop(e)
+        torch.cuda.synchronize()
+        out["copy_blocks"] = dict(ms=tc.mean_ms(), bytes=4096 * 2 * HKV * 16 * D * ELT * 2)
+        log(f"bench: copy 4096 blocks {tc.mean_ms() * 1e3:.1f} us")
+        del kc, vc
 
     # ------------------------------------------------------------------ CPU baseline (oracle)
     cpu = None
@@ -438,6 +457,11 @@ def emit(args, out, cpu):
             "fused_us": round(d["fused"] * 1e3, 2),
             "fused_GB/s": round(d["bytes"] / (d["fused"] / 1e3) / 1e9, 1),
             "fused_frac_of_hbm_peak": round(d["bytes"] / (d["fused"] / 1e3) / PEAK_HBM, 4)}
+    if "copy_blocks" in out:
+        c = out["copy_blocks"]
+        gb = c["bytes"] / (c["ms"] / 1e3) / 1e9
+        comps["copy_on_write_4096_blocks"] = {"us": round(c["ms"] * 1e3, 2), "GB/s": round(gb, 1),
+                                              "frac_of_hbm_peak": round(gb * 1e9 / PEAK_HBM, 4)}
     res["components"] = comps
     if "value" not in res:
         res["value"] = None

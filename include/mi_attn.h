@@ -332,6 +332,42 @@ ATTN_API int attn_pool_refcount(const attn_pool* pool, int32_t id);
 ATTN_API int attn_seq_reserve(attn_pool* pool, int32_t* block_table_row, int32_t max_blocks,
                      int32_t cur_len, int32_t n_new, int32_t* slot_mapping_out);
 
+/* Prefix sharing.  §Paged Attention Kernels: blocks are shared when
+ * sequences have a common prefix.  attn_seq_fork gives child_row (host,
+ * max_blocks entries) the first ceil(len / block_size) entries of parent_row,
+ * each block retained once more; parent and child then read the same
+ * physical blocks.  On error nothing changes. */
+ATTN_API int attn_seq_fork(attn_pool* pool, const int32_t* parent_row, int32_t len, int32_t* child_row,
+                  int32_t max_blocks);
+/* attn_seq_reserve for a row whose blocks may be shared: when the first new
+ * token falls into a partly filled block (cur_len % block_size != 0) that
+ * another sequence still references (refcount > 1), the sequence first gets
+ * a fresh block in its place (the shared one loses this reference) and
+ * copy_pair_out (host int32[2]) = {shared id, fresh id}: the caller copies
+ * the block's contents (attn_copy_blocks) before writing the new tokens.
+ * Otherwise copy_pair_out = {-1, -1}.  All or nothing: NOMEM (the fresh
+ * block and the growth together) changes nothing. */
+ATTN_API int attn_seq_reserve_cow(attn_pool* pool, int32_t* block_table_row, int32_t max_blocks,
+                         int32_t cur_len, int32_t n_new, int32_t* slot_mapping_out,
+                         int32_t* copy_pair_out);
+
+/* -------------------------------------------------------------------------
+ * attn_copy_blocks -- copy whole cache blocks, both pools, every kv head:
+ * for each pair p, block pairs[p][1] of k_cache and of v_cache becomes a
+ * copy of block pairs[p][0] (the copy-on-write step of prefix sharing).
+ *
+ *   k_cache, v_cache  device, [num_blocks][num_kv_heads][block_size][D] and
+ *                     [num_blocks][num_kv_heads][D][block_size]
+ *   pairs             device int32 [num_pairs][2] (src, dst); a pair with an
+ *                     id outside [0, num_blocks) or src == dst is skipped.
+ *                     Destinations must be distinct and no destination may be
+ *                     a source of the same call.
+ *   dtype             BF16 or F32
+ * ---------------------------------------------------------------------- */
+ATTN_API int attn_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                     attn_dtype dtype, attn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,8 @@ def test_header_declares_entry_points():
     syms = declared_symbols()
     for name in ("attn_prefill", "attn_prefill_paged", "attn_prefill_workspace_size", "attn_decode_paged_plan",
                  "attn_prefill_paged_workspace_size", "attn_decode_paged", "attn_decode_paged_workspace_size",
-                 "attn_decode_paged_rope", "attn_prefill_masked",
+                 "attn_decode_paged_rope", "attn_prefill_masked", "attn_seq_fork", "attn_seq_reserve_cow",
+                 "attn_copy_blocks",
                  "attn_kv_cache_write_rope", "attn_pool_create", "attn_pool_alloc", "attn_pool_free",
                  "attn_pool_retain", "attn_seq_reserve", "attn_last_error"):
         assert name in syms
@@ -216,6 +217,25 @@ def decode_rope(lib, **kw):
 def test_decode_rope_rejects(lib, kw, status):
     assert decode_rope(lib, **kw) == status
     assert "attn_decode_paged_rope" in mi.attn_last_error()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kc=None), ATTN_E_INVALID),
+    (dict(pairs=None), ATTN_E_INVALID),
+    (dict(n=-1), ATTN_E_INVALID),
+    (dict(nb=0), ATTN_E_INVALID),
+    (dict(d=96), ATTN_E_UNSUPPORTED),
+    (dict(bs=32), ATTN_E_UNSUPPORTED),
+    (dict(dtype=7), ATTN_E_UNSUPPORTED),
+    (dict(vc=P + 8), ATTN_E_INVALID),
+    (dict(pairs=P + 2), ATTN_E_INVALID),
+])
+def test_copy_blocks_rejects(lib, kw, status):
+    a = dict(kc=P, vc=P, pairs=P, n=4, hkv=2, d=128, bs=16, nb=100, dtype=ATTN_BF16)
+    a.update(kw)
+    assert lib.attn_copy_blocks(a["kc"], a["vc"], a["pairs"], a["n"], a["hkv"], a["d"], a["bs"], a["nb"],
+                                a["dtype"], None) == status
+    assert lib.attn_last_error().decode().startswith("attn_copy_blocks")
 
 
 def test_decode_workspace_size(lib):

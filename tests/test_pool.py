@@ -156,3 +156,139 @@ def test_fragmentation_readings():
     q.free(g.permutation(first))
     got2 = q.alloc(nb)
     assert sorted(got2.tolist()) == list(range(nb))
+
+
+# ------------------------------------------------------------------ prefix sharing, copy on write
+
+def test_fork_shares_blocks():
+    p = Pool(20, 16)
+    parent = np.full(8, -1, np.int32)
+    p.seq_reserve(parent, 0, 37)                 # 3 blocks, the last holds 5 tokens
+    child = np.full(8, -1, np.int32)
+    p.seq_fork(parent, 37, child)
+    np.testing.assert_array_equal(child[:3], parent[:3])
+    assert np.all(child[3:] == -1)
+    assert [p.refcount(int(b)) for b in parent[:3]] == [2, 2, 2]
+    p.seq_fork(parent, 0, child)                 # nothing to share
+    assert [p.refcount(int(b)) for b in parent[:3]] == [2, 2, 2]
+
+
+def test_fork_validates_first():
+    p = Pool(10, 16)
+    parent = np.array([0, 1, 7, -1], np.int32)   # block 7 was never allocated
+    p.alloc(2)
+    child = np.full(4, -1, np.int32)
+    with pytest.raises(AttnError) as e:
+        p.seq_fork(parent, 40, child)
+    assert e.value.status == ATTN_E_STATE
+    assert [p.refcount(i) for i in (0, 1, 7)] == [1, 1, 0] and np.all(child == -1)
+    with pytest.raises(AttnError) as e:
+        p.seq_fork(parent, 40, np.full(2, -1, np.int32))   # the child row is too short
+    assert e.value.status == ATTN_E_INVALID
+
+
+def test_reserve_cow_copies_a_shared_partial_block():
+    p = Pool(20, 16)
+    parent = np.full(8, -1, np.int32)
+    p.seq_reserve(parent, 0, 37)
+    child = np.full(8, -1, np.int32)
+    p.seq_fork(parent, 37, child)
+    shared = int(parent[2])
+    slots, pair = p.seq_reserve_cow(child, 37, 20)   # tokens 37..56: block 2 (11 more), block 3
+    assert pair == (shared, int(child[2])) and child[2] != shared
+    assert p.refcount(shared) == 1 and p.refcount(int(child[2])) == 1 and p.refcount(int(child[3])) == 1
+    np.testing.assert_array_equal(child[:2], parent[:2])       # full blocks stay shared
+    assert p.refcount(int(parent[0])) == 2
+    t = np.arange(37, 57)
+    np.testing.assert_array_equal(slots, child[t // 16] * 16 + t % 16)
+    assert not set(slots // 16) & set(parent[:3].tolist())     # no new token lands in a parent block
+    # the parent, now the only holder of its last block, appends without a copy
+    _, pair = p.seq_reserve_cow(parent, 37, 3)
+    assert pair is None
+
+
+def test_reserve_cow_no_copy_cases():
+    p = Pool(20, 16)
+    parent = np.full(8, -1, np.int32)
+    p.seq_reserve(parent, 0, 32)                 # two full blocks
+    child = np.full(8, -1, np.int32)
+    p.seq_fork(parent, 32, child)
+    _, pair = p.seq_reserve_cow(child, 32, 5)    # the next token starts a new block
+    assert pair is None and child[2] not in parent[:2]
+    other = np.full(8, -1, np.int32)
+    p.seq_fork(parent, 30, other)                # shares two blocks, the second partly filled
+    _, pair = p.seq_reserve_cow(other, 30, 0)    # nothing appended: nothing copied
+    assert pair is None and other[1] == parent[1]
+
+
+def test_reserve_cow_out_of_memory_changes_nothing():
+    p = Pool(5, 16)
+    parent = np.full(4, -1, np.int32)
+    p.seq_reserve(parent, 0, 37)                 # 3 of 5 blocks
+    child = np.full(4, -1, np.int32)
+    p.seq_fork(parent, 37, child)
+    p.alloc(1)                                   # one block left: the copy fits, the growth does not
+    before = ([p.refcount(i) for i in range(5)], p.num_free, child.copy())
+    with pytest.raises(AttnError) as e:
+        p.seq_reserve_cow(child, 37, 20)
+    assert e.value.status == ATTN_E_NOMEM
+    assert ([p.refcount(i) for i in range(5)], p.num_free) == before[:2]
+    np.testing.assert_array_equal(child, before[2])
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_cow_random_against_model(seed):
+    """Random forks, appends and releases: the pool's refcounts and free count
+    follow a brute-force model, and after every append the block receiving the
+    sequence's next token is held by that sequence alone."""
+    g = rng(seed)
+    NB, BS, MAXB = 64, 16, 12
+    p = Pool(NB, BS)
+    ref = np.zeros(NB, np.int64)
+    seqs = []                                    # [row, length]
+    for _ in range(300):
+        op = g.integers(0, 4)
+        if op == 0 or not seqs:                  # new sequence
+            row = np.full(MAXB, -1, np.int32)
+            n = int(g.integers(1, 60))
+            try:
+                p.seq_reserve(row, 0, n)
+            except AttnError:
+                continue
+            ref[row[: -(-n // BS)]] += 1
+            seqs.append([row, n])
+        elif op == 1:                            # fork a prefix of a sequence
+            row, n = seqs[g.integers(len(seqs))]
+            k = int(g.integers(0, n + 1))
+            child = np.full(MAXB, -1, np.int32)
+            p.seq_fork(row, k, child)
+            ref[child[: -(-k // BS)]] += 1
+            seqs.append([child, k])
+        elif op == 2:                            # append
+            s = seqs[g.integers(len(seqs))]
+            row, n = s
+            k = int(g.integers(1, 30))
+            if -(-(n + k) // BS) > MAXB:
+                continue
+            old = row.copy()
+            try:
+                slots, pair = p.seq_reserve_cow(row, n, k)
+            except AttnError as e:
+                assert e.status == ATTN_E_NOMEM
+                np.testing.assert_array_equal(row, old)
+                continue
+            if pair is not None:
+                assert n % BS and pair[0] == old[n // BS] and row[n // BS] == pair[1]
+                ref[pair[0]] -= 1
+                ref[pair[1]] += 1
+            have, need = -(-n // BS), -(-(n + k) // BS)
+            ref[row[have:need]] += 1
+            assert p.refcount(int(row[n // BS])) == 1    # the next token's block is private
+            s[1] = n + k
+        else:                                    # release a sequence
+            row, n = seqs.pop(g.integers(len(seqs)))
+            ids = row[: -(-n // BS)]
+            p.free(ids)
+            ref[ids] -= 1
+        assert [p.refcount(i) for i in range(NB)] == ref.tolist()
+        assert p.num_free == int((ref == 0).sum())

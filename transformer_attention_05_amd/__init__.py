@@ -18,6 +18,7 @@ import torch
 __all__ = [
     "AttnError",
     "Pool",
+    "attn_copy_blocks",
     "attn_decode_paged",
     "attn_decode_paged_auto_partition",
     "attn_decode_paged_rope",
@@ -80,6 +81,9 @@ _SIGNATURES = {
     "attn_pool_num_blocks": (_c_i32, [_vp]),
     "attn_pool_refcount": (ctypes.c_int, [_vp, _c_i32]),
     "attn_seq_reserve": (ctypes.c_int, [_vp, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p]),
+    "attn_seq_fork": (ctypes.c_int, [_vp, _c_i32p, _c_i32, _c_i32p, _c_i32]),
+    "attn_seq_reserve_cow": (ctypes.c_int, [_vp, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32p]),
+    "attn_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int, _vp]),
 }
 
 _lib = None
@@ -331,6 +335,14 @@ def attn_decode_paged_rope(q, k_new, v_new, positions, slot_mapping, k_cache, v_
     return o
 
 
+def attn_copy_blocks(k_cache, v_cache, pairs):
+    """Copy whole blocks of both caches: ``pairs`` is an int32 GPU tensor
+    [n, 2] of (src, dst) block ids."""
+    nb, hkv, bs, d = k_cache.shape
+    _check(load().attn_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(pairs, "pairs"),
+                                   int(pairs.shape[0]), hkv, d, bs, nb, _dtype_code(k_cache), _stream(k_cache)))
+
+
 def attn_kv_cache_write_rope(q, k, v, positions, slot_mapping, k_cache, v_cache, rope_base=10000.0):
     """Rotate q (in place, may be None) and k; write rotated k and v into their slots."""
     n, hkv, d = k.shape
@@ -395,6 +407,29 @@ class Pool:
         if r < 0:
             _check(r)
         return int(r)
+
+    def seq_fork(self, parent_row: np.ndarray, length: int, child_row: np.ndarray):
+        """Share the blocks holding the first ``length`` tokens of the parent
+        with the child (child_row updated in place)."""
+        for name, r in (("parent_row", parent_row), ("child_row", child_row)):
+            if r.dtype != np.int32 or not r.flags["C_CONTIGUOUS"]:
+                raise ValueError(f"{name} must be a contiguous int32 array")
+        _check(self._lib.attn_seq_fork(self._h, parent_row.ctypes.data_as(_c_i32p), int(length),
+                                       child_row.ctypes.data_as(_c_i32p), child_row.size))
+
+    def seq_reserve_cow(self, row: np.ndarray, cur_len: int, n_new: int):
+        """seq_reserve that first gives the sequence its own copy of a shared,
+        partly filled last block: returns (slots, (src, dst) or None), the
+        block pair attn_copy_blocks must copy before the new tokens are
+        written."""
+        if row.dtype != np.int32 or not row.flags["C_CONTIGUOUS"]:
+            raise ValueError("row must be a contiguous int32 array (it is updated in place)")
+        slots = np.zeros(max(int(n_new), 0), dtype=np.int32)
+        pair = np.full(2, -1, dtype=np.int32)
+        _check(self._lib.attn_seq_reserve_cow(self._h, row.ctypes.data_as(_c_i32p), row.size, int(cur_len),
+                                              int(n_new), slots.ctypes.data_as(_c_i32p),
+                                              pair.ctypes.data_as(_c_i32p)))
+        return slots, (None if pair[0] < 0 else (int(pair[0]), int(pair[1])))
 
     def seq_reserve(self, row: np.ndarray, cur_len: int, n_new: int) -> np.ndarray:
         """Grow a sequence in place: ``row`` is its int32 block-table row."""

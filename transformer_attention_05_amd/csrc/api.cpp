@@ -607,3 +607,26 @@ extern "C" int attn_kv_cache_write_rope(void* q, const void* k, const void* v, c
   if (a.rope) a.freqs = rope_freqs(rope_base, head_dim);
   return launched(launch_rope_write(a, head_dim, dtype == ATTN_BF16, reinterpret_cast<hipStream_t>(stream)), fn);
 }
+
+// ---------------------------------------------------------------------------
+extern "C" int attn_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int32_t num_pairs,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                attn_dtype dtype, attn_stream_t stream) {
+  static const char* fn = "attn_copy_blocks";
+  if (!k_cache || !v_cache || (num_pairs > 0 && !pairs))
+    return fail(ATTN_E_INVALID, "%s: k_cache, v_cache and pairs must be non-NULL", fn);
+  if (num_pairs < 0 || num_blocks < 1 || num_kv_heads < 1) return fail(ATTN_E_INVALID, "%s: bad size", fn);
+  int st;
+  if ((st = check_head_dim(head_dim, fn)) != ATTN_OK) return st;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  if (block_size != kBlockSizeHost) return fail(ATTN_E_UNSUPPORTED, "%s: block_size %d (supported: 16)", fn, block_size);
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return fail(ATTN_E_INVALID, "%s: cache pointers must be 16-byte aligned", fn);
+  if (!aligned(pairs, 4)) return fail(ATTN_E_INVALID, "%s: pairs must be 4-byte aligned", fn);
+  if (num_pairs == 0) return ok();
+  CopyBlocksArgs a{};
+  a.k_cache = k_cache; a.v_cache = v_cache; a.pairs = pairs;
+  a.num_pairs = num_pairs; a.num_blocks = num_blocks;
+  a.block_bytes = (int64_t)num_kv_heads * kBlockSizeHost * head_dim * (dtype == ATTN_BF16 ? 2 : 4);
+  return launched(launch_copy_blocks(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}

@@ -97,6 +97,15 @@ struct RopeWriteArgs {
   RopeFreqs freqs;
 };
 
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* pairs;  // [num_pairs][2] (src, dst)
+  int32_t num_pairs;
+  int32_t num_blocks;    // ids outside [0, num_blocks) are skipped
+  int64_t block_bytes;   // bytes of one block of one pool (a multiple of 16)
+};
+
 // Launchers return the launch status (hipSuccess or the error).
 // hpw: query heads sharing each K/V tile (1 or 2); wph: wavefronts of 32
 // queries per head (4 or 2).  Query tile = 32 * wph rows.
@@ -104,6 +113,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, i
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStream_t s);
 hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 
 // Tile geometry of the bf16 prefill kernel, used to size its grid.
 constexpr int kPrefillBlockN = 64;

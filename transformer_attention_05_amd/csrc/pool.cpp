@@ -143,3 +143,54 @@ extern "C" int attn_seq_reserve(attn_pool* pool, int32_t* row, int32_t max_block
     }
   return mi_attn::ok();
 }
+
+extern "C" int attn_seq_fork(attn_pool* pool, const int32_t* parent_row, int32_t len, int32_t* child_row,
+                             int32_t max_blocks) {
+  static const char* fn = "attn_seq_fork";
+  if (!pool) return mi_attn::fail(ATTN_E_INVALID, "%s: pool is NULL", fn);
+  if (!parent_row || !child_row) return mi_attn::fail(ATTN_E_INVALID, "%s: rows must be non-NULL", fn);
+  if (len < 0 || max_blocks < 0) return mi_attn::fail(ATTN_E_INVALID, "%s: negative size", fn);
+  const int64_t n = ((int64_t)len + pool->block_size - 1) / pool->block_size;
+  if (n > max_blocks)
+    return mi_attn::fail(ATTN_E_INVALID, "%s: %lld blocks to share, child row holds %d", fn, (long long)n,
+                         max_blocks);
+  int st = attn_pool_retain(pool, parent_row, (int32_t)n);  // validates every id first
+  if (st != ATTN_OK) return st;
+  if (child_row != parent_row) std::memmove(child_row, parent_row, (size_t)n * sizeof(int32_t));
+  return mi_attn::ok();
+}
+
+extern "C" int attn_seq_reserve_cow(attn_pool* pool, int32_t* row, int32_t max_blocks, int32_t cur_len,
+                                    int32_t n_new, int32_t* slot_mapping_out, int32_t* copy_pair_out) {
+  static const char* fn = "attn_seq_reserve_cow";
+  if (!pool) return mi_attn::fail(ATTN_E_INVALID, "%s: pool is NULL", fn);
+  if (!row || !copy_pair_out) return mi_attn::fail(ATTN_E_INVALID, "%s: row and copy_pair_out must be non-NULL", fn);
+  if (max_blocks < 0 || cur_len < 0 || n_new < 0) return mi_attn::fail(ATTN_E_INVALID, "%s: negative size", fn);
+  const int64_t bs = pool->block_size;
+  const int64_t have = (cur_len + bs - 1) / bs;
+  const int64_t need = ((int64_t)cur_len + n_new + bs - 1) / bs;
+  if (need > max_blocks)
+    return mi_attn::fail(ATTN_E_INVALID, "%s: %lld blocks needed, row holds %d", fn, (long long)need, max_blocks);
+  for (int64_t b = 0; b < have; ++b)
+    if (row[b] < 0 || row[b] >= pool->num_blocks || pool->refcount[row[b]] == 0)
+      return mi_attn::fail(ATTN_E_STATE, "%s: row entry %lld (%d) is not an allocated block", fn, (long long)b,
+                           row[b]);
+  // the next token lands in a partly filled block that another sequence
+  // still references: this sequence gets its own copy of it
+  const bool cow = n_new > 0 && cur_len % bs != 0 && pool->refcount[row[have - 1]] > 1;
+  const int64_t fresh = (need - have) + (cow ? 1 : 0);
+  if (fresh > (int64_t)pool->free_stack.size())
+    return mi_attn::fail(ATTN_E_NOMEM, "%s: %lld blocks needed, %zu free", fn, (long long)fresh,
+                         pool->free_stack.size());
+  copy_pair_out[0] = copy_pair_out[1] = -1;
+  if (cow) {
+    int32_t id;
+    attn_pool_alloc(pool, 1, &id);
+    const int32_t old = row[have - 1];
+    --pool->refcount[old];  // still > 0: another sequence holds it
+    row[have - 1] = id;
+    copy_pair_out[0] = old;
+    copy_pair_out[1] = id;
+  }
+  return attn_seq_reserve(pool, row, max_blocks, cur_len, n_new, slot_mapping_out);
+}
