@@ -11,3 +11,4 @@ from .attention import (  # noqa: F401
     rope,
     round_bf16,
 )
+from .rmsnorm import residual_rms_norm  # noqa: F401

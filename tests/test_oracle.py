@@ -370,3 +370,68 @@ def test_cache_write_rotates_keys_only_and_skips():
         np.testing.assert_array_equal(kc[slots[i] // bs, :, slots[i] % bs], kr[i])
         np.testing.assert_array_equal(vc[slots[i] // bs, :, :, slots[i] % bs], v[i])
     assert np.count_nonzero(np.abs(kc).sum(axis=-1)) == (n - 1) * hkv
+
+
+# ------------------------------------------------------------------ fused residual + RMSNorm
+
+def brute_rms_norm(x, r, w, eps):
+    """Pure-Python loops with math.fsum: one row at a time."""
+    out, hs = [], []
+    for xi, ri in zip(x, r):
+        h = [float(np.float32(a) + np.float32(b)) for a, b in zip(xi, ri)]
+        ms = math.fsum(v * v for v in h) / len(h)
+        out.append([v / math.sqrt(ms + eps) * wj for v, wj in zip(h, w)])
+        hs.append(h)
+    return np.array(out), np.array(hs)
+
+
+def test_rms_norm_brute_force():
+    g = rng(71)
+    x, r = g.standard_normal((5, 24)), g.standard_normal((5, 24))
+    w = g.standard_normal(24)
+    y, h = oracle.residual_rms_norm(x, r, w, eps=1e-3, bf16=False)
+    yb, hb = brute_rms_norm(x, r, w, 1e-3)
+    np.testing.assert_allclose(h, hb, rtol=0, atol=0)
+    np.testing.assert_allclose(y, yb, rtol=1e-13, atol=1e-14)
+
+
+def test_rms_norm_one_hot_closed_form():
+    """A row whose sum is a * e_k: mean square a^2 / H, so the output is
+    a w_k / sqrt(a^2 / H + eps) at k and 0 elsewhere."""
+    H, a, k, eps = 16, 3.0, 5, 1e-6
+    x = np.zeros((1, H)); r = np.zeros((1, H)); x[0, k] = 1.0; r[0, k] = a - 1.0
+    w = np.arange(1, H + 1, dtype=np.float64)
+    y, h = oracle.residual_rms_norm(x, r, w, eps=eps)
+    want = np.zeros(H); want[k] = a * w[k] / math.sqrt(a * a / H + eps)
+    np.testing.assert_allclose(y[0], want, rtol=1e-15, atol=0)
+    assert h[0, k] == a
+
+
+def test_rms_norm_invariants():
+    """With unit weights each output row has root mean square
+    sqrt(ms / (ms + eps)); the map commutes with a permutation of the hidden
+    dimension (weights permuted alike); with eps = 0 it is invariant to
+    scaling the row by a power of two (exact in float32 and bf16)."""
+    g = rng(72)
+    x, r = g.standard_normal((6, 40)), g.standard_normal((6, 40))
+    eps = 1e-2
+    y, h = oracle.residual_rms_norm(x, r, np.ones(40), eps=eps)
+    ms = np.mean(h * h, axis=1)
+    np.testing.assert_allclose(np.sqrt(np.mean(y * y, axis=1)), np.sqrt(ms / (ms + eps)), rtol=1e-14)
+    w = g.standard_normal(40)
+    perm = g.permutation(40)
+    y1, _ = oracle.residual_rms_norm(x, r, w)
+    y2, _ = oracle.residual_rms_norm(x[:, perm], r[:, perm], w[perm])
+    np.testing.assert_allclose(y2, y1[:, perm], rtol=1e-14, atol=0)
+    y3, _ = oracle.residual_rms_norm(8 * x, 8 * r, w, eps=0.0)
+    y4, _ = oracle.residual_rms_norm(x, r, w, eps=0.0)
+    np.testing.assert_allclose(y3, y4, rtol=1e-14, atol=0)
+
+
+def test_rms_norm_stored_residual_is_bf16_of_the_float32_sum():
+    """The updated residual: 1 + 2^-8 (exact in float32) rounds to nearest
+    even in bf16 (to 1.0); 1 + 3 * 2^-8 rounds up to 1 + 2^-6."""
+    x = np.array([[1.0, 1.0]])
+    r = np.array([[2.0 ** -8, 3 * 2.0 ** -8]])
+    _, h = oracle.residual_rms_norm(x, r, np.ones(2))
+    assert h[0, 0] == 1.0 and h[0, 1] == 1.0 + 2.0 ** -6
