@@ -330,6 +330,27 @@ def main():
         log(f"bench: copy 4096 blocks {tc.mean_ms() * 1e3:.1f} us")
         del kc, vc
 
+    # ------------------------------------------------------------------ fused residual + RMSNorm
+    if not args.no_components and args.only in (None, "decode"):
+        # the mixed step's 4224 new tokens at the tutorial model's hidden width
+        # 1536, bf16; three input sets in rotation (78 MB touched)
+        g = np.random.default_rng(1008)
+        sets = [tuple(torch.from_numpy(g.standard_normal((4224, 1536)).astype(np.float32)).to(dev, torch.bfloat16)
+                      for _ in range(2)) for _ in range(3)]
+        wgt = torch.ones(1536, dtype=torch.bfloat16, device=dev)
+        yb = torch.empty(4224, 1536, dtype=torch.bfloat16, device=dev)
+        hb = torch.empty_like(yb)
+        for i in range(3):
+            mi.attn_residual_rms_norm(*sets[i], wgt, y=yb, residual_out=hb)
+        torch.cuda.synchronize()
+        tn = EventTimer(torch)
+        for i in range(max(12, args.steps)):
+            e = tn.start(); mi.attn_residual_rms_norm(*sets[i % 3], wgt, y=yb, residual_out=hb); tn.stop(e)
+        torch.cuda.synchronize()
+        out["rmsnorm"] = dict(ms=tn.mean_ms(), bytes=4224 * 1536 * ELT * 4 + 1536 * ELT)
+        log(f"bench: residual + RMSNorm 4224 x 1536 {tn.mean_ms() * 1e3:.1f} us")
+        del sets, yb, hb
+
     # ------------------------------------------------------------------ CPU baseline (oracle)
     cpu = None
     if not args.no_cpu_baseline and "mixed" in out:
@@ -457,6 +478,11 @@ def emit(args, out, cpu):
             "fused_us": round(d["fused"] * 1e3, 2),
             "fused_GB/s": round(d["bytes"] / (d["fused"] / 1e3) / 1e9, 1),
             "fused_frac_of_hbm_peak": round(d["bytes"] / (d["fused"] / 1e3) / PEAK_HBM, 4)}
+    if "rmsnorm" in out:
+        c = out["rmsnorm"]
+        gb = c["bytes"] / (c["ms"] / 1e3) / 1e9
+        comps["residual_rmsnorm_4224x1536"] = {"us": round(c["ms"] * 1e3, 2), "GB/s": round(gb, 1),
+                                               "frac_of_hbm_peak": round(gb * 1e9 / PEAK_HBM, 4)}
     if "copy_blocks" in out:
         c = out["copy_blocks"]
         gb = c["bytes"] / (c["ms"] / 1e3) / 1e9

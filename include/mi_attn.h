@@ -299,6 +299,27 @@ ATTN_API int attn_kv_cache_write_rope(void* q, const void* k, const void* v, con
                              float rope_base, attn_dtype dtype, attn_stream_t stream);
 
 /* -------------------------------------------------------------------------
+ * attn_residual_rms_norm -- fused residual add + RMS normalisation.
+ *
+ * §Operator Fusion names "adding a residual connection and applying RMSNorm"
+ * as a fusion and gives its definition: h = x + residual (stored in the
+ * input dtype: the updated residual), y = h / sqrt(mean(h^2) + eps) * weight
+ * row by row (mean over the hidden dimension); both y and h are returned.
+ * One pass: x, residual and weight read once, y and h written once.
+ *
+ *   x, residual   device [rows][hidden]
+ *   weight        device [hidden]
+ *   y             device [rows][hidden], written; must not alias the others
+ *   residual_out  device [rows][hidden], written with h; may be residual or
+ *                 x itself (in place)
+ *   hidden        a multiple of 8, 8 .. 8192; eps finite, >= 0 (the example
+ *                 uses 1e-6); dtype BF16 or F32 (all tensors share it)
+ * ---------------------------------------------------------------------- */
+ATTN_API int attn_residual_rms_norm(const void* x, const void* residual, const void* weight, void* y,
+                           void* residual_out, int32_t rows, int32_t hidden, float eps, attn_dtype dtype,
+                           attn_stream_t stream);
+
+/* -------------------------------------------------------------------------
  * Block pool (host only).  §Paged Attention Kernels: fixed-size blocks are
  * allocated on demand, returned to a pool when a request ends and may be
  * shared by sequences with a common prefix; a block table maps a sequence's

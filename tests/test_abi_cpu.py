@@ -32,7 +32,7 @@ def test_header_declares_entry_points():
     for name in ("attn_prefill", "attn_prefill_paged", "attn_prefill_workspace_size", "attn_decode_paged_plan",
                  "attn_prefill_paged_workspace_size", "attn_decode_paged", "attn_decode_paged_workspace_size",
                  "attn_decode_paged_rope", "attn_prefill_masked", "attn_seq_fork", "attn_seq_reserve_cow",
-                 "attn_copy_blocks",
+                 "attn_copy_blocks", "attn_residual_rms_norm",
                  "attn_kv_cache_write_rope", "attn_pool_create", "attn_pool_alloc", "attn_pool_free",
                  "attn_pool_retain", "attn_seq_reserve", "attn_last_error"):
         assert name in syms
@@ -236,6 +236,26 @@ def test_copy_blocks_rejects(lib, kw, status):
     assert lib.attn_copy_blocks(a["kc"], a["vc"], a["pairs"], a["n"], a["hkv"], a["d"], a["bs"], a["nb"],
                                 a["dtype"], None) == status
     assert lib.attn_last_error().decode().startswith("attn_copy_blocks")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), ATTN_E_INVALID),
+    (dict(rows=-1), ATTN_E_INVALID),
+    (dict(hidden=12), ATTN_E_UNSUPPORTED),
+    (dict(hidden=8200), ATTN_E_UNSUPPORTED),
+    (dict(hidden=0), ATTN_E_UNSUPPORTED),
+    (dict(eps=-1.0), ATTN_E_INVALID),
+    (dict(eps=float("nan")), ATTN_E_INVALID),
+    (dict(dtype=7), ATTN_E_UNSUPPORTED),
+    (dict(w=P + 8), ATTN_E_INVALID),
+    (dict(y=P), ATTN_E_INVALID),                 # y aliases x
+])
+def test_residual_rms_norm_rejects(lib, kw, status):
+    a = dict(x=P, r=P + 4096, w=P + 8192, y=P + 12288, h=P + 4096, rows=4, hidden=1536, eps=1e-6, dtype=ATTN_BF16)
+    a.update(kw)
+    assert lib.attn_residual_rms_norm(a["x"], a["r"], a["w"], a["y"], a["h"], a["rows"], a["hidden"], a["eps"],
+                                      a["dtype"], None) == status
+    assert lib.attn_last_error().decode().startswith("attn_residual_rms_norm")
 
 
 def test_decode_workspace_size(lib):

@@ -28,6 +28,7 @@ __all__ = [
     "attn_last_error",
     "attn_prefill",
     "attn_prefill_masked",
+    "attn_residual_rms_norm",
     "attn_prefill_paged",
     "attn_prefill_paged_workspace_size",
     "attn_prefill_workspace_size",
@@ -81,6 +82,8 @@ _SIGNATURES = {
     "attn_pool_num_blocks": (_c_i32, [_vp]),
     "attn_pool_refcount": (ctypes.c_int, [_vp, _c_i32]),
     "attn_seq_reserve": (ctypes.c_int, [_vp, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p]),
+    "attn_residual_rms_norm": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, ctypes.c_float, ctypes.c_int,
+                                              _vp]),
     "attn_seq_fork": (ctypes.c_int, [_vp, _c_i32p, _c_i32, _c_i32p, _c_i32]),
     "attn_seq_reserve_cow": (ctypes.c_int, [_vp, _c_i32p, _c_i32, _c_i32, _c_i32, _c_i32p, _c_i32p]),
     "attn_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int, _vp]),
@@ -333,6 +336,26 @@ def attn_decode_paged_rope(q, k_new, v_new, positions, slot_mapping, k_cache, v_
         ws_ptr, ws_bytes, _stream(q))
     _check(st)
     return o
+
+
+def attn_residual_rms_norm(x, residual, weight, eps=1e-6, y=None, residual_out=None):
+    """Fused residual add + RMSNorm over the last dimension of [rows, hidden]
+    tensors: returns (y, h) with h = x + residual (written to residual_out,
+    which may be residual itself) and y = h / rms(h) * weight."""
+    if y is None:
+        y = torch.empty_like(x)
+    if residual_out is None:
+        residual_out = torch.empty_like(x)
+    rows, hidden = x.shape
+    for name, t in (("residual", residual), ("y", y), ("residual_out", residual_out)):
+        if t.shape != x.shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [rows, hidden] tensor like x")
+    if not x.is_contiguous() or weight.shape != (hidden,) or not weight.is_contiguous():
+        raise ValueError("x must be contiguous and weight a contiguous [hidden] tensor")
+    _check(load().attn_residual_rms_norm(_dev(x, "x"), _dev(residual, "residual"), _dev(weight, "weight"),
+                                         _dev(y, "y"), _dev(residual_out, "residual_out"), rows, hidden,
+                                         float(eps), _dtype_code(x), _stream(x)))
+    return y, residual_out
 
 
 def attn_copy_blocks(k_cache, v_cache, pairs):

@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmi_attn.so")
 
-SOURCES = ["prefill.hip", "decode.hip", "rope_write.hip", "copy_blocks.hip", "api.cpp", "pool.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "rope_write.hip", "copy_blocks.hip", "rmsnorm.hip", "api.cpp", "pool.cpp"]
 ARCH = "gfx950"
 
 

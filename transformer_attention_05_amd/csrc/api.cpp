@@ -630,3 +630,27 @@ extern "C" int attn_copy_blocks(void* k_cache, void* v_cache, const int32_t* pai
   a.block_bytes = (int64_t)num_kv_heads * kBlockSizeHost * head_dim * (dtype == ATTN_BF16 ? 2 : 4);
   return launched(launch_copy_blocks(a, reinterpret_cast<hipStream_t>(stream)), fn);
 }
+
+// ---------------------------------------------------------------------------
+extern "C" int attn_residual_rms_norm(const void* x, const void* residual, const void* weight, void* y,
+                                      void* residual_out, int32_t rows, int32_t hidden, float eps, attn_dtype dtype,
+                                      attn_stream_t stream) {
+  static const char* fn = "attn_residual_rms_norm";
+  if (!x || !residual || !weight || !y || !residual_out)
+    return fail(ATTN_E_INVALID, "%s: pointer arguments must be non-NULL", fn);
+  if (rows < 0) return fail(ATTN_E_INVALID, "%s: rows < 0", fn);
+  if (hidden < 8 || hidden % 8 != 0 || hidden > 8192)
+    return fail(ATTN_E_UNSUPPORTED, "%s: hidden %d (supported: multiples of 8 up to 8192)", fn, hidden);
+  if (!std::isfinite(eps) || eps < 0.f) return fail(ATTN_E_INVALID, "%s: eps must be finite and >= 0", fn);
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  const void* ptrs[] = {x, residual, weight, y, residual_out};
+  for (const void* p : ptrs)
+    if (!aligned(p, 16)) return fail(ATTN_E_INVALID, "%s: pointers must be 16-byte aligned", fn);
+  if (y == x || y == residual || y == residual_out)
+    return fail(ATTN_E_INVALID, "%s: y must not alias an input or residual_out", fn);
+  if (rows == 0) return ok();
+  RmsNormArgs a{};
+  a.x = x; a.residual = residual; a.weight = weight; a.y = y; a.h_out = residual_out;
+  a.rows = rows; a.hidden = hidden; a.eps = eps;
+  return launched(launch_residual_rms_norm(a, dtype == ATTN_BF16, reinterpret_cast<hipStream_t>(stream)), fn);
+}

@@ -106,6 +106,17 @@ struct CopyBlocksArgs {
   int64_t block_bytes;   // bytes of one block of one pool (a multiple of 16)
 };
 
+struct RmsNormArgs {
+  const void* x;         // [rows][hidden]
+  const void* residual;  // [rows][hidden]
+  const void* weight;    // [hidden]
+  void* y;               // [rows][hidden] normalised rows
+  void* h_out;           // [rows][hidden] updated residual (may alias x or residual)
+  int64_t rows;
+  int32_t hidden;        // a multiple of 8, at most 8192
+  float eps;
+};
+
 // Launchers return the launch status (hipSuccess or the error).
 // hpw: query heads sharing each K/V tile (1 or 2); wph: wavefronts of 32
 // queries per head (4 or 2).  Query tile = 32 * wph rows.
@@ -114,6 +125,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s)
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStream_t s);
 hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
+hipError_t launch_residual_rms_norm(const RmsNormArgs& a, bool bf16, hipStream_t s);
 
 // Tile geometry of the bf16 prefill kernel, used to size its grid.
 constexpr int kPrefillBlockN = 64;
