@@ -89,25 +89,20 @@ def write_bytes(n_tokens):
 
 # ----------------------------------------------------------------------------- timing helpers
 
-class EventTimer:
-    """Accumulates GPU time between event pairs on the current stream."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
-
-    def start(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def stop(self, e0):
-        e1 = self.torch.cuda.Event(enable_timing=True)
-        e1.record()
-        self.pairs.append((e0, e1))
-
-    def mean_ms(self):
-        return float(np.mean([a.elapsed_time(b) for a, b in self.pairs])) if self.pairs else float("nan")
+def per_call_ms(torch, fn, n):
+    """Average duration of one call, in ms, over n back-to-back calls fn(0) ..
+    fn(n - 1): one pair of HIP events on the current stream (the stream the
+    calls launch on) around all of them.  An event recorded between two
+    kernels leaves the GPU idle for several microseconds on this stack, so
+    per-call event pairs would inflate short kernels."""
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(n):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
 
 
 def main():
@@ -167,17 +162,13 @@ def main():
             step.run()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / args.steps
-        # per-stage durations: each stage repeated on its own, HIP events on
-        # the stream the kernels are launched on around every call
+        # per-stage durations: each stage repeated on its own, back to back,
+        # between two HIP events on the stream the kernels are launched on
         stage_ms = []
         for fn in (step.write, step.prefill, step.decode):
             fn()
             torch.cuda.synchronize()
-            tm = EventTimer(torch)
-            for _ in range(args.steps):
-                e = tm.start(); fn(); tm.stop(e)
-            torch.cuda.synchronize()
-            stage_ms.append(tm.mean_ms())
+            stage_ms.append(per_call_ms(torch, lambda i: fn(), args.steps))
         ms_wr, ms_pre, ms_dec = stage_ms
         # the same step captured in a HIP graph, replays back to back
         graph_s = None
@@ -213,13 +204,10 @@ def main():
         for _ in range(max(2, args.warmup)):
             mi.attn_prefill(qd, kd, vd, o=o)
         torch.cuda.synchronize()
-        tp = EventTimer(torch)
-        for _ in range(max(5, args.steps // 2)):
-            e = tp.start(); mi.attn_prefill(qd, kd, vd, o=o); tp.stop(e)
-        torch.cuda.synchronize()
+        ms = per_call_ms(torch, lambda i: mi.attn_prefill(qd, kd, vd, o=o), max(5, args.steps // 2))
         fl = 4 * D * HQ * 16384 * 16385 // 2
-        out["prefill_c4"] = dict(ms=tp.mean_ms(), flops=fl)
-        log(f"bench: prefill C4 {tp.mean_ms():.3f} ms  {fl / tp.mean_ms() / 1e9:.1f} TFLOP/s")
+        out["prefill_c4"] = dict(ms=ms, flops=fl)
+        log(f"bench: prefill C4 {ms:.3f} ms  {fl / ms / 1e9:.1f} TFLOP/s")
         del qd, kd, vd, o
         # the 2048-token prompt: too few query tiles for the GPU, so split-KV
         log("bench: contiguous prefill T 2048")
@@ -231,26 +219,20 @@ def main():
         for _ in range(max(3, args.warmup)):
             mi.attn_prefill(qd, kd, vd, o=o, workspace=ws)
         torch.cuda.synchronize()
-        tp = EventTimer(torch)
-        for _ in range(max(10, args.steps)):
-            e = tp.start(); mi.attn_prefill(qd, kd, vd, o=o, workspace=ws); tp.stop(e)
-        torch.cuda.synchronize()
+        ms = per_call_ms(torch, lambda i: mi.attn_prefill(qd, kd, vd, o=o, workspace=ws), max(10, args.steps))
         fl = 4 * D * HQ * 2048 * 2049 // 2
-        out["prefill_c2"] = dict(ms=tp.mean_ms(), flops=fl)
-        log(f"bench: prefill C2 {tp.mean_ms() * 1e3:.1f} us  {fl / tp.mean_ms() / 1e9:.1f} TFLOP/s")
+        out["prefill_c2"] = dict(ms=ms, flops=fl)
+        log(f"bench: prefill C2 {ms * 1e3:.1f} us  {fl / ms / 1e9:.1f} TFLOP/s")
         # the same shape with a general additive mask (one fp32 [T, T] mask for
         # every head, no causal structure): every (query, key) pair is computed
         mask = additive_mask(1006, (2048, 2048), amp=1.0, p_masked=0.1).to(dev)
         for _ in range(3):
             mi.attn_prefill_masked(qd, kd, vd, mask, o=o)
         torch.cuda.synchronize()
-        tp = EventTimer(torch)
-        for _ in range(max(10, args.steps)):
-            e = tp.start(); mi.attn_prefill_masked(qd, kd, vd, mask, o=o); tp.stop(e)
-        torch.cuda.synchronize()
+        ms = per_call_ms(torch, lambda i: mi.attn_prefill_masked(qd, kd, vd, mask, o=o), max(10, args.steps))
         fl = 4 * D * HQ * 2048 * 2048
-        out["prefill_masked"] = dict(ms=tp.mean_ms(), flops=fl)
-        log(f"bench: masked prefill T 2048 {tp.mean_ms() * 1e3:.1f} us  {fl / tp.mean_ms() / 1e9:.1f} TFLOP/s")
+        out["prefill_masked"] = dict(ms=ms, flops=fl)
+        log(f"bench: masked prefill T 2048 {ms * 1e3:.1f} us  {fl / ms / 1e9:.1f} TFLOP/s")
         del qd, kd, vd, o, ws, mask
 
     # ------------------------------------------------------------------ uniform decode
@@ -269,14 +251,12 @@ def main():
         for i in range(max(3, args.warmup)):
             mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws, plan=plan)
         torch.cuda.synchronize()
-        td = EventTimer(torch)
         n = max(9, args.steps)
-        for i in range(n):
-            e = td.start(); mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws, plan=plan); td.stop(e)
-        torch.cuda.synchronize()
+        ms = per_call_ms(torch, lambda i: mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws,
+                                                                 plan=plan), n)
         by = decode_bytes(dc.lengths)
-        out["decode_c3"] = dict(ms=td.mean_ms(), bytes=by, part=mi.attn_decode_paged_auto_partition(64, HKV, mx))
-        log(f"bench: decode C3 {td.mean_ms() * 1e3:.1f} us  {by / td.mean_ms() / 1e6:.0f} GB/s")
+        out["decode_c3"] = dict(ms=ms, bytes=by, part=mi.attn_decode_paged_auto_partition(64, HKV, mx))
+        log(f"bench: decode C3 {ms * 1e3:.1f} us  {by / ms / 1e6:.0f} GB/s")
         # a decode-only serving step: each sequence's new token (the last of
         # its context) rotated and written into its slot, then the decode;
         # as two launches, and as the one decode launch that writes it
@@ -301,11 +281,7 @@ def main():
             for i in range(3):
                 fn(i)
             torch.cuda.synchronize()
-            tm = EventTimer(torch)
-            for i in range(n):
-                e = tm.start(); fn(i); tm.stop(e)
-            torch.cuda.synchronize()
-            step_ms[name] = tm.mean_ms()
+            step_ms[name] = per_call_ms(torch, fn, n)
         out["decode_step_c3"] = dict(bytes=by + write_bytes(64), **step_ms)
         log(f"bench: decode-only step C3: write + decode {step_ms['write_then_decode'] * 1e3:.1f} us, "
             f"fused {step_ms['fused'] * 1e3:.1f} us")
@@ -322,12 +298,9 @@ def main():
         for i in range(3):
             mi.attn_copy_blocks(kc, vc, sets[i])
         torch.cuda.synchronize()
-        tc = EventTimer(torch)
-        for i in range(max(12, args.steps)):
-            e = tc.start(); mi.attn_copy_blocks(kc, vc, sets[i % 3]); tc.stop(e)
-        torch.cuda.synchronize()
-        out["copy_blocks"] = dict(ms=tc.mean_ms(), bytes=4096 * 2 * HKV * 16 * D * ELT * 2)
-        log(f"bench: copy 4096 blocks {tc.mean_ms() * 1e3:.1f} us")
+        ms = per_call_ms(torch, lambda i: mi.attn_copy_blocks(kc, vc, sets[i % 3]), max(12, args.steps))
+        out["copy_blocks"] = dict(ms=ms, bytes=4096 * 2 * HKV * 16 * D * ELT * 2)
+        log(f"bench: copy 4096 blocks {ms * 1e3:.1f} us")
         del kc, vc
 
     # ------------------------------------------------------------------ fused residual + RMSNorm
@@ -343,12 +316,10 @@ def main():
         for i in range(3):
             mi.attn_residual_rms_norm(*sets[i], wgt, y=yb, residual_out=hb)
         torch.cuda.synchronize()
-        tn = EventTimer(torch)
-        for i in range(max(12, args.steps)):
-            e = tn.start(); mi.attn_residual_rms_norm(*sets[i % 3], wgt, y=yb, residual_out=hb); tn.stop(e)
-        torch.cuda.synchronize()
-        out["rmsnorm"] = dict(ms=tn.mean_ms(), bytes=4224 * 1536 * ELT * 4 + 1536 * ELT)
-        log(f"bench: residual + RMSNorm 4224 x 1536 {tn.mean_ms() * 1e3:.1f} us")
+        ms = per_call_ms(torch, lambda i: mi.attn_residual_rms_norm(*sets[i % 3], wgt, y=yb, residual_out=hb),
+                         max(12, args.steps))
+        out["rmsnorm"] = dict(ms=ms, bytes=4224 * 1536 * ELT * 4 + 1536 * ELT)
+        log(f"bench: residual + RMSNorm 4224 x 1536 {ms * 1e3:.1f} us")
         del sets, yb, hb
 
     # ------------------------------------------------------------------ CPU baseline (oracle)
