@@ -195,3 +195,15 @@ def test_decode_equals_prefill_row():
     for i, r in enumerate(rows):
         d = np.abs(f64(o[i]) - f64(full[0, r])).max()
         assert d <= 1e-2, (r, d)
+
+
+@pytest.mark.parametrize("hq,hkv", [(40, 2), (34, 1)])
+def test_query_head_slices(hq, hkv):
+    """Groups of more than 16 query heads per kv head run as slices of at
+    most 16 heads (20 = 16 + 4, 34 = 16 + 16 + 2), each with its own
+    workgroups and arrival counter; several partitions per sequence."""
+    say(f"case: decode {hq}/{hkv} heads (head slices)")
+    case = decode_case(34, 9, 1, 2500, hq=hq, hkv=hkv)
+    kc, vc = build_decode_pool(case, DEV)
+    o = run_decode(case, kc, vc, partition_size=256)
+    check(f64(o), oracle_decode(case), torch.bfloat16, f"{hq}/{hkv} heads")

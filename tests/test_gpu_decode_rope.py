@@ -125,3 +125,11 @@ def test_head_dim_64_mha():
     say("case: fused decode, D 64, 8/8 heads")
     case = decode_case(53, 10, 1, 3000, hq=8, hkv=8, d=64)
     run_pair(case, part=128)
+
+
+def test_head_slices_fused():
+    """40 query heads on 2 kv heads: two head slices per kv head, each of
+    whose last-partition workgroups writes the (same) new token."""
+    say("case: fused decode, 40/2 heads")
+    case = decode_case(54, 8, 1, 2500, hq=40, hkv=2)
+    run_pair(case, part=256)
