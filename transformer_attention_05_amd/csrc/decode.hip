@@ -251,16 +251,12 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, co
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (t0 + i >= tok_end) sacc[i] = -INFINITY;
+      // this lane's 4 tokens t0 .. t0+3 are two dwords of two bf16 each
       const int nvalid = tok_end - t0;
+      const uint32_t keep0 = nvalid >= 2 ? 0xffffffffu : (nvalid == 1 ? 0xffffu : 0u);
+      const uint32_t keep1 = nvalid >= 4 ? 0xffffffffu : (nvalid == 3 ? 0xffffu : 0u);
 #pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        u32x2 w = r.v[dt];
-        if (nvalid <= 0) w = u32x2{0, 0};
-        else if (nvalid == 1) w = u32x2{w[0] & 0xffffu, 0};
-        else if (nvalid == 2) w = u32x2{w[0], 0};
-        else if (nvalid == 3) w = u32x2{w[0], w[1] & 0xffffu};
-        r.v[dt] = w;
-      }
+      for (int dt = 0; dt < D / 16; ++dt) r.v[dt] = u32x2{r.v[dt][0] & keep0, r.v[dt][1] & keep1};
     }
     float tmax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     tmax = fmaxf(tmax, xor16(tmax));

@@ -232,6 +232,15 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       krow[i] = (int64_t)((wave * LPW + i) * RPI) * a.ks_t;
       vrow[i] = (int64_t)((wave * LPW + i) * RPI) * a.vs_t;
     }
+  } else {
+    // paged K rows: the RPI rows of one DMA lie in one block, so a DMA reads
+    // from that block's (scalar) base plus this lane's byte offset within
+    // it, the same for every tile
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int r = (wave * LPW + i) * RPI + lane / CH;
+      koff[i] = 2u * (uint32_t)((r & 15) * D + 8 * ((lane % CH) ^ k_swz<D>(r)));
+    }
   }
   // LDS byte address of the ring array (the one generic-to-LDS conversion);
   // a DMA destination is this plus a uniform byte offset
@@ -245,11 +254,9 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     if constexpr (PAGED) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
-        const int ii = wave * LPW + i;
-        const int r = ii * RPI + lane / CH;  // the RPI rows of one DMA share a block
+        const int ii = wave * LPW + i;     // uniform: so is the block of its rows
         const int32_t bk = pick4(blk, (ii * RPI) >> 4);
-        dma16(kbase + (((int64_t)bk * a.hkv + g) * kBlockSize + (r & 15)) * D + 8 * ((lane % CH) ^ k_swz<D>(r)),
-              lds_of(dk) + ii * 1024);
+        dma16s(kbase + ((int64_t)bk * a.hkv + g) * (kBlockSize * D), koff[i], lds_of(dk) + ii * 1024);
       }
     } else if (n0 + BN <= tk) {
       const __bf16* tb = kb0 + (int64_t)n0 * a.ks_t;
