@@ -172,6 +172,31 @@ ATTN_API int attn_prefill_paged(const void* q, const void* k_cache, const void* 
                        float scale, int32_t causal, attn_dtype dtype,
                        void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/* attn_prefill_paged_ex -- attn_prefill_paged with a flags word (same
+ * arguments otherwise; attn_prefill_paged is this with flags 0).  The
+ * results do not depend on the flags: every query row is computed in the
+ * same order either way, so the outputs are bit-identical.
+ *
+ *   ATTN_PREFILL_SHARE_CU  the launch runs while another kernel (a paged
+ *                decode on another stream, the usual case in a serving step
+ *                that mixes chunked prefill and decode) is given the rest of
+ *                the GPU.  The prefill then takes the 4-wavefront tile, whose
+ *                registers leave room on every CU for one decode workgroup;
+ *                the default 8-wavefront tile fills a CU's register file.
+ *                Alone, the flagged launch is slower.
+ *   Other bits: ATTN_E_INVALID.  The workspace size that
+ *   attn_prefill_paged_workspace_size reports suffices for either tile. */
+#define ATTN_PREFILL_SHARE_CU 1
+ATTN_API int attn_prefill_paged_ex(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                          const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                          void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                          int32_t max_context_len,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks,
+                          float scale, int32_t causal, attn_dtype dtype, int32_t flags,
+                          void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
 /* -------------------------------------------------------------------------
  * attn_decode_paged -- one query token per sequence over its paged cache.
  *

@@ -32,7 +32,7 @@ def test_header_declares_entry_points():
     for name in ("attn_prefill", "attn_prefill_paged", "attn_prefill_workspace_size", "attn_decode_paged_plan",
                  "attn_prefill_paged_workspace_size", "attn_decode_paged", "attn_decode_paged_workspace_size",
                  "attn_decode_paged_rope", "attn_prefill_masked", "attn_seq_fork", "attn_seq_reserve_cow",
-                 "attn_copy_blocks", "attn_residual_rms_norm",
+                 "attn_copy_blocks", "attn_residual_rms_norm", "attn_prefill_paged_ex",
                  "attn_kv_cache_write_rope", "attn_pool_create", "attn_pool_alloc", "attn_pool_free",
                  "attn_pool_retain", "attn_seq_reserve", "attn_last_error"):
         assert name in syms
@@ -309,6 +309,17 @@ def test_paged_prefill_and_write_reject(lib):
     st = lib.attn_prefill_paged(P, P, P, P, 200, P, P, P, 2, 250, 200, 3200, 12, 2, 128, 16, 100, 0.0, 1,
                                 ATTN_BF16, P, need - 256, None)
     assert st == ATTN_E_NOMEM
+
+    # the flagged form: same checks, plus unknown flag bits
+    def paged_ex(flags, **kw):
+        a = dict(dtype=ATTN_BF16, ws=None, wsb=0)
+        a.update(kw)
+        return lib.attn_prefill_paged_ex(P, P, P, P, 200, P, P, P, 2, 250, 200, 3200, 12, 2, 128, 16, 100, 0.0, 1,
+                                         a["dtype"], flags, a["ws"], a["wsb"], None)
+    assert paged_ex(2) == ATTN_E_INVALID
+    assert paged_ex(-1) == ATTN_E_INVALID
+    assert paged_ex(mi.ATTN_PREFILL_SHARE_CU, dtype=ATTN_F32) == ATTN_E_UNSUPPORTED
+    assert paged_ex(mi.ATTN_PREFILL_SHARE_CU, ws=P, wsb=need - 256) == ATTN_E_NOMEM
     st = lib.attn_kv_cache_write_rope(P, P, P, P, P, P, P, 10, 12, 2, 128, 8, 100, 10000.0, ATTN_BF16, None)
     assert st == ATTN_E_UNSUPPORTED
     st = lib.attn_kv_cache_write_rope(P, None, P, P, P, P, P, 10, 12, 2, 128, 16, 100, 10000.0, ATTN_BF16, None)

@@ -94,6 +94,21 @@ def test_split_kv_chunked_prefill(ctx_hint, d):
     check(f64(o_split), f64(o_one), torch.bfloat16, "split vs one pass")
 
 
+def test_share_cu_tile_bit_identical():
+    """ATTN_PREFILL_SHARE_CU picks the 4-wavefront tile where the default is
+    the 8-wavefront one (8 chunks of 512: 192 workgroups); every row is
+    computed in the same order, so the outputs match bit for bit, and both
+    match the oracle."""
+    cached, new = [0, 300, 1000, 17, 2048, 64, 500, 5], [512] * 8
+    say("case: paged prefill, share-CU tile vs default, 8 x 512")
+    qs, ks, vs, bt, kc, vc, total = paged_setup(95, cached, new)
+    o_def, _ = run_paged(qs, bt, kc, vc, total)
+    o_sh, _ = run_paged(qs, bt, kc, vc, total, share_cu=True)
+    assert torch.equal(o_def.view(torch.int16), o_sh.view(torch.int16))
+    refs = oracle.chunked_prefill([to_f64(q) for q in qs], [to_f64(k) for k in ks], [to_f64(v) for v in vs])
+    check(f64(o_sh), np.concatenate(refs), torch.bfloat16, "share-CU chunked")
+
+
 def test_noncausal_paged():
     qs, ks, vs, bt, kc, vc, total = paged_setup(81, [40, 0], [30, 70])
     o, _ = run_paged(qs, bt, kc, vc, total, causal=False)

@@ -42,6 +42,7 @@ BLOCK_SIZE = 16
 
 ATTN_OK, ATTN_E_INVALID, ATTN_E_UNSUPPORTED, ATTN_E_NOMEM, ATTN_E_STATE, ATTN_E_DEVICE = 0, -1, -2, -3, -4, -5
 ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_PREFILL_SHARE_CU = 1  # attn_prefill_paged_ex flag
 
 _c_i32 = ctypes.c_int32
 _c_i64p = ctypes.POINTER(ctypes.c_int64)
@@ -61,6 +62,9 @@ _SIGNATURES = {
     "attn_prefill_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                                           _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
                                           _c_i32, ctypes.c_int, _vp, ctypes.c_size_t, _vp]),
+    "attn_prefill_paged_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
+                                             _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
+                                             _c_i32, ctypes.c_int, _c_i32, _vp, ctypes.c_size_t, _vp]),
     "attn_decode_paged_workspace_size": (ctypes.c_size_t, [_c_i32] * 6),
     "attn_decode_paged_auto_partition": (_c_i32, [_c_i32] * 3),
     "attn_decode_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -231,11 +235,14 @@ def attn_prefill_paged_workspace_size(num_seqs, total_q, max_seqlen_q, max_conte
 
 
 def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, context_lens, max_seqlen_q,
-                       o=None, causal=True, scale=0.0, max_context_len=0, workspace=None):
+                       o=None, causal=True, scale=0.0, max_context_len=0, workspace=None, share_cu=False):
     """Chunked prefill of packed queries q [total_q, Hq, D] over the paged caches.
 
     ``max_context_len``: the longest context (0: what the block table holds),
-    used to plan split-KV; ``workspace`` as for attn_prefill."""
+    used to plan split-KV; ``workspace`` as for attn_prefill.  ``share_cu``:
+    the launch runs beside a decode on another stream (attn_prefill_paged_ex
+    with ATTN_PREFILL_SHARE_CU; same results, a tile that leaves the decode
+    room on every CU)."""
     if o is None:
         o = torch.empty_like(q)
     total_q, hq, d = q.shape
@@ -244,11 +251,14 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, context_l
     bound = int(max_context_len) if max_context_len else block_table.shape[1] * bs
     need = attn_prefill_paged_workspace_size(s, total_q, int(max_seqlen_q), bound, hq, hkv, d)
     ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
-    st = load().attn_prefill_paged(
-        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
-        block_table.shape[1], _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(context_lens, "context_lens"),
-        _dev(o, "o"), s, total_q, int(max_seqlen_q), int(max_context_len), hq, hkv, d, bs, nb,
-        float(scale), 1 if causal else 0, _dtype_code(q), ws_ptr, ws_bytes, _stream(q))
+    args = (_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+            block_table.shape[1], _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(context_lens, "context_lens"),
+            _dev(o, "o"), s, total_q, int(max_seqlen_q), int(max_context_len), hq, hkv, d, bs, nb,
+            float(scale), 1 if causal else 0, _dtype_code(q))
+    if share_cu:
+        st = load().attn_prefill_paged_ex(*args, ATTN_PREFILL_SHARE_CU, ws_ptr, ws_bytes, _stream(q))
+    else:
+        st = load().attn_prefill_paged(*args, ws_ptr, ws_bytes, _stream(q))
     _check(st)
     return o
 

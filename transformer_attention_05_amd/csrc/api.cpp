@@ -80,7 +80,7 @@ struct PrefillTile {
   int hpw, wph;
 };
 
-PrefillTile prefill_tile(int64_t max_q, int32_t hq, int32_t group, int64_t batch, bool paged) {
+PrefillTile prefill_tile(int64_t max_q, int32_t hq, int32_t group, int64_t batch, bool paged, bool share_cu) {
   const int hpw = (group % 2 == 0) ? 2 : 1;
   // measured on MI355X.  Contiguous: 4-wavefront tiles (2 heads x 64 queries,
   // or 1 x 128) hold 80 KiB of LDS, so two workgroups share a CU and their
@@ -93,6 +93,12 @@ PrefillTile prefill_tile(int64_t max_q, int32_t hq, int32_t group, int64_t batch
   if (paged) {
     t = PrefillTile{hpw, 4};
     if (wgs(t) < 128) t.wph = 2;
+    // sharing the GPU with a decode: the 4-wavefront tile (275 VGPRs per
+    // lane) leaves room beside it for one decode workgroup (232), which the
+    // 8-wavefront tile (2 x 254 per SIMD) does not.  Measured on the mixed
+    // step: 198.5 vs 204 us, while alone the 4-wavefront chunk is slower
+    // (100 vs 85 us).
+    if (share_cu) t.wph = 2;
   }
   static const char* env = std::getenv("MI_ATTN_PREFILL_TILE");
   if (env) {
@@ -130,9 +136,9 @@ struct PrefillPlan {
 // rows: (query row, head) pairs of the output, the workspace's row count.
 // max_k: keys of the longest sequence (an upper bound for a paged batch).
 PrefillPlan plan_prefill(int64_t max_q, int64_t max_k, int32_t hq, int32_t group, int64_t batch,
-                         int32_t d, bool paged, int64_t rows) {
+                         int32_t d, bool paged, int64_t rows, bool share_cu = false) {
   PrefillPlan p;
-  p.t = prefill_tile(max_q, hq, group, batch, paged);
+  p.t = prefill_tile(max_q, hq, group, batch, paged, share_cu);
   p.num_m_tiles = ceil_div(max_q, 32 * p.t.wph);
   p.num_wg = (int64_t)p.num_m_tiles * (hq / p.t.hpw) * batch;
   // two 4-wavefront contiguous workgroups share a CU (80 KiB of LDS each)
@@ -319,7 +325,23 @@ extern "C" int attn_prefill_paged(const void* q, const void* k_cache, const void
                                   int32_t block_size, int32_t num_blocks,
                                   float scale, int32_t causal, attn_dtype dtype,
                                   void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  return attn_prefill_paged_ex(q, k_cache, v_cache, block_table, max_blocks_per_seq, cu_seqlens_q, context_lens, o,
+                               num_seqs, total_q, max_seqlen_q, max_context_len, num_q_heads, num_kv_heads,
+                               head_dim, block_size, num_blocks, scale, causal, dtype, 0, workspace,
+                               workspace_bytes, stream);
+}
+
+extern "C" int attn_prefill_paged_ex(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                     void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                     int32_t max_context_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks,
+                                     float scale, int32_t causal, attn_dtype dtype, int32_t flags,
+                                     void* workspace, size_t workspace_bytes, attn_stream_t stream) {
   static const char* fn = "attn_prefill_paged";
+  if ((flags & ~ATTN_PREFILL_SHARE_CU) != 0) return fail(ATTN_E_INVALID, "%s: unknown flags 0x%x", fn, flags);
   if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !context_lens || !o)
     return fail(ATTN_E_INVALID, "%s: pointer arguments must be non-NULL", fn);
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_context_len < 0 || max_blocks_per_seq < 1 ||
@@ -349,7 +371,7 @@ extern "C" int attn_prefill_paged(const void* q, const void* k_cache, const void
   // the plan's key bound: the caller's, else what the block table can hold
   const int64_t ctx_bound = max_context_len > 0 ? max_context_len : (int64_t)max_blocks_per_seq * kBlockSizeHost;
   PrefillPlan p = plan_prefill(max_seqlen_q, ctx_bound, num_q_heads, a.group, num_seqs, head_dim, true,
-                               (int64_t)total_q * num_q_heads);
+                               (int64_t)total_q * num_q_heads, (flags & ATTN_PREFILL_SHARE_CU) != 0);
   if ((st = use_workspace(p, workspace, workspace_bytes, a, fn)) != ATTN_OK) return st;
   a.num_m_tiles = p.num_m_tiles;
   if (p.num_wg * a.num_splits > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);

@@ -99,11 +99,15 @@ class MixedStep:
         attn_kv_cache_write_rope(self.q[lo:hi], self.k[lo:hi], self.v[lo:hi], self.positions[lo:hi],
                                  self.slots[lo:hi], self.k_cache, self.v_cache, rope_base=self.case.rope_base)
 
-    def prefill(self):
+    def prefill(self, share_cu=False):
+        """Chunked prefill; ``share_cu`` when a decode runs beside it (the
+        concurrent schedules): same results, a tile that leaves every CU room
+        for a decode workgroup."""
         R = self.R
         attn_prefill_paged(self.q[: self.n_prefill], self.k_cache, self.v_cache, self.tables[:R],
                            self.cu_seqlens_q, self.context_lens[:R], self.case.chunk, o=self.o_prefill,
-                           causal=True, max_context_len=self.max_pre_ctx, workspace=self.pre_workspace)
+                           causal=True, max_context_len=self.max_pre_ctx, workspace=self.pre_workspace,
+                           share_cu=share_cu)
 
     def decode(self):
         """Decode over the cache, whose decode tokens are already written."""
@@ -159,7 +163,7 @@ class MixedStep:
             # before the prefill's (MI355X: 234 us per step instead of 207)
             after_write = torch.cuda.Event()
             after_write.record(main)
-            self.prefill()
+            self.prefill(share_cu=True)
             with torch.cuda.stream(self.side):
                 self.side.wait_event(after_write)
                 self.decode_fused()          # writes the decode tokens itself
@@ -169,7 +173,7 @@ class MixedStep:
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)      # the step's inputs come from the caller's stream
             self.write(0, self.n_prefill)    # the chunk tokens
-            self.prefill()
+            self.prefill(share_cu=True)
             with torch.cuda.stream(self.side):
                 self.write(self.n_prefill)   # the decode tokens
                 self.decode()
