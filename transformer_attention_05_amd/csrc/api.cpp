@@ -95,8 +95,9 @@ PrefillTile prefill_tile(int64_t max_q, int32_t hq, int32_t group, int64_t batch
     if (wgs(t) < 128) t.wph = 2;
     // sharing the GPU with a decode: the 4-wavefront tile (275 VGPRs per
     // lane) leaves room beside it for one decode workgroup (232), which the
-    // 8-wavefront tile (2 x 254 per SIMD) does not.  Measured on the mixed
-    // step: 198.5 vs 204 us, while alone the 4-wavefront chunk is slower
+    // 8-wavefront tile (2 x 254 per SIMD) does not.  Measured on MI355X with
+    // 8 chunks of 512 new tokens beside a 128-sequence decode: 198.5 vs
+    // 204 us for both, while the chunks alone are slower with this tile
     // (100 vs 85 us).
     if (share_cu) t.wph = 2;
   }
