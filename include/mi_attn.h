@@ -210,7 +210,9 @@ ATTN_API int attn_prefill_paged_ex(const void* q, const void* k_cache, const voi
  * with one partition needs no combination.  One kernel launch per call.
  *
  *   q            device bf16 [num_seqs][num_q_heads][head_dim]
- *   block_table  device int32 [num_seqs][max_blocks_per_seq]
+ *   block_table  device int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                a sequence's last block (within its row) may be read, and
+ *                are never used
  *   context_lens device int32 [num_seqs], 1 .. max_context_len (the new
  *                token included)
  *   o            device bf16 [num_seqs][num_q_heads][head_dim], written

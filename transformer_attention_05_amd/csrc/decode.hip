@@ -122,11 +122,6 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
 // (with a multiple of 8, short contexts would load only a few XCDs).
 template <int D, int DWT, bool FUSED>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, const int yy, const int s, char* lds) {
-  // the grid and the block table bound what a malformed length can reach
-  const int ctx = min(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize));
-  const int nparts = (ctx + a.part_size - 1) / a.part_size;
-  if (p >= nparts) return;
-
   const int kvh = yy / a.head_groups;
   const int hgi = yy % a.head_groups;
   const int head0 = kvh * a.group + hgi * 16;
@@ -138,18 +133,43 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, co
   const int col = lane & 15;  // token (K operand) / head (Q operand, S and O columns) / channel (V operand)
   const int g4 = lane >> 4;
 
+  // The partition's block-table entries (at most 64 blocks, one per lane)
+  // and Q^T do not depend on the context length: they are loaded before it
+  // arrives, so the length's round trip overlaps theirs.  Table entries are
+  // read up to the partition's end or the row's, whichever comes first.
   const int tok_begin = p * a.part_size;
-  const int tok_end = min(ctx, tok_begin + a.part_size);
   const int blk_begin = tok_begin >> 4;
-  const int blk_end = (tok_end + 15) >> 4;
   const int32_t* bt = a.block_table + (int64_t)s * a.bt_stride;
+  // (unconditional loads from clamped indexes, selected afterwards: a load
+  // under a lane condition becomes a branch the compiler waits behind)
+  const int tab_n = min(a.bt_stride - blk_begin, a.part_size >> 4);  // entries readable, <= 0 past the row
+  const int tab_ld = bt[blk_begin + min(lane, max(tab_n - 1, 0)) - (tab_n > 0 ? 0 : blk_begin)];
+  // Q^T: lane holds head `col`, channels 32c + 8*g4 .. +7
+  bf16x8 qreg[D / 32];
+  {
+    const __bf16* qrow = static_cast<const __bf16*>(a.q) + ((int64_t)s * a.hq + head0 + (col < nh ? col : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) qreg[c] = *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g4);
+  }
+
+  // the grid and the block table bound what a malformed length can reach
+  const int ctx = min(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize));
+  const int nparts = (ctx + a.part_size - 1) / a.part_size;
+  // (a partition past the context leaves after the wait below: a branch
+  // here would let the compiler sink the loads above behind the length)
+
+  const int tok_end = min(ctx, tok_begin + a.part_size);
+  const int blk_end = (tok_end + 15) >> 4;
   const __bf16* kc = static_cast<const __bf16*>(a.k_cache);
   const __bf16* vc = static_cast<const __bf16*>(a.v_cache);
   const int64_t k_lane = (int64_t)col * D + 8 * g4;          // within a K block of one kv head
   const int64_t v_lane = (int64_t)col * kBlockSize + 4 * g4;  // within a V^T block of one kv head
-
-  // block-table entries of the partition (at most 64 blocks), one per lane
-  const int tab = (blk_begin + lane < blk_end) ? bt[blk_begin + lane] : 0;
+  // entries past the context: block 0 (the ring's prefetches past the end
+  // then all read one block)
+  const int tab = (blk_begin + lane < blk_end) ? tab_ld : 0;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c)
+    if (col >= nh) qreg[c] = bf16x8{};
 
   // Block pointers.  Blocks past the partition (prefetched, never consumed)
   // and table entries outside the pool read block 0, so every load is
@@ -162,15 +182,6 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, co
     vb = vc + base + v_lane;
   };
 
-  // Q^T: lane holds head `col`, channels 32c + 8*g4 .. +7
-  bf16x8 qreg[D / 32];
-  {
-    const __bf16* qrow = static_cast<const __bf16*>(a.q) + ((int64_t)s * a.hq + head0 + col) * D;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      qreg[c] = col < nh ? *reinterpret_cast<const bf16x8*>(qrow + 32 * c + 8 * g4) : bf16x8{};
-  }
-
   // fused RoPE: this lane's cos and sin for pair index `lane` (D/2 pairs)
   float rc = 1.f, rs = 0.f;
   if constexpr (FUSED) {
@@ -180,6 +191,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, co
   // the table and Q^T must be in registers before the block pipeline starts:
   // waiting here keeps the loop's waits to the blocks themselves
   __builtin_amdgcn_s_waitcnt(0);
+  if (p >= nparts) return;
 
   if constexpr (FUSED) {
     // rotate Q^T: the pair (channel i, i + D/2) sits in qreg[c][e] and
