@@ -95,8 +95,8 @@ template <int D>
 __device__ __forceinline__ int v_swz(int r) {    // V rows, read 4 rows x 64 B at a time by the transpose read
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
-__device__ __forceinline__ int vt_swz(int d) {   // V^T rows (paged, 64 keys = 8 chunks per row)
-  return (d >> 1) & 7;
+__device__ __forceinline__ int vt_swz(int d) {   // V^T rows (paged): the two 16-byte halves of a
+  return (d >> 3) & 1;                            // block's 32-byte row swap every 8 rows
 }
 
 // Tile geometry: HPW query heads share every K/V tile (same kv head under
@@ -235,11 +235,13 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   } else {
     // paged K rows: the RPI rows of one DMA lie in one block, so a DMA reads
     // from that block's (scalar) base plus this lane's byte offset within
-    // it, the same for every tile
+    // it, the same for every tile.  V^T: a DMA covers 32 channel rows of
+    // one block (lane = row pair x half), so one offset serves every DMA
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int r = (wave * LPW + i) * RPI + lane / CH;
       koff[i] = 2u * (uint32_t)((r & 15) * D + 8 * ((lane % CH) ^ k_swz<D>(r)));
+      voff[i] = 32u * (uint32_t)(lane >> 1) + 16u * (uint32_t)((lane & 1) ^ vt_swz(lane >> 1));
     }
   }
   // LDS byte address of the ring array (the one generic-to-LDS conversion);
@@ -278,15 +280,16 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   auto issue_v = [&](__bf16* dv, int t, const int32_t (&blk)[4]) {
     const int n0 = t * BN;
     if constexpr (PAGED) {
-      // V^T tile: row d holds the tile's 64 keys (8 chunks of 8 tokens),
-      // read straight from the token-minor value blocks
+      // V^T tile, block-major: the tile's four token-minor value blocks
+      // (D rows of 16 keys each) one after the other, as stored; DMA ii
+      // takes rows 32 (ii % (D / 32)) .. +31 of block ii / (D / 32)
+      constexpr int DPB = D / 32;
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
         const int ii = wave * LPW + i;
-        const int d = ii * 8 + lane / 8;
-        const int c = (lane % 8) ^ vt_swz(d);
-        const int32_t bk = pick4(blk, c >> 1);
-        dma16(vbase + (((int64_t)bk * a.hkv + g) * D + d) * kBlockSize + 8 * (c & 1), lds_of(dv) + ii * 1024);
+        const int32_t bk = pick4(blk, ii / DPB);
+        dma16s(vbase + ((int64_t)bk * a.hkv + g) * (D * kBlockSize) + (ii % DPB) * (32 * kBlockSize), voff[i],
+               lds_of(dv) + ii * 1024);
       }
     } else if (n0 + BN <= tk) {
       const __bf16* tb = vb0 + (int64_t)n0 * a.vs_t;
@@ -310,7 +313,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     const int nz = (t + 1) * BN - tk;
     for (int e = tid; e < D * nz; e += 64 * NW) {
       const int d = e / nz, kl = BN - nz + e % nz;
-      dv[d * BN + 8 * ((kl >> 3) ^ vt_swz(d)) + (kl & 7)] = __bf16{};
+      dv[(kl >> 4) * (D * kBlockSize) + d * kBlockSize + 8 * (((kl >> 3) & 1) ^ vt_swz(d)) + (kl & 7)] = __bf16{};
     }
   };
   auto tail_tile = [&](int t) { return PAGED && t == n_all - 1 && (t + 1) * BN > tk; };
@@ -342,8 +345,10 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   auto v_op = [&](const __bf16* sv, int dt, int kc) -> bf16x8 {
     if constexpr (PAGED) {
       const int d = dt * 32 + lq;
-      const u32x2 lo = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc) ^ vt_swz(d)) + 4 * hh);
-      const u32x2 hi = *reinterpret_cast<const u32x2*>(sv + d * BN + 8 * ((2 * kc + 1) ^ vt_swz(d)) + 4 * hh);
+      // key step kc is block kc of the tile: row d, keys 4hh.. and 8 + 4hh..
+      const __bf16* row = sv + kc * (D * kBlockSize) + d * kBlockSize;
+      const u32x2 lo = *reinterpret_cast<const u32x2*>(row + 8 * vt_swz(d) + 4 * hh);
+      const u32x2 hi = *reinterpret_cast<const u32x2*>(row + 8 * (1 ^ vt_swz(d)) + 4 * hh);
       return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
     } else {
       // transpose read: lane j of each 16-lane group addresses row (key)
