@@ -403,8 +403,8 @@ def emit(args, out, cpu):
                                      "Hq 12 / Hkv 2, D 128, bf16, block 16, fragmented pool, seed 1004",
                          "new_tokens": m["n_new"], "decode_context_tokens": m["dec_tokens"],
                          "pool_blocks": m["pool_blocks"], "decode_partition": m["part"],
-                         "schedule": "chunk tokens' RoPE write then chunked prefill (ATTN_PREFILL_SHARE_CU: "
-                                     "4-wavefront tile) on one stream, beside the decode tokens' RoPE write "
+                         "schedule": "chunk tokens' RoPE write then chunked prefill (ATTN_PREFILL_SHARE_CU: one "
+                                     "4-wavefront workgroup per CU) on one stream, beside the decode tokens' RoPE write "
                                      "then the decode on a second; stage figures run alone, default tiles",
                          "parallelism": "single GPU"}
         dec_s = m["ms_decode"] / 1e3

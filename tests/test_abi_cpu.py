@@ -319,7 +319,9 @@ def test_paged_prefill_and_write_reject(lib):
     assert paged_ex(2) == ATTN_E_INVALID
     assert paged_ex(-1) == ATTN_E_INVALID
     assert paged_ex(mi.ATTN_PREFILL_SHARE_CU, dtype=ATTN_F32) == ATTN_E_UNSUPPORTED
-    assert paged_ex(mi.ATTN_PREFILL_SHARE_CU, ws=P, wsb=need - 256) == ATTN_E_NOMEM
+    # (the flagged plan fits one workgroup per CU, so it splits into no more
+    # shares than the default: a workspace far below either is refused)
+    assert paged_ex(mi.ATTN_PREFILL_SHARE_CU, ws=P, wsb=256) == ATTN_E_NOMEM
     st = lib.attn_kv_cache_write_rope(P, P, P, P, P, P, P, 10, 12, 2, 128, 8, 100, 10000.0, ATTN_BF16, None)
     assert st == ATTN_E_UNSUPPORTED
     st = lib.attn_kv_cache_write_rope(P, None, P, P, P, P, P, 10, 12, 2, 128, 16, 100, 10000.0, ATTN_BF16, None)

@@ -95,10 +95,10 @@ def test_split_kv_chunked_prefill(ctx_hint, d):
 
 
 def test_share_cu_tile_bit_identical():
-    """ATTN_PREFILL_SHARE_CU picks the 4-wavefront tile where the default is
-    the 8-wavefront one (8 chunks of 512: 192 workgroups); every row is
-    computed in the same order, so the outputs match bit for bit, and both
-    match the oracle."""
+    """ATTN_PREFILL_SHARE_CU runs the 4-wavefront tile with a three-deep V
+    ring (one workgroup per CU) where the default has a two-deep one (two
+    per CU); every row is computed in the same order, so the outputs match
+    bit for bit, and both match the oracle."""
     cached, new = [0, 300, 1000, 17, 2048, 64, 500, 5], [512] * 8
     say("case: paged prefill, share-CU tile vs default, 8 x 512")
     qs, ks, vs, bt, kc, vc, total = paged_setup(95, cached, new)

@@ -72,35 +72,22 @@ RopeFreqs rope_freqs(float base, int32_t head_dim) {
 }
 
 // Tile shape of the bf16 prefill kernel: two query heads of one kv group per
-// workgroup (each K/V tile serves both) and 128-query tiles unless that
-// leaves most CUs idle.  The
-// environment variable MI_ATTN_PREFILL_TILE="hpw,wph" overrides the choice
-// (tuning only).
+// workgroup (each K/V tile serves both) and 64-query tiles, or one head and
+// 128 queries for odd groups: 4 wavefronts.  The environment variable
+// MI_ATTN_PREFILL_TILE="hpw,wph" overrides the choice (tuning only).
 struct PrefillTile {
   int hpw, wph;
 };
 
-PrefillTile prefill_tile(int64_t max_q, int32_t hq, int32_t group, int64_t batch, bool paged, bool share_cu) {
+PrefillTile prefill_tile(int32_t group) {
   const int hpw = (group % 2 == 0) ? 2 : 1;
-  // measured on MI355X.  Contiguous: 4-wavefront tiles (2 heads x 64 queries,
-  // or 1 x 128) hold 80 KiB of LDS, so two workgroups share a CU and their
-  // phases drift apart: one's matrix work overlaps the other's softmax; this
-  // beats the 8-wavefront tile at every size measured.  Paged: the 8-wavefront
-  // 2 x 128 tile (it halves the K/V gathers per query) down to ~128
-  // workgroups, then 64-query tiles to keep more CUs busy.
+  // measured on MI355X: 4-wavefront tiles hold 80 KiB of LDS, so two
+  // workgroups share a CU and their phases drift apart (one's matrix work
+  // overlaps the other's softmax).  Contiguous: faster than the 8-wavefront
+  // tile at every size measured.  Paged (8 chunks of 512 new tokens on
+  // 0-2048 cached): 69.7 us against 82.6 for the 8-wavefront tile, which
+  // halves the block gathers per query but fits one workgroup per CU.
   PrefillTile t{hpw, hpw == 2 ? 2 : 4};
-  auto wgs = [&](const PrefillTile& c) { return ((max_q + 32 * c.wph - 1) / (32 * c.wph)) * (hq / c.hpw) * batch; };
-  if (paged) {
-    t = PrefillTile{hpw, 4};
-    if (wgs(t) < 128) t.wph = 2;
-    // sharing the GPU with a decode: the 4-wavefront tile (275 VGPRs per
-    // lane) leaves room beside it for one decode workgroup (232), which the
-    // 8-wavefront tile (2 x 254 per SIMD) does not.  Measured on MI355X with
-    // 8 chunks of 512 new tokens beside a 128-sequence decode: 198.5 vs
-    // 204 us for both, while the chunks alone are slower with this tile
-    // (100 vs 85 us).
-    if (share_cu) t.wph = 2;
-  }
   static const char* env = std::getenv("MI_ATTN_PREFILL_TILE");
   if (env) {
     int h = 0, w = 0;
@@ -127,6 +114,7 @@ constexpr int kCUs = 256;           // MI355X compute units
 constexpr int kMinSplitTiles = 8;
 struct PrefillPlan {
   PrefillTile t;
+  bool deep_v = false;  // paged 4-wavefront tile with a three-deep V ring (one per CU)
   int32_t num_m_tiles = 0;
   int64_t num_wg = 0;
   int32_t num_splits = 1, split_tiles = 0;
@@ -139,11 +127,18 @@ struct PrefillPlan {
 PrefillPlan plan_prefill(int64_t max_q, int64_t max_k, int32_t hq, int32_t group, int64_t batch,
                          int32_t d, bool paged, int64_t rows, bool share_cu = false) {
   PrefillPlan p;
-  p.t = prefill_tile(max_q, hq, group, batch, paged, share_cu);
+  p.t = prefill_tile(group);
+  // sharing the GPU with a decode: the paged 4-wavefront tile with a
+  // three-deep V ring (96 KiB of LDS, 264 VGPRs) fits once per CU, which
+  // leaves room beside it for one decode workgroup (232 VGPRs); two of the
+  // two-deep tiles (80 KiB, 256 VGPRs each) fill a CU.  Measured on MI355X
+  // with 8 chunks of 512 new tokens beside a 128-sequence decode: 190-191
+  // vs 193-195 us per step, while alone the chunks take 82.6 vs 69.7 us.
+  p.deep_v = paged && share_cu && p.t.hpw * p.t.wph == 4;
   p.num_m_tiles = ceil_div(max_q, 32 * p.t.wph);
   p.num_wg = (int64_t)p.num_m_tiles * (hq / p.t.hpw) * batch;
-  // two 4-wavefront contiguous workgroups share a CU (80 KiB of LDS each)
-  const int64_t slots = (int64_t)kCUs * ((!paged && p.t.hpw * p.t.wph == 4) ? 2 : 1);
+  // two 4-wavefront workgroups share a CU (80 KiB of LDS each)
+  const int64_t slots = (int64_t)kCUs * ((p.t.hpw * p.t.wph == 4 && !p.deep_v) ? 2 : 1);
   const int64_t t_max = (max_k + 63) / 64;  // key tiles of the longest query tile
   int64_t split = 0;                        // forced share length (tuning only)
   static const char* env = std::getenv("MI_ATTN_PREFILL_SPLIT");
@@ -280,7 +275,7 @@ int prefill_common(const char* fn, const void* q, const void* k, const void* v, 
     a.num_m_tiles = p.num_m_tiles;
     if (p.num_wg * a.num_splits > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
     a.num_wg = (uint32_t)p.num_wg;
-    return launched(launch_prefill_bf16(a, head_dim, false, p.t.hpw, p.t.wph, s), fn);
+    return launched(launch_prefill_bf16(a, head_dim, false, p.t.hpw, p.t.wph, false, s), fn);
   }
   a.num_splits = 1;
   a.num_m_tiles = ceil_div(seqlen_q, kPrefillF32BlockM);
@@ -381,7 +376,8 @@ extern "C" int attn_prefill_paged_ex(const void* q, const void* k_cache, const v
   a.cu_seqlens_q = cu_seqlens_q; a.context_lens = context_lens;
   a.num_blocks = num_blocks;
   a.total_q = total_q;
-  return launched(launch_prefill_bf16(a, head_dim, true, p.t.hpw, p.t.wph, reinterpret_cast<hipStream_t>(stream)), fn);
+  return launched(launch_prefill_bf16(a, head_dim, true, p.t.hpw, p.t.wph, p.deep_v,
+                                      reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
 // ---------------------------------------------------------------------------

@@ -119,8 +119,10 @@ struct RmsNormArgs {
 
 // Launchers return the launch status (hipSuccess or the error).
 // hpw: query heads sharing each K/V tile (1 or 2); wph: wavefronts of 32
-// queries per head (4 or 2).  Query tile = 32 * wph rows.
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, hipStream_t s);
+// queries per head (4 or 2).  Query tile = 32 * wph rows.  deep_v (paged,
+// 4-wavefront tiles): a three-deep V ring, one workgroup per CU.
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, bool deep_v,
+                               hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStream_t s);
 hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hipStream_t s);

@@ -102,7 +102,7 @@ __device__ __forceinline__ int vt_swz(int d) {   // V^T rows (paged): the two 16
 // Tile geometry: HPW query heads share every K/V tile (same kv head under
 // GQA); each head has WPH wavefronts of 32 queries.  MASKED adds the caller's
 // additive mask M to every score (contiguous layout only).
-template <int D, bool PAGED, int HPW, int WPH, bool MASKED = false>
+template <int D, bool PAGED, int HPW, int WPH, bool MASKED = false, bool DEEP_V = false>
 __global__ __launch_bounds__(64 * HPW * WPH) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NW = HPW * WPH;
@@ -115,9 +115,11 @@ void prefill_bf16_kernel(const PrefillArgs a) {
 
   // LDS: a ring of three K tiles followed by a ring of three V tiles
   constexpr int TILE = BN * D;
-  // V ring depth: three tiles, or two for 4-wavefront contiguous workgroups,
-  // which keeps them at 80 KiB of LDS so that two fit on a CU
-  constexpr int NVB = (!PAGED && NW == 4) ? 2 : 3;
+  // V ring depth: three tiles, or two for 4-wavefront workgroups, which
+  // keeps them at 80 KiB of LDS so that two fit on a CU.  DEEP_V keeps three
+  // (96 KiB) for a paged launch that shares the GPU with a decode: one such
+  // workgroup per CU leaves the rest of the CU to a decode workgroup.
+  constexpr int NVB = (NW == 4 && !DEEP_V) ? 2 : 3;
   __shared__ __attribute__((aligned(1024))) __bf16 sm[(3 + NVB) * TILE];
 
   // split-KV share index fastest: all shares of the longest query tiles
@@ -543,7 +545,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // paged: block-table entries of the K tile and the V tile the next
   // iteration loads (the V tile of one iteration is the K tile of the one
   // before, and the K entries are fetched an iteration ahead)
-  int32_t blk_k[4], blk_v[4];
+  int32_t blk_k[4], blk_v[4], blk_v1[4];
   if (n_tiles > 0) {
     {
       int32_t b0[4], b1[4];
@@ -556,6 +558,8 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       issue_k(kring + TILE, T0 + min(1, n_tiles - 1), b1);
       if constexpr (NVB == 3) issue_v(vring + TILE, T0 + min(1, n_tiles - 1), b1);
       issue_k(kring + 2 * TILE, T0 + min(2, n_tiles - 1), blk_v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) blk_v1[i] = b1[i];
     }
     __builtin_amdgcn_s_waitcnt(0);   // also retires the Q loads
     __syncthreads();
@@ -585,12 +589,15 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
       issue_v(vring + r2 * TILE, T0 + min(j + 2, n_tiles - 1), blk_v);
     } else {
-      issue_v(vring + vnext * TILE, T0 + min(j + 1, n_tiles - 1), blk_v);
+      issue_v(vring + vnext * TILE, T0 + min(j + 1, n_tiles - 1), blk_v1);
       issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
     }
     if constexpr (PAGED) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) blk_v[i] = blk_k[i];
+      for (int i = 0; i < 4; ++i) {
+        blk_v1[i] = blk_v[i];  // tile j + 2 (the two-deep ring's next V)
+        blk_v[i] = blk_k[i];   // tile j + 3
+      }
       tile_blocks(T0 + min(j + 4, n_tiles - 1), blk_k);
     }
     phase_a(kring + r1 * TILE, sc, sn);
@@ -850,8 +857,17 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
 
 
 template <int D, bool PAGED, int HPW, int WPH>
-static void launch_one(const PrefillArgs& a, hipStream_t s) {
+static void launch_one(const PrefillArgs& a, bool deep_v, hipStream_t s) {
   dim3 grid(a.num_wg * (uint32_t)a.num_splits);
+  if constexpr (PAGED && HPW * WPH == 4) {
+    if (deep_v) {
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, true, HPW, WPH, false, true>), grid, dim3(64 * HPW * WPH), 0, s, a);
+      if (a.num_splits > 1)
+        hipLaunchKernelGGL((prefill_merge_kernel<D, PAGED, HPW, WPH>), dim3(a.num_wg * merge_parts<D, HPW, WPH>()),
+                           dim3(256), 0, s, a);
+      return;
+    }
+  }
   if constexpr (!PAGED && ((HPW == 2 && WPH == 2) || (HPW == 1 && WPH == 4))) {
     // the masked variant exists for the default contiguous tiles only (the
     // host picks one of them and never splits a masked launch)
@@ -867,20 +883,21 @@ static void launch_one(const PrefillArgs& a, hipStream_t s) {
 }
 
 template <int D, bool PAGED>
-static void launch_cfg(const PrefillArgs& a, int hpw, int wph, hipStream_t s) {
-  if (hpw == 2 && wph == 4) launch_one<D, PAGED, 2, 4>(a, s);
-  else if (hpw == 2 && wph == 2) launch_one<D, PAGED, 2, 2>(a, s);
-  else if (hpw == 1 && wph == 4) launch_one<D, PAGED, 1, 4>(a, s);
-  else launch_one<D, PAGED, 1, 2>(a, s);
+static void launch_cfg(const PrefillArgs& a, int hpw, int wph, bool deep_v, hipStream_t s) {
+  if (hpw == 2 && wph == 4) launch_one<D, PAGED, 2, 4>(a, deep_v, s);
+  else if (hpw == 2 && wph == 2) launch_one<D, PAGED, 2, 2>(a, deep_v, s);
+  else if (hpw == 1 && wph == 4) launch_one<D, PAGED, 1, 4>(a, deep_v, s);
+  else launch_one<D, PAGED, 1, 2>(a, deep_v, s);
 }
 
-hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, hipStream_t s) {
+hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, bool deep_v,
+                               hipStream_t s) {
   if (head_dim == 128) {
-    if (paged) launch_cfg<128, true>(a, hpw, wph, s);
-    else launch_cfg<128, false>(a, hpw, wph, s);
+    if (paged) launch_cfg<128, true>(a, hpw, wph, deep_v, s);
+    else launch_cfg<128, false>(a, hpw, wph, deep_v, s);
   } else {
-    if (paged) launch_cfg<64, true>(a, hpw, wph, s);
-    else launch_cfg<64, false>(a, hpw, wph, s);
+    if (paged) launch_cfg<64, true>(a, hpw, wph, deep_v, s);
+    else launch_cfg<64, false>(a, hpw, wph, deep_v, s);
   }
   return hipGetLastError();
 }
