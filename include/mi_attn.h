@@ -180,10 +180,11 @@ ATTN_API int attn_prefill_paged(const void* q, const void* k_cache, const void* 
  *   ATTN_PREFILL_SHARE_CU  the launch runs while another kernel (a paged
  *                decode on another stream, the usual case in a serving step
  *                that mixes chunked prefill and decode) is given the rest of
- *                the GPU.  The prefill then takes the 4-wavefront tile, whose
- *                registers leave room on every CU for one decode workgroup;
- *                the default 8-wavefront tile fills a CU's register file.
- *                Alone, the flagged launch is slower.
+ *                the GPU.  The prefill's workgroups then hold a deeper ring
+ *                of value tiles in LDS, so that one fits per CU and leaves
+ *                room beside it for a decode workgroup; by default two
+ *                prefill workgroups share a CU and fill it.  Alone, the
+ *                flagged launch is slower.
  *   Other bits: ATTN_E_INVALID.  The workspace size that
  *   attn_prefill_paged_workspace_size reports suffices for either tile. */
 #define ATTN_PREFILL_SHARE_CU 1
