@@ -76,15 +76,19 @@ __global__ __launch_bounds__(kThreads) void rope_write_kernel(const RopeWriteArg
   const int ntok = min(kTok, a.num_tokens - n0);
   const bool rot = a.rope != 0;
 
-  // round trip 1: slots and positions (the frequencies meanwhile)
+  // round trip 1: slots, positions and frequencies, all in flight at once
+  // (unconditional loads from clamped indexes: a load under a lane
+  // condition becomes a branch the compiler waits behind)
+  const int tt = min(tid, ntok - 1);
+  int32_t sl = a.slot_mapping[n0 + tt];
+  const int32_t ps = a.positions[n0 + tt];
+  const double th = a.freqs.theta[tid & (H2 - 1)];
   if (tid < kTok) {
-    int32_t sl = tid < ntok ? a.slot_mapping[n0 + tid] : -1;
-    if (sl >= a.num_blocks * kBlockSize) sl = -1;  // outside the pool: skipped
+    if (tid >= ntok || sl >= a.num_blocks * kBlockSize) sl = -1;  // outside the pool: skipped
     slot_sm[tid] = sl;
-    pos_sm[tid] = tid < ntok ? a.positions[n0 + tid] : 0;
+    pos_sm[tid] = tid < ntok ? ps : 0;
   }
-  if (rot)
-    for (int i = tid; i < H2; i += kThreads) theta[i] = a.freqs.theta[i];
+  if (rot && tid < H2) theta[tid] = th;
   __syncthreads();
 
   T* q = static_cast<T*>(a.q);
