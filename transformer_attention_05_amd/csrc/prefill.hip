@@ -34,7 +34,9 @@
 //     same rounded values, so the output weights stay exactly normalised.
 // The paged variant is the same loop with K/V rows gathered through the
 // block table (16-token blocks): token t of sequence s lives in block
-// block_table[s][t / 16] at offset t % 16.
+// block_table[s][t / 16] at offset t % 16.  Its V^T tile stays block-major
+// in LDS (the four token-minor value blocks as stored), so each V DMA and
+// each 16-key contraction step touches one block.
 //
 // f32 path: a plain VALU kernel (one query per one or two lanes), used for
 // full-precision parity runs.
