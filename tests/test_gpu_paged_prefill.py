@@ -109,6 +109,22 @@ def test_share_cu_tile_bit_identical():
     check(f64(o_sh), np.concatenate(refs), torch.bfloat16, "share-CU chunked")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_share_cu_split_kv(d):
+    """The flagged form through split-KV: few query tiles over long contexts
+    split into shares (fewer than the default's, one workgroup per CU) and
+    merge; the workspace sized for the default plan suffices.  Checked
+    against the oracle (share boundaries differ from the default's, so the
+    rounding may too)."""
+    cached, new = [3000, 100], [200, 50]
+    say(f"case: paged split-KV with the share-CU form, D {d}")
+    qs, ks, vs, bt, kc, vc, total = paged_setup(96, cached, new, d=d)
+    o, _ = run_paged(qs, bt, kc, vc, total, max_context_len=3200, share_cu=True)
+    refs = np.concatenate(oracle.chunked_prefill([to_f64(q) for q in qs], [to_f64(k) for k in ks],
+                                                 [to_f64(v) for v in vs]))
+    check(f64(o), refs, torch.bfloat16, "share-CU split-KV chunked")
+
+
 def test_noncausal_paged():
     qs, ks, vs, bt, kc, vc, total = paged_setup(81, [40, 0], [30, 70])
     o, _ = run_paged(qs, bt, kc, vc, total, causal=False)
