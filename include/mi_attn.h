@@ -199,6 +199,33 @@ ATTN_API int attn_prefill_paged_ex(const void* q, const void* k_cache, const voi
                           void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
 /* -------------------------------------------------------------------------
+ * attn_prefill_paged_masked -- attn_prefill_paged with a general additive
+ * mask M (the attention equation of §FlashAttention-Style Kernels).
+ *
+ * Element (packed query row r, query head h, key position j) of M is
+ * mask[r*mask_strides[0] + h*mask_strides[1] + j], fp32, keys contiguous, for
+ * j < mask_keys; j counts the logical positions of the row's sequence
+ * (0 .. context_lens[s]-1, cached tokens first).  A stride of 0 broadcasts
+ * (one row for every head, say).  Entries are finite or -infinity; keys at
+ * or past mask_keys are never read and count as masked (-infinity), so
+ * mask_keys should be at least the longest context.  `causal` applies on
+ * top.  A row whose every key is masked yields O = 0.  Single pass (no
+ * workspace, no flags).
+ *
+ *   mask         device fp32, 16-byte aligned; strides >= 0 and multiples of
+ *                4 elements
+ *   every other argument as for attn_prefill_paged.
+ * ---------------------------------------------------------------------- */
+ATTN_API int attn_prefill_paged_masked(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, int32_t max_blocks_per_seq,
+                              const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                              const float* mask, const int64_t mask_strides[2], int32_t mask_keys,
+                              void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                              int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                              int32_t causal, attn_dtype dtype, attn_stream_t stream);
+
+/* -------------------------------------------------------------------------
  * attn_decode_paged -- one query token per sequence over its paged cache.
  *
  * §FlashAttention-Style Kernels: decode has one new query per request and is
@@ -253,9 +280,9 @@ ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v
  * attn_decode_paged_rope -- the decode above, with each sequence's new token
  * rotated and written into the cache by the same launch.
  *
- * §Operator Fusion names "applying rotary position embeddings to queries and
- * keys" and "updating the KV cache while transforming key and value tensors"
- * as fusions; here they are fused into the decode itself.  Equivalent to
+ * §Operator Fusion lists the rotary embedding of queries and keys and the
+ * KV-cache update done while keys and values are transformed among the usual
+ * fusions; here both are folded into the decode itself.  Equivalent to
  * attn_kv_cache_write_rope(q, k_new, v_new, positions, slot_mapping, ...)
  * (one token per sequence) followed by attn_decode_paged on the rotated q,
  * with the same rotation arithmetic bit for bit, except that q is not
@@ -308,8 +335,9 @@ ATTN_API int32_t attn_decode_paged_auto_partition(int32_t num_seqs, int32_t num_
  * applying rotary position embeddings to queries and keys, and updating the
  * KV cache while transforming keys and values.  For token n with position
  * positions[n]: each pair (x[i], x[i + D/2]), i < D/2, of every query and key
- * head is rotated by angle positions[n] * rope_base^(-2i/D) (angle and its
- * sine and cosine in double precision); the rotated key and the unchanged
+ * head is rotated by angle positions[n] * rope_base^(-2i/D) (the angle is
+ * formed and reduced modulo 2 pi in double precision, its sine and cosine
+ * then taken in single precision); the rotated key and the unchanged
  * value are stored in slot slot_mapping[n] (block slot / 16, offset slot % 16);
  * slot -1 skips the cache write for that token.  Rotated queries overwrite q.
  *
@@ -329,8 +357,8 @@ ATTN_API int attn_kv_cache_write_rope(void* q, const void* k, const void* v, con
 /* -------------------------------------------------------------------------
  * attn_residual_rms_norm -- fused residual add + RMS normalisation.
  *
- * §Operator Fusion names "adding a residual connection and applying RMSNorm"
- * as a fusion and gives its definition: h = x + residual (stored in the
+ * §Operator Fusion counts the residual add followed by RMSNorm among the
+ * common fusions and gives a definition of it: h = x + residual (stored in the
  * input dtype: the updated residual), y = h / sqrt(mean(h^2) + eps) * weight
  * row by row (mean over the hidden dimension); both y and h are returned.
  * One pass: x, residual and weight read once, y and h written once.

@@ -38,6 +38,26 @@ def test_header_declares_entry_points():
         assert name in syms
 
 
+def declared_arg_counts():
+    """{name: number of parameters} from the header's prototypes."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"ATTN_API\s+[\w\s\*]*?\b(attn_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else len(params.split(","))
+    return out
+
+
+def test_binding_signatures_match_header():
+    """Every ctypes prototype of the binding has as many arguments as the
+    header's declaration, and every declared symbol has a prototype."""
+    counts = declared_arg_counts()
+    assert set(counts) == set(declared_symbols())
+    for name, n in counts.items():
+        assert name in mi._SIGNATURES, f"{name} has no ctypes prototype"
+        assert len(mi._SIGNATURES[name][1]) == n, (name, len(mi._SIGNATURES[name][1]), n)
+
+
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_symbols():
         assert hasattr(lib, name), name
@@ -330,6 +350,101 @@ def test_paged_prefill_and_write_reject(lib):
     assert st == ATTN_E_INVALID
     st = lib.attn_kv_cache_write_rope(None, P, P, P, P, P, P, 0, 12, 2, 128, 16, 100, 10000.0, ATTN_BF16, None)
     assert st == 0  # nothing to do
+
+
+def test_paged_masked_rejects(lib):
+    ms = (ctypes.c_int64 * 2)(12 * 304, 304)
+
+    def pm(**kw):
+        a = dict(mask=P, ms=ms, mk=300, dtype=ATTN_BF16, d=128, bs=16)
+        a.update(kw)
+        return lib.attn_prefill_paged_masked(P, P, P, P, 20, P, P, a["mask"], a["ms"], a["mk"], P, 2, 250, 200,
+                                             300, 12, 2, a["d"], a["bs"], 100, 0.0, 1, a["dtype"], None)
+    assert pm(mask=None) == ATTN_E_INVALID
+    assert pm(ms=None) == ATTN_E_INVALID
+    assert pm(mask=P + 4) == ATTN_E_INVALID                                   # not 16-byte aligned
+    assert pm(ms=(ctypes.c_int64 * 2)(12 * 302, 302)) == ATTN_E_INVALID      # stride not a multiple of 4
+    assert pm(ms=(ctypes.c_int64 * 2)(-4, 0)) == ATTN_E_INVALID
+    assert pm(mk=-1) == ATTN_E_INVALID
+    assert pm(d=96) == ATTN_E_UNSUPPORTED
+    assert pm(bs=8) == ATTN_E_UNSUPPORTED
+    assert pm(dtype=7) == ATTN_E_UNSUPPORTED
+
+
+def test_bindings_validate_tensors():
+    """The binding refuses malformed tensors before taking any pointer: wrong
+    integer dtypes, non-contiguous or wrongly shaped caches and queries."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(3, 12, 128, dtype=bf)
+    kc = torch.zeros(10, 2, 16, 128, dtype=bf)
+    vc = torch.zeros(10, 2, 128, 16, dtype=bf)
+    bt = torch.zeros(3, 4, dtype=torch.int32)
+    cl = torch.full((3,), 20, dtype=torch.int32)
+    cu = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    dec = lambda **kw: mi.attn_decode_paged(**{**dict(q=q, k_cache=kc, v_cache=vc, block_table=bt,
+                                                      context_lens=cl, max_context_len=64), **kw})
+    with pytest.raises(ValueError, match="block_table must be int32"):
+        dec(block_table=bt.long())
+    with pytest.raises(ValueError, match="context_lens must be int32"):
+        dec(context_lens=cl.long())
+    with pytest.raises(ValueError, match="context_lens must have shape"):
+        dec(context_lens=cl[:2])
+    with pytest.raises(ValueError, match="v_cache"):
+        dec(v_cache=torch.zeros(10, 2, 16, 128, dtype=bf))           # token-major values
+    with pytest.raises(ValueError, match="v_cache"):
+        dec(v_cache=vc.transpose(2, 3).contiguous().transpose(2, 3))  # right shape, not contiguous
+    with pytest.raises(ValueError, match="k_cache"):
+        dec(k_cache=kc.float())
+    with pytest.raises(ValueError, match="q must"):
+        dec(q=torch.zeros(3, 128, 12, dtype=bf).transpose(1, 2))
+    with pytest.raises(ValueError, match="block_table has"):
+        dec(block_table=bt[:2], context_lens=cl[:2])
+    with pytest.raises(ValueError, match="plan must be int32"):
+        dec(plan=torch.zeros(4, 2, dtype=torch.int64))
+    with pytest.raises(ValueError, match="o must"):
+        dec(o=torch.zeros(3, 12, 64, dtype=bf))
+    pf = lambda **kw: mi.attn_prefill_paged(**{**dict(q=q, k_cache=kc, v_cache=vc, block_table=bt,
+                                                      cu_seqlens_q=cu, context_lens=cl, max_seqlen_q=1), **kw})
+    with pytest.raises(ValueError, match="cu_seqlens_q must be int32"):
+        pf(cu_seqlens_q=cu.long())
+    with pytest.raises(ValueError, match="cu_seqlens_q must have shape"):
+        pf(cu_seqlens_q=cu[:3])
+    mask = torch.zeros(3, 12, 64)
+    with pytest.raises(ValueError, match="mask must be float32"):
+        mi.attn_prefill_paged_masked(q, kc, vc, bt, cu, cl, 1, mask.double())
+    with pytest.raises(ValueError, match="mask must be"):
+        mi.attn_prefill_paged_masked(q, kc, vc, bt, cu, cl, 1, torch.zeros(2, 64))
+    rw = lambda **kw: mi.attn_kv_cache_write_rope(**{**dict(q=q, k=torch.zeros(3, 2, 128, dtype=bf),
+                                                            v=torch.zeros(3, 2, 128, dtype=bf),
+                                                            positions=cl, slot_mapping=cl, k_cache=kc,
+                                                            v_cache=vc), **kw})
+    with pytest.raises(ValueError, match="slot_mapping must be int32"):
+        rw(slot_mapping=cl.long())
+    with pytest.raises(ValueError, match="positions must have shape"):
+        rw(positions=cl[:1])
+    with pytest.raises(ValueError, match="v must"):
+        rw(v=torch.zeros(3, 2, 128, dtype=torch.float32))
+    with pytest.raises(ValueError, match="v_cache"):
+        rw(v_cache=torch.zeros(10, 2, 16, 128, dtype=bf))
+    dr = lambda **kw: mi.attn_decode_paged_rope(**{**dict(q=q, k_new=torch.zeros(3, 2, 128, dtype=bf),
+                                                          v_new=torch.zeros(3, 2, 128, dtype=bf), positions=cl,
+                                                          slot_mapping=cl, k_cache=kc, v_cache=vc, block_table=bt,
+                                                          context_lens=cl, max_context_len=64), **kw})
+    with pytest.raises(ValueError, match="slot_mapping must be int32"):
+        dr(slot_mapping=cl.long())
+    with pytest.raises(ValueError, match="k_new must have shape"):
+        dr(k_new=torch.zeros(3, 12, 128, dtype=bf))
+    with pytest.raises(ValueError, match="pairs must be int32"):
+        mi.attn_copy_blocks(kc, vc, torch.zeros(2, 2, dtype=torch.int64))
+    x = torch.zeros(4, 64, dtype=bf)
+    with pytest.raises(ValueError, match="residual"):
+        mi.attn_residual_rms_norm(x, torch.zeros(4, 64, dtype=torch.float32), torch.zeros(64, dtype=bf))
+    k4 = torch.zeros(1, 64, 1, 64)
+    with pytest.raises(ValueError, match="lse must have shape"):
+        mi.attn_prefill(k4, k4, k4, lse=torch.zeros(1, 1, 63))
+    with pytest.raises(ValueError, match="share one dtype"):
+        mi.attn_prefill(k4, k4.to(bf), k4)
 
 
 def test_wrappers_refuse_cpu_tensors():

@@ -205,14 +205,19 @@ def test_concurrent_step_equals_serial(fused):
 def test_graph_replay_equals_eager(fused):
     """The step captured in a HIP graph and replayed three times, with eager
     work (restoring the unrotated queries) and synchronisations between the
-    replays, gives the eager step's outputs, rotated queries and caches bit
-    for bit every time."""
+    replays: every replay matches the oracle (outputs at the bf16 bar, rotated
+    queries within the storage bound) and gives the eager step's outputs,
+    rotated queries and caches bit for bit."""
     say(f"case: graph-captured step, fused decode write {fused}")
     case = mixed_case(79, num_req=3, chunk=150, cached_max=700, num_dec=17, dec_lo=1, dec_hi=6000)
+    pre, dec, q_rot = mixed_reference(case)
+    q_exact = oracle.rope(to_f64(case.q_new), case.positions, case.rope_base)
     st = MixedStep(case, assign_blocks, DEV, scatter=scatter_to_pool, fuse_decode_write=fused)
     q0 = st.q.clone()
     st.run()
     torch.cuda.synchronize()
+    check(f64(st.o_prefill), pre, torch.bfloat16, "eager prefill")
+    check(f64(st.o_decode), dec, torch.bfloat16, "eager decode")
     names = ("o_prefill", "o_decode", "k_cache", "v_cache")
     eager = {n: getattr(st, n).clone() for n in names}
     eager["rotated_q"] = st.rotated_q().clone()
@@ -224,6 +229,9 @@ def test_graph_replay_equals_eager(fused):
         torch.cuda.synchronize()
         st.replay()
         torch.cuda.synchronize()
+        check(f64(st.o_prefill), pre, torch.bfloat16, f"replay {rep} prefill")
+        check(f64(st.o_decode), dec, torch.bfloat16, f"replay {rep} decode")
+        check_stored(f64(st.rotated_q()), q_exact, torch.bfloat16, f"replay {rep} rotated q")
         for n in names:
             assert torch.equal(getattr(st, n).view(torch.int16), eager[n].view(torch.int16)), (rep, n)
         assert torch.equal(st.rotated_q().view(torch.int16), eager["rotated_q"].view(torch.int16)), rep

@@ -30,6 +30,7 @@ __all__ = [
     "attn_prefill_masked",
     "attn_residual_rms_norm",
     "attn_prefill_paged",
+    "attn_prefill_paged_masked",
     "attn_prefill_paged_workspace_size",
     "attn_prefill_workspace_size",
     "lib_path",
@@ -65,6 +66,9 @@ _SIGNATURES = {
     "attn_prefill_paged_ex": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32,
                                              _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
                                              _c_i32, ctypes.c_int, _c_i32, _vp, ctypes.c_size_t, _vp]),
+    "attn_prefill_paged_masked": (ctypes.c_int, [_vp, _vp, _vp, _vp, _c_i32, _vp, _vp, _vp, _c_i64p, _c_i32, _vp,
+                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                 _c_i32, ctypes.c_float, _c_i32, ctypes.c_int, _vp]),
     "attn_decode_paged_workspace_size": (ctypes.c_size_t, [_c_i32] * 6),
     "attn_decode_paged_auto_partition": (_c_i32, [_c_i32] * 3),
     "attn_decode_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
@@ -151,6 +155,63 @@ def _stream(t: torch.Tensor):
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+# --- argument checks.  They run before any pointer is taken, so a malformed
+# call raises ValueError/TypeError here (CPU tensors included) instead of
+# reaching the kernels: an int64 block table or a token-major value cache
+# would otherwise be read with the wrong layout.
+
+def _tensor(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    return t
+
+
+def _int32(t, name, shape=None):
+    """A contiguous int32 tensor, optionally of an exact shape."""
+    _tensor(t, name)
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32 (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _like(t, name, shape, dtype):
+    """A contiguous tensor of an exact shape and dtype."""
+    _tensor(t, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} like q (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _caches(k_cache, v_cache, dtype, head_dim, num_kv_heads=None):
+    """k_cache [nb, hkv, 16, D] and v_cache [nb, hkv, D, 16] (value blocks
+    token-minor), contiguous, in the queries' dtype.  Returns (nb, hkv, bs)."""
+    _tensor(k_cache, "k_cache")
+    _tensor(v_cache, "v_cache")
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
+    nb, hkv, bs, d = k_cache.shape
+    if d != head_dim or (num_kv_heads is not None and hkv != num_kv_heads):
+        raise ValueError(f"k_cache shape {tuple(k_cache.shape)} does not match the queries' heads / head_dim")
+    _like(k_cache, "k_cache", (nb, hkv, bs, d), dtype)
+    _like(v_cache, "v_cache [num_blocks, num_kv_heads, head_dim, block_size]", (nb, hkv, d, bs), dtype)
+    return nb, hkv, bs
+
+
+def _workspace_bytes(ws, name="workspace"):
+    _tensor(ws, name)
+    if not ws.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ws.numel() * ws.element_size()
+
+
 def _i64x3(vals):
     return (ctypes.c_int64 * 3)(*[int(x) for x in vals])
 
@@ -172,7 +233,30 @@ def _workspace(ws, need, device):
         return None, 0
     if ws is None:
         ws = torch.empty(need, dtype=torch.uint8, device=device)
-    return _dev(ws, "workspace"), ws.numel() * ws.element_size()
+    nbytes = _workspace_bytes(ws)
+    return _dev(ws, "workspace"), nbytes
+
+
+def _check_bthd(q, k, v, o, lse):
+    """q [B, Tq, Hq, D]; k, v [B, Tk, Hkv, D] (any strides, D contiguous);
+    o like q; lse float32 [B, Hq, Tq] contiguous."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _tensor(t, name)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [batch, tokens, heads, head_dim]")
+    b, tq, hq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != b or k.shape[3] != d:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} must be [batch, seqlen_k, num_kv_heads, head_dim]"
+                         f" matching q {tuple(q.shape)}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share one dtype")
+    if o is not None:
+        _tensor(o, "o")
+        if o.shape != q.shape or o.dtype != q.dtype:
+            raise ValueError("o must have q's shape and dtype")
+    if lse is not None:
+        _like(lse, "lse", (b, hq, tq), torch.float32)
+    return b, tq, hq, d, k.shape[1], k.shape[2]
 
 
 def attn_prefill_workspace_size(batch, seqlen_q, seqlen_k, num_q_heads, num_kv_heads, head_dim,
@@ -188,10 +272,9 @@ def attn_prefill(q, k, v, o=None, lse=None, causal=True, scale=0.0, workspace=No
     ``workspace``: a uint8 GPU tensor of at least
     attn_prefill_workspace_size(...) bytes, None to allocate one here, or
     False to run without split-KV."""
+    b, tq, hq, d, tk, hkv = _check_bthd(q, k, v, o, lse)
     if o is None:
         o = torch.empty_like(q)
-    b, tq, hq, d = q.shape
-    _, tk, hkv, _ = k.shape
     need = attn_prefill_workspace_size(b, tq, tk, hq, hkv, d, q.dtype)
     ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
     st = load().attn_prefill(
@@ -207,10 +290,10 @@ def attn_prefill_masked(q, k, v, mask, o=None, lse=None, causal=False, scale=0.0
     """Contiguous attention with an additive fp32 mask: ``mask`` is a GPU
     float32 tensor broadcastable to [B, Hq, Tq, Tk] (a [Tq, Tk] mask serves
     every batch and head) with contiguous keys; `causal` applies on top."""
+    b, tq, hq, d, tk, hkv = _check_bthd(q, k, v, o, lse)
     if o is None:
         o = torch.empty_like(q)
-    b, tq, hq, d = q.shape
-    _, tk, hkv, _ = k.shape
+    _tensor(mask, "mask")
     if mask.dtype != torch.float32:
         raise ValueError("mask must be float32")
     m = mask
@@ -243,11 +326,10 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, context_l
     the launch runs beside a decode on another stream (attn_prefill_paged_ex
     with ATTN_PREFILL_SHARE_CU; same results, a tile that leaves the decode
     room on every CU)."""
+    total_q, hq, d, nb, hkv, bs, s = _check_paged(q, o, k_cache, v_cache, block_table, context_lens)
+    _int32(cu_seqlens_q, "cu_seqlens_q", (s + 1,))
     if o is None:
         o = torch.empty_like(q)
-    total_q, hq, d = q.shape
-    nb, hkv, bs, _ = k_cache.shape
-    s = context_lens.shape[0]
     bound = int(max_context_len) if max_context_len else block_table.shape[1] * bs
     need = attn_prefill_paged_workspace_size(s, total_q, int(max_seqlen_q), bound, hq, hkv, d)
     ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
@@ -259,6 +341,55 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, context_l
         st = load().attn_prefill_paged_ex(*args, ATTN_PREFILL_SHARE_CU, ws_ptr, ws_bytes, _stream(q))
     else:
         st = load().attn_prefill_paged(*args, ws_ptr, ws_bytes, _stream(q))
+    _check(st)
+    return o
+
+
+def _check_paged(q, o, k_cache, v_cache, block_table, context_lens):
+    """Queries [rows, Hq, D] contiguous, o like q, the two caches, an int32
+    block table [S, max_blocks] and int32 context lengths [S]."""
+    _tensor(q, "q")
+    if q.dim() != 3:
+        raise ValueError("q must be [rows, num_q_heads, head_dim]")
+    rows, hq, d = q.shape
+    _like(q, "q", (rows, hq, d), q.dtype)
+    if o is not None:
+        _like(o, "o", (rows, hq, d), q.dtype)
+    nb, hkv, bs = _caches(k_cache, v_cache, q.dtype, d)
+    _int32(block_table, "block_table")
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [num_seqs, max_blocks_per_seq]")
+    s = block_table.shape[0]
+    _int32(context_lens, "context_lens", (s,))
+    return rows, hq, d, nb, hkv, bs, s
+
+
+def attn_prefill_paged_masked(q, k_cache, v_cache, block_table, cu_seqlens_q, context_lens, max_seqlen_q, mask,
+                              o=None, causal=True, scale=0.0, max_context_len=0):
+    """attn_prefill_paged with an additive fp32 mask: ``mask`` is a GPU
+    float32 tensor [total_q, Hq, K] or [total_q, K] (one row for every head;
+    it broadcasts over heads) whose row for packed query r holds one entry
+    per key position of r's sequence, K >= the longest context.  Keys
+    contiguous; row and head strides multiples of 4 elements."""
+    total_q, hq, d, nb, hkv, bs, s = _check_paged(q, o, k_cache, v_cache, block_table, context_lens)
+    _int32(cu_seqlens_q, "cu_seqlens_q", (s + 1,))
+    _tensor(mask, "mask")
+    if mask.dtype != torch.float32:
+        raise ValueError("mask must be float32")
+    m = mask if mask.dim() == 3 else mask.unsqueeze(1)
+    if m.dim() != 3 or m.shape[0] != total_q:
+        raise ValueError("mask must be [total_q, num_q_heads, keys] or [total_q, keys]")
+    m = m.expand(total_q, hq, m.shape[2])
+    if m.stride(2) != 1:
+        raise ValueError("mask: keys must be contiguous")
+    if o is None:
+        o = torch.empty_like(q)
+    st = load().attn_prefill_paged_masked(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        block_table.shape[1], _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(context_lens, "context_lens"),
+        _dev(m, "mask"), (ctypes.c_int64 * 2)(int(m.stride(0)), int(m.stride(1))), int(m.shape[2]),
+        _dev(o, "o"), s, total_q, int(max_seqlen_q), int(max_context_len), hq, hkv, d, bs, nb,
+        float(scale), 1 if causal else 0, _dtype_code(q), _stream(q))
     _check(st)
     return o
 
@@ -300,15 +431,20 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
     zeroed, if None.
     ``plan``: optional int32 GPU tensor [n, 2] from attn_decode_paged_plan
     (same lengths and arguments)."""
+    s, hq, d, nb, hkv, bs, s_bt = _check_paged(q, o, k_cache, v_cache, block_table, context_lens)
+    if s_bt != s:
+        raise ValueError(f"block_table has {s_bt} rows for {s} queries")
+    if plan is not None:
+        _int32(plan, "plan")
+        if plan.dim() != 2 or plan.shape[1] != 2:
+            raise ValueError("plan must be [n, 2] (sequence, partition)")
     if o is None:
         o = torch.empty_like(q)
-    s, hq, d = q.shape
-    nb, hkv, bs, _ = k_cache.shape
     need = attn_decode_paged_workspace_size(s, hq, hkv, d, int(max_context_len), int(partition_size))
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = _workspace_bytes(workspace) if workspace is not None else 0
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().attn_decode_paged(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
         _dev(context_lens, "context_lens"), _dev(o, "o"), s, hq, hkv, d, bs, nb, block_table.shape[1],
@@ -327,15 +463,26 @@ def attn_decode_paged_rope(q, k_new, v_new, positions, slot_mapping, k_cache, v_
     k_new / v_new [S, Hkv, D], positions / slot_mapping [S] int32.  The
     rotated queries go to ``q_rot_out`` when given.  ``workspace`` and
     ``plan`` as for attn_decode_paged."""
+    s, hq, d, nb, hkv, bs, s_bt = _check_paged(q, o, k_cache, v_cache, block_table, context_lens)
+    if s_bt != s:
+        raise ValueError(f"block_table has {s_bt} rows for {s} queries")
+    _like(k_new, "k_new", (s, hkv, d), q.dtype)
+    _like(v_new, "v_new", (s, hkv, d), q.dtype)
+    _int32(positions, "positions", (s,))
+    _int32(slot_mapping, "slot_mapping", (s,))
+    if q_rot_out is not None:
+        _like(q_rot_out, "q_rot_out", (s, hq, d), q.dtype)
+    if plan is not None:
+        _int32(plan, "plan")
+        if plan.dim() != 2 or plan.shape[1] != 2:
+            raise ValueError("plan must be [n, 2] (sequence, partition)")
     if o is None:
         o = torch.empty_like(q)
-    s, hq, d = q.shape
-    nb, hkv, bs, _ = k_cache.shape
     need = attn_decode_paged_workspace_size(s, hq, hkv, d, int(max_context_len), int(partition_size))
     if workspace is None and need > 0:
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = _workspace_bytes(workspace) if workspace is not None else 0
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().attn_decode_paged_rope(
         _dev(q_rot_out, "q_rot_out") if q_rot_out is not None else None, _dev(q, "q"), _dev(k_new, "k_new"),
         _dev(v_new, "v_new"), _dev(positions, "positions"), _dev(slot_mapping, "slot_mapping"), float(rope_base),
@@ -352,13 +499,21 @@ def attn_residual_rms_norm(x, residual, weight, eps=1e-6, y=None, residual_out=N
     """Fused residual add + RMSNorm over the last dimension of [rows, hidden]
     tensors: returns (y, h) with h = x + residual (written to residual_out,
     which may be residual itself) and y = h / rms(h) * weight."""
+    _tensor(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x must be [rows, hidden]")
+    for name, t in (("residual", residual), ("weight", weight)):
+        _tensor(t, name)
+        if t.dtype != x.dtype:
+            raise ValueError(f"{name} must have x's dtype")
     if y is None:
         y = torch.empty_like(x)
     if residual_out is None:
         residual_out = torch.empty_like(x)
     rows, hidden = x.shape
     for name, t in (("residual", residual), ("y", y), ("residual_out", residual_out)):
-        if t.shape != x.shape or not t.is_contiguous():
+        _tensor(t, name)
+        if t.shape != x.shape or not t.is_contiguous() or t.dtype != x.dtype:
             raise ValueError(f"{name} must be a contiguous [rows, hidden] tensor like x")
     if not x.is_contiguous() or weight.shape != (hidden,) or not weight.is_contiguous():
         raise ValueError("x must be contiguous and weight a contiguous [hidden] tensor")
@@ -371,17 +526,35 @@ def attn_residual_rms_norm(x, residual, weight, eps=1e-6, y=None, residual_out=N
 def attn_copy_blocks(k_cache, v_cache, pairs):
     """Copy whole blocks of both caches: ``pairs`` is an int32 GPU tensor
     [n, 2] of (src, dst) block ids."""
+    _tensor(k_cache, "k_cache")
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [num_blocks, num_kv_heads, block_size, head_dim]")
     nb, hkv, bs, d = k_cache.shape
+    _caches(k_cache, v_cache, k_cache.dtype, d)
+    _int32(pairs, "pairs")
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [n, 2] (src, dst)")
     _check(load().attn_copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(pairs, "pairs"),
                                    int(pairs.shape[0]), hkv, d, bs, nb, _dtype_code(k_cache), _stream(k_cache)))
 
 
 def attn_kv_cache_write_rope(q, k, v, positions, slot_mapping, k_cache, v_cache, rope_base=10000.0):
     """Rotate q (in place, may be None) and k; write rotated k and v into their slots."""
+    _tensor(k, "k")
+    if k.dim() != 3:
+        raise ValueError("k must be [num_tokens, num_kv_heads, head_dim]")
     n, hkv, d = k.shape
+    _like(k, "k", (n, hkv, d), k.dtype)
+    _like(v, "v", (n, hkv, d), k.dtype)
+    if q is not None:
+        _tensor(q, "q")
+        if q.dim() != 3 or q.shape[0] != n or q.shape[2] != d:
+            raise ValueError("q must be [num_tokens, num_q_heads, head_dim] like k")
+        _like(q, "q", tuple(q.shape), k.dtype)
     hq = q.shape[1] if q is not None else hkv
-    nb = k_cache.shape[0]
-    bs = k_cache.shape[2]
+    nb, _, bs = _caches(k_cache, v_cache, k.dtype, d, hkv)
+    _int32(positions, "positions", (n,))
+    _int32(slot_mapping, "slot_mapping", (n,))
     st = load().attn_kv_cache_write_rope(
         _dev(q, "q") if q is not None else None, _dev(k, "k"), _dev(v, "v"), _dev(positions, "positions"),
         _dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),

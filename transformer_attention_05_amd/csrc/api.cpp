@@ -73,8 +73,7 @@ RopeFreqs rope_freqs(float base, int32_t head_dim) {
 
 // Tile shape of the bf16 prefill kernel: two query heads of one kv group per
 // workgroup (each K/V tile serves both) and 64-query tiles, or one head and
-// 128 queries for odd groups: 4 wavefronts.  The environment variable
-// MI_ATTN_PREFILL_TILE="hpw,wph" overrides the choice (tuning only).
+// 128 queries for odd groups: 4 wavefronts.
 struct PrefillTile {
   int hpw, wph;
 };
@@ -87,14 +86,7 @@ PrefillTile prefill_tile(int32_t group) {
   // tile at every size measured.  Paged (8 chunks of 512 new tokens on
   // 0-2048 cached): 69.7 us against 82.6 for the 8-wavefront tile, which
   // halves the block gathers per query but fits one workgroup per CU.
-  PrefillTile t{hpw, hpw == 2 ? 2 : 4};
-  static const char* env = std::getenv("MI_ATTN_PREFILL_TILE");
-  if (env) {
-    int h = 0, w = 0;
-    if (std::sscanf(env, "%d,%d", &h, &w) == 2 && (h == 1 || (h == 2 && group % 2 == 0)) && (w == 4 || w == 2))
-      t = PrefillTile{h, w};
-  }
-  return t;
+  return PrefillTile{hpw, hpw == 2 ? 2 : 4};
 }
 
 // Split-KV plan of the bf16 prefill.  A launch with too few query tiles to
@@ -140,15 +132,8 @@ PrefillPlan plan_prefill(int64_t max_q, int64_t max_k, int32_t hq, int32_t group
   // two 4-wavefront workgroups share a CU (80 KiB of LDS each)
   const int64_t slots = (int64_t)kCUs * ((p.t.hpw * p.t.wph == 4 && !p.deep_v) ? 2 : 1);
   const int64_t t_max = (max_k + 63) / 64;  // key tiles of the longest query tile
-  int64_t split = 0;                        // forced share length (tuning only)
-  static const char* env = std::getenv("MI_ATTN_PREFILL_SPLIT");
-  if (env) split = std::atoll(env);
   int64_t L = 0;
-  if (env && split <= 0) {
-    L = 0;
-  } else if (split > 0) {
-    L = split;
-  } else if (2 * p.num_wg <= slots && t_max >= 2 * kMinSplitTiles) {
+  if (2 * p.num_wg <= slots && t_max >= 2 * kMinSplitTiles) {
     const int64_t s = std::min((slots + p.num_wg - 1) / p.num_wg, (t_max + kMinSplitTiles - 1) / kMinSplitTiles);
     if (s > 1) L = (t_max + s - 1) / s;
   }
@@ -327,16 +312,22 @@ extern "C" int attn_prefill_paged(const void* q, const void* k_cache, const void
                                workspace_bytes, stream);
 }
 
-extern "C" int attn_prefill_paged_ex(const void* q, const void* k_cache, const void* v_cache,
-                                     const int32_t* block_table, int32_t max_blocks_per_seq,
-                                     const int32_t* cu_seqlens_q, const int32_t* context_lens,
-                                     void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
-                                     int32_t max_context_len,
-                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                     int32_t block_size, int32_t num_blocks,
-                                     float scale, int32_t causal, attn_dtype dtype, int32_t flags,
-                                     void* workspace, size_t workspace_bytes, attn_stream_t stream) {
-  static const char* fn = "attn_prefill_paged";
+namespace {
+// Paged mask: row of packed query row r and head h at mask + r*ms[0] + h*ms[1],
+// mask_keys entries each.
+struct PagedMask {
+  const float* mask;
+  const int64_t* strides;
+  int32_t keys;
+};
+
+int prefill_paged_common(const char* fn, const PagedMask* pm, const void* q, const void* k_cache,
+                         const void* v_cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* cu_seqlens_q, const int32_t* context_lens, void* o, int32_t num_seqs,
+                         int32_t total_q, int32_t max_seqlen_q, int32_t max_context_len, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                         int32_t causal, attn_dtype dtype, int32_t flags, void* workspace, size_t workspace_bytes,
+                         attn_stream_t stream) {
   if ((flags & ~ATTN_PREFILL_SHARE_CU) != 0) return fail(ATTN_E_INVALID, "%s: unknown flags 0x%x", fn, flags);
   if (!q || !k_cache || !v_cache || !block_table || !cu_seqlens_q || !context_lens || !o)
     return fail(ATTN_E_INVALID, "%s: pointer arguments must be non-NULL", fn);
@@ -356,6 +347,15 @@ extern "C" int attn_prefill_paged_ex(const void* q, const void* k_cache, const v
     if (!aligned(p, 16)) return fail(ATTN_E_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
   if (!aligned(block_table, 4) || !aligned(cu_seqlens_q, 4) || !aligned(context_lens, 4))
     return fail(ATTN_E_INVALID, "%s: int32 arrays must be 4-byte aligned", fn);
+  if (pm != nullptr) {
+    if (!pm->mask || !pm->strides) return fail(ATTN_E_INVALID, "%s: mask and mask_strides must be non-NULL", fn);
+    // the kernels read four consecutive mask floats with one 16-byte load
+    if (!aligned(pm->mask, 16)) return fail(ATTN_E_INVALID, "%s: mask must be 16-byte aligned", fn);
+    for (int i = 0; i < 2; ++i)
+      if (pm->strides[i] < 0 || pm->strides[i] % 4 != 0)
+        return fail(ATTN_E_INVALID, "%s: mask strides must be >= 0 and multiples of 4 elements", fn);
+    if (pm->keys < 0) return fail(ATTN_E_INVALID, "%s: mask_keys must be >= 0", fn);
+  }
   if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return ok();
 
   PrefillArgs a{};
@@ -368,6 +368,18 @@ extern "C" int attn_prefill_paged_ex(const void* q, const void* k_cache, const v
   const int64_t ctx_bound = max_context_len > 0 ? max_context_len : (int64_t)max_blocks_per_seq * kBlockSizeHost;
   PrefillPlan p = plan_prefill(max_seqlen_q, ctx_bound, num_q_heads, a.group, num_seqs, head_dim, true,
                                (int64_t)total_q * num_q_heads, (flags & ATTN_PREFILL_SHARE_CU) != 0);
+  if (pm != nullptr) {
+    // one pass on the default tile (the masked kernel's only shapes)
+    a.mask = pm->mask;
+    a.ms_q = pm->strides[0]; a.ms_h = pm->strides[1]; a.ms_b = 0;
+    a.mask_keys = pm->keys;
+    a.mask_scale = (float)((double)kLog2eHost / (double)scale_log2);  // 1 / scale
+    p.t = prefill_tile(a.group);
+    p.deep_v = false;
+    p.num_m_tiles = ceil_div(max_seqlen_q, 32 * p.t.wph);
+    p.num_wg = (int64_t)p.num_m_tiles * (num_q_heads / p.t.hpw) * num_seqs;
+    p.num_splits = 1;
+  }
   if ((st = use_workspace(p, workspace, workspace_bytes, a, fn)) != ATTN_OK) return st;
   a.num_m_tiles = p.num_m_tiles;
   if (p.num_wg * a.num_splits > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
@@ -378,6 +390,37 @@ extern "C" int attn_prefill_paged_ex(const void* q, const void* k_cache, const v
   a.total_q = total_q;
   return launched(launch_prefill_bf16(a, head_dim, true, p.t.hpw, p.t.wph, p.deep_v,
                                       reinterpret_cast<hipStream_t>(stream)), fn);
+}
+}  // namespace
+
+extern "C" int attn_prefill_paged_ex(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                     void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                     int32_t max_context_len,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                     int32_t block_size, int32_t num_blocks,
+                                     float scale, int32_t causal, attn_dtype dtype, int32_t flags,
+                                     void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  return prefill_paged_common("attn_prefill_paged", nullptr, q, k_cache, v_cache, block_table, max_blocks_per_seq,
+                              cu_seqlens_q, context_lens, o, num_seqs, total_q, max_seqlen_q, max_context_len,
+                              num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, causal, dtype,
+                              flags, workspace, workspace_bytes, stream);
+}
+
+extern "C" int attn_prefill_paged_masked(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                                         const int32_t* cu_seqlens_q, const int32_t* context_lens,
+                                         const float* mask, const int64_t mask_strides[2], int32_t mask_keys,
+                                         void* o, int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
+                                         int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                         int32_t causal, attn_dtype dtype, attn_stream_t stream) {
+  const PagedMask pm{mask, mask_strides, mask_keys};
+  return prefill_paged_common("attn_prefill_paged_masked", &pm, q, k_cache, v_cache, block_table,
+                              max_blocks_per_seq, cu_seqlens_q, context_lens, o, num_seqs, total_q, max_seqlen_q,
+                              max_context_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                              causal, dtype, 0, nullptr, 0, stream);
 }
 
 // ---------------------------------------------------------------------------

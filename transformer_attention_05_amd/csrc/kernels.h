@@ -48,11 +48,14 @@ struct PrefillArgs {
   int64_t ws_rows;      // partial rows per split: (query row, head) pairs
   float* ws_o;          // [num_splits][ws_rows][D], unnormalised output
   float* ws_ml;         // [num_splits][ws_rows][2]: max (log2 units), row sum
-  // additive mask (contiguous prefill): fp32, element (b, h, i, j) at
-  // mask[b*ms_b + h*ms_h + i*ms_q + j]; null: none.  mask_scale = 1 / scale.
+  // additive mask, fp32; null: none.  mask_scale = 1 / scale.
+  // contiguous: element (b, h, i, j) at mask[b*ms_b + h*ms_h + i*ms_q + j];
+  // paged: element (packed query row r, h, key position j) at
+  // mask[r*ms_q + h*ms_h + j] for j < mask_keys (later keys are masked out).
   const float* mask;
   int64_t ms_b, ms_h, ms_q;
   float mask_scale;
+  int32_t mask_keys;
 };
 
 struct DecodeArgs {

@@ -103,7 +103,8 @@ __device__ __forceinline__ int vt_swz(int d) {   // V^T rows (paged): the two 16
 
 // Tile geometry: HPW query heads share every K/V tile (same kv head under
 // GQA); each head has WPH wavefronts of 32 queries.  MASKED adds the caller's
-// additive mask M to every score (contiguous layout only).
+// additive mask M to every score and carries the weights P of the PV
+// product as a bf16 pair (rounded value and rounded remainder).
 template <int D, bool PAGED, int HPW, int WPH, bool MASKED = false, bool DEEP_V = false>
 __global__ __launch_bounds__(64 * HPW * WPH) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(const PrefillArgs a) {
@@ -332,6 +333,11 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   for (int dt = 0; dt < D / 32; ++dt) oacc[dt] = f32x16{};
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
   bf16x8 pb[4];  // P of the current tile, B operand of the PV MFMAs
+  // MASKED: the remainder P - bf16(P), rounded to bf16 again.  A general
+  // mask can leave a row a few keys with weights far from uniform, where the
+  // 8-bit rounding of each weight no longer averages out; the second PV
+  // product with the remainder carries the weights to about 16 bits.
+  bf16x8 pl[MASKED ? 4 : 1];
 
   constexpr int NC = D / 16;        // contraction steps of S (16 channels each)
   constexpr int NS = 2 * NC;        // S MFMAs per tile
@@ -381,12 +387,20 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // the row sum of exactly those rounded weights
   auto exp_half = [&](const f32x16 (&s)[2], int kc, int h, float& lsum) {
 #pragma unroll
-    for (int i = 4 * h; i < 4 * h + 4; ++i)
-      pb[kc][i] = static_cast<__bf16>(__builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], c2, -mc)));
+    for (int i = 4 * h; i < 4 * h + 4; ++i) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], c2, -mc));
+      pb[kc][i] = static_cast<__bf16>(p);
+      // p - bf16(p) is exact in fp32
+      if constexpr (MASKED) pl[kc][i] = static_cast<__bf16>(p - static_cast<float>(pb[kc][i]));
+    }
 #pragma unroll
     for (int i = 2 * h; i < 2 * h + 2; ++i) {
       const bf16x2 pr = {pb[kc][2 * i], pb[kc][2 * i + 1]};
       lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+      if constexpr (MASKED) {
+        const bf16x2 pq = {pl[kc][2 * i], pl[kc][2 * i + 1]};
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pq, ones, lsum, false);
+      }
     }
   };
   // Phase A: S(next) = K Q^T on the matrix cores while the VALU forms P
@@ -418,6 +432,9 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       // keep the exponentials in this chunk: without a use here, code motion
       // above the scheduler sinks them to the PV product that consumes them
       if (q & 1) asm volatile("" : "+v"(pb[q >> 1]));
+      if constexpr (MASKED) {
+        if (q & 1) asm volatile("" : "+v"(pl[q >> 1]));
+      }
       asm volatile("" : "+v"(lsum));
 #pragma unroll
       for (int u = 0; u < SPC; ++u) {
@@ -447,12 +464,15 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         for (int dt = 0; dt < DT; ++dt) vnxt[dt] = v_op(sv, dt, kc + 1);
       }
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[dt] = mfma32(vcur[dt], pb[kc], oacc[dt]);
+      for (int dt = 0; dt < DT; ++dt) {
+        oacc[dt] = mfma32(vcur[dt], pb[kc], oacc[dt]);
+        if constexpr (MASKED) oacc[dt] = mfma32(vcur[dt], pl[kc], oacc[dt]);
+      }
 #pragma unroll
       for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, sn[kc >> 1][8 * (kc & 1) + r]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, MASKED ? 2 : 1, 1);  // MFMA
         if (kc < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // DS reads (next chunk)
         __builtin_amdgcn_sched_group_barrier(0x002, 1, 1);  // VALU
       }
@@ -476,24 +496,28 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       // lane keys t*BN + 32kt + 8g + 4hh + j, j < 4, are four consecutive
       // floats of the mask row (rows past the queries read the last row,
       // keys past the keys read nothing: both are discarded or masked)
-      const float* mrow = a.mask + b * a.ms_b + h * a.ms_h + (int64_t)min(qi, tq - 1) * a.ms_q;
-      f32x4 mv[2][4];
+      // Paged: the row of packed query q_row0 + qi, keys = positions in the
+      // sequence's context; entries at or past mask_keys are never read and
+      // those keys are masked out.
+      const int64_t mq = PAGED ? q_row0 + min(qi, tq - 1) : (int64_t)min(qi, tq - 1);
+      const float* mrow = a.mask + (PAGED ? 0 : b * a.ms_b) + h * a.ms_h + mq * a.ms_q;
+      const int mk = PAGED ? min(tk, a.mask_keys) : tk;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt) {
+        f32x4 mv[4];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int key0 = t * BN + kt * 32 + 8 * g4 + 4 * hh;
-          if (key0 + 4 <= tk) {
-            mv[kt][g4] = *reinterpret_cast<const f32x4*>(mrow + key0);
+          if (key0 + 4 <= mk) {
+            mv[g4] = *reinterpret_cast<const f32x4*>(mrow + key0);
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mv[kt][g4][j] = key0 + j < tk ? mrow[key0 + j] : 0.f;
+            for (int j = 0; j < 4; ++j) mv[g4][j] = key0 + j < mk ? mrow[key0 + j] : (key0 + j < tk ? -INFINITY : 0.f);
           }
         }
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = fmaf(mv[kt][r >> 2][r & 3], a.mask_scale, s[kt][r]);
+        for (int r = 0; r < 16; ++r) s[kt][r] = fmaf(mv[r >> 2][r & 3], a.mask_scale, s[kt][r]);
+      }
     }
     const int lim = a.causal ? min(key_end - 1, qi + off) : key_end - 1;
 #pragma unroll
@@ -870,11 +894,11 @@ static void launch_one(const PrefillArgs& a, bool deep_v, hipStream_t s) {
       return;
     }
   }
-  if constexpr (!PAGED && ((HPW == 2 && WPH == 2) || (HPW == 1 && WPH == 4))) {
-    // the masked variant exists for the default contiguous tiles only (the
-    // host picks one of them and never splits a masked launch)
+  if constexpr ((HPW == 2 && WPH == 2) || (HPW == 1 && WPH == 4)) {
+    // the masked variant exists for the default tiles only (the host picks
+    // one of them and never splits a masked launch)
     if (a.mask != nullptr) {
-      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, HPW, WPH, true>), grid, dim3(64 * HPW * WPH), 0, s, a);
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, HPW, WPH, true>), grid, dim3(64 * HPW * WPH), 0, s, a);
       return;
     }
   }

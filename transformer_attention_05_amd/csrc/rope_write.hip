@@ -1,10 +1,10 @@
 // Fused rotary embedding + paged KV-cache write.
 //
-// "Fast Attention Kernels and Operator Fusion", §Operator Fusion, lists
-// "applying rotary position embeddings to queries and keys" and "updating the
-// KV cache while transforming key and value tensors" as fusion targets: one
-// pass reads q, k and v once, rotates q in place and writes the rotated key
-// and the value into the token's paged slot.
+// "Fast Attention Kernels and Operator Fusion", §Operator Fusion, counts the
+// rotary embedding of queries and keys, and the KV-cache update made while
+// keys and values are transformed, among the usual fusion targets: one pass
+// reads q, k and v once, rotates q in place and writes the rotated key and
+// the value into the token's paged slot.
 //
 // Rotation (half-split pairs): for i < D/2 the pair (x[i], x[i + D/2]) turns
 // by angle pos * base^(-2i/D) (frequencies from the host, in double; the
