@@ -276,6 +276,31 @@ ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v
                       const int32_t* plan, int32_t plan_items,
                       void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/* attn_decode_paged_noalloc -- attn_decode_paged for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments without a
+ * workspace, the same kernels and results bit for bit.  The split-KV
+ * scratch (arrival counters, partial outputs and (m, l) pairs, in
+ * attn_decode_paged's workspace layout) is a fixed 32 MiB device array of
+ * the library's own, which every GPU the library runs on holds until the
+ * process ends; the first call on a device finds its address there and
+ * zero-fills it with a kernel on `stream`.  Nothing is allocated or freed.
+ *   - A call whose attn_decode_paged_workspace_size(...) exceeds 32 MiB
+ *     returns ATTN_E_NOMEM (launching nothing): about 160 sequences of
+ *     12 query heads at 32768 tokens with 1024-token partitions fit.
+ *   - Every call on one GPU shares that GPU's array, and a completed call
+ *     leaves its counters zero for the next; calls that overlap on one GPU
+ *     (other streams, other threads) race and corrupt each other's results.
+ *     Serialise them on one stream.
+ * ---------------------------------------------------------------------- */
+ATTN_API int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_table, const int32_t* context_lens, void* o,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                              int32_t partition_size, float scale, attn_dtype dtype,
+                              const int32_t* plan, int32_t plan_items, attn_stream_t stream);
+
 /* -------------------------------------------------------------------------
  * attn_decode_paged_rope -- the decode above, with each sequence's new token
  * rotated and written into the cache by the same launch.

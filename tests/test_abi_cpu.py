@@ -352,6 +352,26 @@ def test_paged_prefill_and_write_reject(lib):
     assert st == 0  # nothing to do
 
 
+def test_decode_noalloc_rejects_before_any_hip_call(lib):
+    """The no-allocation decode validates like attn_decode_paged, and a call
+    whose scratch need exceeds the fixed 32 MiB is refused with NOMEM before
+    any HIP call (these run without a GPU)."""
+    def na(**kw):
+        a = dict(q=P, s=64, hq=12, hkv=2, d=128, bs=16, mb=256, mctx=4096, part=0, dtype=ATTN_BF16)
+        a.update(kw)
+        return lib.attn_decode_paged_noalloc(a["q"], P, P, P, P, P, a["s"], a["hq"], a["hkv"], a["d"], a["bs"], 1000,
+                                             a["mb"], a["mctx"], a["part"], 0.0, a["dtype"], None, 0, None)
+    assert na(q=None) == ATTN_E_INVALID
+    assert na(d=96) == ATTN_E_UNSUPPORTED
+    assert na(part=100) == ATTN_E_INVALID
+    assert na(mb=10) == ATTN_E_INVALID
+    # 4096 sequences x 12 heads x 32 partitions of 1024 tokens: ~200 MiB of partials
+    need = lib.attn_decode_paged_workspace_size(4096, 12, 2, 128, 32768, 1024)
+    assert need > (32 << 20)
+    assert na(s=4096, mb=2048, mctx=32768, part=1024) == ATTN_E_NOMEM
+    assert "32" in mi.attn_last_error() or "scratch" in mi.attn_last_error()
+
+
 def test_paged_masked_rejects(lib):
     ms = (ctypes.c_int64 * 2)(12 * 304, 304)
 

@@ -1,0 +1,62 @@
+"""attn_decode_paged_noalloc, the decode for callers that cannot allocate:
+through the C ABI against attn_decode_paged (same kernels, so bit for bit)
+and the oracle, on two calls in a row (the second smaller), then a call too
+large for the fixed scratch, refused without a launch."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import transformer_attention_05_amd as mi
+from tests.gpu_util import DEV, check, f64, say
+from workloads import build_decode_pool, decode_case, to_f64
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def run_both(case, partition_size):
+    kc, vc = build_decode_pool(case, DEV)
+    q = case.q.to(DEV)
+    bt = torch.from_numpy(case.block_tables).to(DEV)
+    cl = torch.from_numpy(case.lengths.astype(np.int32)).to(DEV)
+    mctx = int(case.lengths.max())
+    plan = torch.from_numpy(mi.attn_decode_paged_plan(case.lengths, case.hkv, mctx, partition_size)).to(DEV)
+    o_na = torch.full_like(q, float("nan"))
+    mi.attn_decode_paged_noalloc(q, kc, vc, bt, cl, mctx, o_na, partition_size=partition_size, plan=plan)
+    o_ws = mi.attn_decode_paged(q, kc, vc, bt, cl, mctx, partition_size=partition_size, plan=plan)
+    torch.cuda.synchronize()
+    return o_na.cpu(), o_ws.cpu()
+
+
+def reference(case):
+    ks = [to_f64(k) for k in case.k]
+    vs = [to_f64(v) for v in case.v]
+    out, _ = oracle.decode(to_f64(case.q), ks, vs)
+    return out
+
+
+@pytest.mark.parametrize("first,second", [((64, 128, 4096, 0), (9, 1, 3000, 256))])
+def test_noalloc_decode_two_calls(first, second):
+    for i, (n, lo, hi, part) in enumerate((first, second)):
+        say(f"case: no-allocation decode, call {i + 1}: {n} seqs ctx U[{lo}, {hi}], partition {part or 'auto'}")
+        case = decode_case(3100 + i, n, lo, hi)
+        o_na, o_ws = run_both(case, part)
+        assert torch.equal(o_na.view(torch.int16), o_ws.view(torch.int16)), f"call {i + 1}: differs from attn_decode_paged"
+        check(f64(o_na), reference(case), torch.bfloat16, f"call {i + 1} vs oracle")
+
+
+def test_noalloc_decode_refuses_above_the_fixed_scratch():
+    say("case: no-allocation decode above the fixed scratch")
+    q = torch.zeros(4096, 12, 128, dtype=torch.bfloat16, device=DEV)
+    kc = torch.zeros(8, 2, 16, 128, dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros(8, 2, 128, 16, dtype=torch.bfloat16, device=DEV)
+    bt = torch.zeros(4096, 2048, dtype=torch.int32, device=DEV)
+    cl = torch.ones(4096, dtype=torch.int32, device=DEV)
+    o = torch.zeros_like(q)
+    with pytest.raises(mi.AttnError) as e:
+        mi.attn_decode_paged_noalloc(q, kc, vc, bt, cl, 32768, o, partition_size=1024)
+    assert e.value.status == mi.ATTN_E_NOMEM
+    torch.cuda.synchronize()
+    assert int(o.abs().sum().item()) == 0, "a refused call launches nothing"

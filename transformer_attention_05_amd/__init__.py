@@ -21,6 +21,7 @@ __all__ = [
     "attn_copy_blocks",
     "attn_decode_paged",
     "attn_decode_paged_auto_partition",
+    "attn_decode_paged_noalloc",
     "attn_decode_paged_rope",
     "attn_decode_paged_plan",
     "attn_decode_paged_workspace_size",
@@ -74,6 +75,9 @@ _SIGNATURES = {
     "attn_decode_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp, _c_i32,
                                          _vp, ctypes.c_size_t, _vp]),
+    "attn_decode_paged_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                 _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
+                                                 ctypes.c_int, _vp, _c_i32, _vp]),
     "attn_decode_paged_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp,
                                               _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                               _c_i32, ctypes.c_float, ctypes.c_int, _vp, _c_i32, _vp,
@@ -451,6 +455,30 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, context_lens, max_contex
         int(max_context_len), int(partition_size), float(scale), _dtype_code(q),
         _dev(plan, "plan") if plan is not None else None, int(plan.shape[0]) if plan is not None else 0,
         ws_ptr, ws_bytes, _stream(q))
+    _check(st)
+    return o
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, context_lens, max_context_len, o,
+                              partition_size=0, scale=0.0, plan=None):
+    """attn_decode_paged with the library's fixed device scratch instead of
+    a workspace: nothing is allocated, here or in the library (``o`` is
+    required).  Calls that overlap on one GPU race."""
+    s, hq, d, nb, hkv, bs, s_bt = _check_paged(q, o, k_cache, v_cache, block_table, context_lens)
+    if s_bt != s:
+        raise ValueError(f"block_table has {s_bt} rows for {s} queries")
+    if o is None:
+        raise ValueError("o is required (the no-allocation call allocates nothing)")
+    if plan is not None:
+        _int32(plan, "plan")
+        if plan.dim() != 2 or plan.shape[1] != 2:
+            raise ValueError("plan must be [n, 2] (sequence, partition)")
+    st = load().attn_decode_paged_noalloc(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
+        _dev(context_lens, "context_lens"), _dev(o, "o"), s, hq, hkv, d, bs, nb, block_table.shape[1],
+        int(max_context_len), int(partition_size), float(scale), _dtype_code(q),
+        _dev(plan, "plan") if plan is not None else None, int(plan.shape[0]) if plan is not None else 0,
+        _stream(q))
     _check(st)
     return o
 

@@ -525,12 +525,15 @@ struct DecodeWrite {
   float rope_base;
 };
 
+// use_scratch: the workspace is the library's fixed device scratch
+// (attn_decode_paged_noalloc); workspace / workspace_bytes are ignored.
 int decode_common(const char* fn, const DecodeWrite* w, const void* q, const void* k_cache, const void* v_cache,
                   const int32_t* block_table, const int32_t* context_lens, void* o, int32_t num_seqs,
                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                   int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                   int32_t partition_size, float scale, attn_dtype dtype, const int32_t* plan,
-                  int32_t plan_items, void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+                  int32_t plan_items, void* workspace, size_t workspace_bytes, attn_stream_t stream,
+                  bool use_scratch = false) {
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !o)
     return fail(ATTN_E_INVALID, "%s: pointer arguments must be non-NULL", fn);
   if (num_seqs < 0 || num_blocks < 1 || max_context_len < 1)
@@ -558,13 +561,25 @@ int decode_common(const char* fn, const DecodeWrite* w, const void* q, const voi
   if (plan != nullptr && (int64_t)plan_items > (int64_t)num_seqs * gm.max_parts)
     return fail(ATTN_E_INVALID, "%s: plan_items %d exceeds num_seqs x partitions", fn, plan_items);
   const size_t need = gm.total();
-  if (need > 0) {
+  if (use_scratch) {
+    if (need > kDecodeScratchBytes)
+      return fail(ATTN_E_NOMEM, "%s: the call needs %zu bytes of scratch, above the fixed %zu (fewer sequences, or "
+                  "a larger partition_size, fit)", fn, need, kDecodeScratchBytes);
+  } else if (need > 0) {
     if (!workspace) return fail(ATTN_E_INVALID, "%s: workspace of %zu bytes required", fn, need);
     if (!aligned(workspace, 256)) return fail(ATTN_E_INVALID, "%s: workspace must be 256-byte aligned", fn);
     if (workspace_bytes < need)
       return fail(ATTN_E_NOMEM, "%s: workspace %zu bytes, %zu needed", fn, workspace_bytes, need);
   }
+  if ((int64_t)plan_items * num_kv_heads * ceil_div(num_q_heads / num_kv_heads, 16) > INT32_MAX)
+    return fail(ATTN_E_UNSUPPORTED, "%s: plan too large for one launch", fn);
+  if ((int64_t)num_kv_heads * ceil_div(num_q_heads / num_kv_heads, 16) > 65535 || num_seqs > 65535)
+    return fail(ATTN_E_UNSUPPORTED, "%s: at most 65535 sequences (and kv head slices) per call", fn);
   if (num_seqs == 0) return ok();
+  if (use_scratch && need > 0) {
+    const hipError_t e = decode_scratch(reinterpret_cast<hipStream_t>(stream), &workspace);
+    if (e != hipSuccess) return fail(ATTN_E_DEVICE, "%s: decode scratch: %s", fn, hipGetErrorString(e));
+  }
   const int32_t group = num_q_heads / num_kv_heads;
   DecodeArgs a{};
   a.q = q; a.k_cache = k_cache; a.v_cache = v_cache;
@@ -581,10 +596,6 @@ int decode_common(const char* fn, const DecodeWrite* w, const void* q, const voi
   a.scale_log2 = scale_log2;
   a.plan = plan;
   a.plan_items = plan_items;
-  if ((int64_t)plan_items * num_kv_heads * a.head_groups > INT32_MAX)
-    return fail(ATTN_E_UNSUPPORTED, "%s: plan too large for one launch", fn);
-  if ((int64_t)num_kv_heads * a.head_groups > 65535 || num_seqs > 65535)
-    return fail(ATTN_E_UNSUPPORTED, "%s: at most 65535 sequences (and kv head slices) per call", fn);
   if (w != nullptr) {
     a.q_rot_out = w->q_rot_out;
     a.k_new = w->k_new;
@@ -610,6 +621,18 @@ extern "C" int attn_decode_paged(const void* q, const void* k_cache, const void*
                        num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, partition_size, scale, dtype, plan, plan_items, workspace, workspace_bytes,
                        stream);
+}
+
+extern "C" int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                         const int32_t* block_table, const int32_t* context_lens, void* o,
+                                         int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                         int32_t max_blocks_per_seq, int32_t max_context_len,
+                                         int32_t partition_size, float scale, attn_dtype dtype,
+                                         const int32_t* plan, int32_t plan_items, attn_stream_t stream) {
+  return decode_common("attn_decode_paged_noalloc", nullptr, q, k_cache, v_cache, block_table, context_lens, o,
+                       num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, partition_size, scale, dtype, plan, plan_items, nullptr, 0, stream, true);
 }
 
 extern "C" int attn_decode_paged_rope(void* q_rot_out, const void* q, const void* k_new, const void* v_new,

@@ -31,6 +31,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -408,7 +410,46 @@ __global__ __launch_bounds__(64 * DW) void decode_planned_kernel(const DecodeArg
   decode_body<D, DW, FUSED>(a, p, yy, s, lds);
 }
 
+// ---------------------------------------------------------------------------
+// Fixed decode scratch for attn_decode_paged_noalloc: the same workspace
+// layout (arrival counters, partial outputs, (m, l) pairs) in a device array
+// of the library's own, so that a call allocates nothing.  Each GPU holds
+// its own copy at its own address, found once per device.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+__global__ __launch_bounds__(256) void zero_fill_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) p[i] = uint4{0, 0, 0, 0};
+}
+
 }  // namespace
+
+hipError_t decode_scratch(hipStream_t s, void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    // the host-side name of the array is not a device address: take the
+    // address this device gave it, and use only that from here on
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // the arrival counters must start at zero (every completed call leaves
+    // them zero again); a fill kernel rather than a memset, so that a first
+    // call under graph capture records a plain kernel node
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(p),
+                       kDecodeScratchBytes / 16);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
 
 template <int D, bool FUSED>
 static void launch_decode_t(const DecodeArgs& a, hipStream_t st) {

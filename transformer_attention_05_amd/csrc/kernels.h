@@ -128,6 +128,11 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, i
                                hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStream_t s);
+// The library's fixed decode scratch on the current device (32 MiB, found
+// and zero-filled on `s` on the first call per device), for
+// attn_decode_paged_noalloc.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t decode_scratch(hipStream_t s, void** out);
 hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_residual_rms_norm(const RmsNormArgs& a, bool bf16, hipStream_t s);
