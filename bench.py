@@ -11,6 +11,13 @@ timed both ways: RoPE write then decode, and the decode launch that writes
 its own tokens.
 Inputs are synthetic and already resident in HBM when timing starts.
 
+Timing: the headline times --steps steps after --warmup untimed ones,
+between two device synchronisations.  Every component figure takes 20
+untimed calls and then 100 timed calls in samples of 5 back-to-back calls
+between a pair of HIP events on the launching stream; it reports the median
+(`us`), the min and the mean per call.  The decode roofline uses the mean
+(the average launch duration), as the profiler summary does.
+
 value = percent of the step's roofline time reached:
     100 * max(F / 2.5 PFLOP/s, B / 8 TB/s) / measured step time
 with F the chunked-prefill flops (4 * D per unmasked query-key pair) and B the
@@ -89,23 +96,51 @@ def write_bytes(n_tokens):
 
 # ----------------------------------------------------------------------------- timing helpers
 
-def per_call_ms(torch, fn, n):
-    """Average duration of one call, in ms, over n back-to-back calls fn(0) ..
-    fn(n - 1): one pair of HIP events on the current stream (the stream the
-    calls launch on) around all of them.  An event recorded between two
-    kernels leaves the GPU idle for several microseconds on this stack, so
-    per-call event pairs would inflate short kernels."""
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for i in range(n):
+WARM_CALLS, TIMED_CALLS, PER_SAMPLE = 20, 100, 5
+
+
+def timed(torch, fn, warm=None, calls=None, per=PER_SAMPLE):
+    """Per-call duration of fn(i), in ms: `warm` untimed calls, then `calls`
+    timed ones as calls / per samples, each a pair of HIP events on the
+    current stream (the stream the calls launch on) around `per` back-to-back
+    calls.  (An event recorded between two kernels leaves the GPU idle for
+    several microseconds on this stack, so an event pair around every single
+    call would inflate short kernels.)  Returns mean, median and min over the
+    samples, and the call counts."""
+    warm = WARM_CALLS if warm is None else warm
+    calls = TIMED_CALLS if calls is None else calls
+    for i in range(warm):
         fn(i)
-    b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / n
+    samples = []
+    for k in range(calls // per):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for j in range(per):
+            fn(k * per + j)
+        b.record()
+        torch.cuda.synchronize()
+        samples.append(a.elapsed_time(b) / per)
+    return dict(mean=float(np.mean(samples)), median=float(np.median(samples)), min=float(np.min(samples)),
+                warm=warm, calls=(calls // per) * per, per_sample=per)
+
+
+def fig(t, work=None, unit=None, peak=None, key="frac_of_peak"):
+    """A component figure: median us (the primary), min and mean us, the
+    iteration counts, and the median's rate (and fraction of peak)."""
+    d = {"us": round(t["median"] * 1e3, 2), "us_min": round(t["min"] * 1e3, 2), "us_mean": round(t["mean"] * 1e3, 2),
+         "iters": f"{t['warm']} warm-up + {t['calls']} timed calls ({t['per_sample']} per event pair)"}
+    if work is not None:
+        rate = work / (t["median"] / 1e3)
+        d[unit] = round(rate / (1e12 if unit == "TFLOP/s" else 1e9), 1)
+        if peak:
+            d[key] = round(rate / peak, 4)
+    return d
 
 
 def main():
+    global WARM_CALLS, TIMED_CALLS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -116,7 +151,11 @@ def main():
                     help="run one workload only (for profiling)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="first copy a 256 MiB buffer (known bytes) so hardware byte counters can be scaled")
+    ap.add_argument("--calls", type=int, default=TIMED_CALLS,
+                    help="timed calls per component figure (default 100; fewer for profiler runs)")
+    ap.add_argument("--warm-calls", type=int, default=WARM_CALLS, help="untimed calls before each figure (default 20)")
     args = ap.parse_args()
+    WARM_CALLS, TIMED_CALLS = max(0, args.warm_calls), max(PER_SAMPLE, args.calls)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(multi-GPU sharding is a design note, not implemented)"}))
@@ -162,14 +201,28 @@ def main():
             step.run()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / args.steps
-        # per-stage durations: each stage repeated on its own, back to back,
-        # between two HIP events on the stream the kernels are launched on
-        stage_ms = []
-        for fn in (step.write, step.prefill, step.decode):
-            fn()
+        # the step again, event-timed (median and min over samples)
+        t_step = timed(torch, lambda i: step.run())
+        # the prefill and the decode inside the step: events on each stream
+        # around each of them (each event adds a few microseconds of idle
+        # time to its stream, so these are slight overestimates)
+        names = ("prefill0", "prefill1", "decode0", "decode1")
+        in_pre, in_dec = [], []
+        for _ in range(WARM_CALLS + TIMED_CALLS // PER_SAMPLE):
+            marks = {n: torch.cuda.Event(enable_timing=True) for n in names}
+            step.run(marks)
             torch.cuda.synchronize()
-            stage_ms.append(per_call_ms(torch, lambda i: fn(), args.steps))
-        ms_wr, ms_pre, ms_dec = stage_ms
+            in_pre.append(marks["prefill0"].elapsed_time(marks["prefill1"]))
+            in_dec.append(marks["decode0"].elapsed_time(marks["decode1"]))
+        in_pre, in_dec = in_pre[WARM_CALLS:], in_dec[WARM_CALLS:]
+        in_step = dict(prefill=dict(mean=float(np.mean(in_pre)), median=float(np.median(in_pre)),
+                                    min=float(np.min(in_pre)), warm=WARM_CALLS, calls=len(in_pre), per_sample=1),
+                       decode=dict(mean=float(np.mean(in_dec)), median=float(np.median(in_dec)),
+                                   min=float(np.min(in_dec)), warm=WARM_CALLS, calls=len(in_dec), per_sample=1))
+        # per-stage durations: each stage repeated on its own, back to back,
+        # between HIP events on the stream the kernels are launched on
+        stages = [timed(torch, lambda i, f=fn: f()) for fn in (step.write, step.prefill, step.decode)]
+        ms_wr, ms_pre, ms_dec = (t["mean"] for t in stages)
         # the same step captured in a HIP graph, replays back to back
         graph_s = None
         if not args.no_components:
@@ -186,7 +239,8 @@ def main():
         # larger of its total HBM bytes and its total matrix-core flops
         B_pre = prefill_io_bytes(case)
         t_roof = max(F / PEAK_BF16_FLOPS, (B_dec + B_wr + B_pre) / PEAK_HBM)
-        out["mixed"] = dict(wall_s=wall, ms_write=ms_wr, ms_prefill=ms_pre, ms_decode=ms_dec, F=F, B_dec=B_dec,
+        out["mixed"] = dict(wall_s=wall, ms_write=ms_wr, ms_prefill=ms_pre, ms_decode=ms_dec, stages=stages,
+                            t_step=t_step, in_step=in_step, F=F, B_dec=B_dec,
                             B_wr=B_wr, B_pre=B_pre, t_roof=t_roof, n_new=n_new, part=mi.attn_decode_paged_auto_partition(
                                 len(case.dec_lengths), HKV, int(case.dec_lengths.max())),
                             dec_tokens=int(case.dec_lengths.sum()), pool_blocks=case.num_blocks,
@@ -201,13 +255,10 @@ def main():
         q, k, v = prefill_case(1003, 1, 16384, HQ, HKV, D, torch.bfloat16)
         qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
         o = torch.empty_like(qd)
-        for _ in range(max(2, args.warmup)):
-            mi.attn_prefill(qd, kd, vd, o=o)
-        torch.cuda.synchronize()
-        ms = per_call_ms(torch, lambda i: mi.attn_prefill(qd, kd, vd, o=o), max(5, args.steps // 2))
+        t = timed(torch, lambda i: mi.attn_prefill(qd, kd, vd, o=o))
         fl = 4 * D * HQ * 16384 * 16385 // 2
-        out["prefill_c4"] = dict(ms=ms, flops=fl)
-        log(f"bench: prefill C4 {ms:.3f} ms  {fl / ms / 1e9:.1f} TFLOP/s")
+        out["prefill_c4"] = dict(t=t, flops=fl)
+        log(f"bench: prefill C4 median {t['median']:.3f} ms  {fl / t['median'] / 1e9:.1f} TFLOP/s")
         del qd, kd, vd, o
         # the 2048-token prompt: too few query tiles for the GPU, so split-KV
         log("bench: contiguous prefill T 2048")
@@ -216,23 +267,17 @@ def main():
         o = torch.empty_like(qd)
         ws = torch.empty(max(256, mi.attn_prefill_workspace_size(1, 2048, 2048, HQ, HKV, D)), dtype=torch.uint8,
                          device=dev)
-        for _ in range(max(3, args.warmup)):
-            mi.attn_prefill(qd, kd, vd, o=o, workspace=ws)
-        torch.cuda.synchronize()
-        ms = per_call_ms(torch, lambda i: mi.attn_prefill(qd, kd, vd, o=o, workspace=ws), max(10, args.steps))
+        t = timed(torch, lambda i: mi.attn_prefill(qd, kd, vd, o=o, workspace=ws))
         fl = 4 * D * HQ * 2048 * 2049 // 2
-        out["prefill_c2"] = dict(ms=ms, flops=fl)
-        log(f"bench: prefill C2 {ms * 1e3:.1f} us  {fl / ms / 1e9:.1f} TFLOP/s")
+        out["prefill_c2"] = dict(t=t, flops=fl)
+        log(f"bench: prefill C2 median {t['median'] * 1e3:.1f} us  {fl / t['median'] / 1e9:.1f} TFLOP/s")
         # the same shape with a general additive mask (one fp32 [T, T] mask for
         # every head, no causal structure): every (query, key) pair is computed
         mask = additive_mask(1006, (2048, 2048), amp=1.0, p_masked=0.1).to(dev)
-        for _ in range(3):
-            mi.attn_prefill_masked(qd, kd, vd, mask, o=o)
-        torch.cuda.synchronize()
-        ms = per_call_ms(torch, lambda i: mi.attn_prefill_masked(qd, kd, vd, mask, o=o), max(10, args.steps))
+        t = timed(torch, lambda i: mi.attn_prefill_masked(qd, kd, vd, mask, o=o))
         fl = 4 * D * HQ * 2048 * 2048
-        out["prefill_masked"] = dict(ms=ms, flops=fl)
-        log(f"bench: masked prefill T 2048 {ms * 1e3:.1f} us  {fl / ms / 1e9:.1f} TFLOP/s")
+        out["prefill_masked"] = dict(t=t, flops=fl)
+        log(f"bench: masked prefill T 2048 median {t['median'] * 1e3:.1f} us  {fl / t['median'] / 1e9:.1f} TFLOP/s")
         del qd, kd, vd, o, ws, mask
 
     # ------------------------------------------------------------------ uniform decode
@@ -248,15 +293,10 @@ def main():
                          device=dev)
         o = torch.empty_like(qd)
         plan = torch.from_numpy(mi.attn_decode_paged_plan(dc.lengths, HKV, mx)).to(dev)
-        for i in range(max(3, args.warmup)):
-            mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws, plan=plan)
-        torch.cuda.synchronize()
-        n = max(9, args.steps)
-        ms = per_call_ms(torch, lambda i: mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws,
-                                                                 plan=plan), n)
+        t = timed(torch, lambda i: mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws, plan=plan))
         by = decode_bytes(dc.lengths)
-        out["decode_c3"] = dict(ms=ms, bytes=by, part=mi.attn_decode_paged_auto_partition(64, HKV, mx))
-        log(f"bench: decode C3 {ms * 1e3:.1f} us  {by / ms / 1e6:.0f} GB/s")
+        out["decode_c3"] = dict(t=t, bytes=by, part=mi.attn_decode_paged_auto_partition(64, HKV, mx))
+        log(f"bench: decode C3 median {t['median'] * 1e3:.1f} us  {by / t['median'] / 1e6:.0f} GB/s")
         # a decode-only serving step: each sequence's new token (the last of
         # its context) rotated and written into its slot, then the decode;
         # as two launches, and as the one decode launch that writes it
@@ -276,15 +316,10 @@ def main():
         def one_launch(i):
             mi.attn_decode_paged_rope(qd, k_new, v_new, pos, slots, *pools[i % 3], bt, cl, mx, o=o, q_rot_out=q_rot,
                                       workspace=ws, plan=plan)
-        step_ms = {}
-        for name, fn in (("write_then_decode", two_launches), ("fused", one_launch)):
-            for i in range(3):
-                fn(i)
-            torch.cuda.synchronize()
-            step_ms[name] = per_call_ms(torch, fn, n)
-        out["decode_step_c3"] = dict(bytes=by + write_bytes(64), **step_ms)
-        log(f"bench: decode-only step C3: write + decode {step_ms['write_then_decode'] * 1e3:.1f} us, "
-            f"fused {step_ms['fused'] * 1e3:.1f} us")
+        step_t = {name: timed(torch, fn) for name, fn in (("write_then_decode", two_launches), ("fused", one_launch))}
+        out["decode_step_c3"] = dict(bytes=by + write_bytes(64), **step_t)
+        log(f"bench: decode-only step C3: write + decode {step_t['write_then_decode']['median'] * 1e3:.1f} us, "
+            f"fused {step_t['fused']['median'] * 1e3:.1f} us")
         del pools
         # copy on write of prefix sharing: 4096 whole blocks (both pools, 2 kv
         # heads, D 128, bf16: 8 KiB per block and pool) copied in one launch;
@@ -295,12 +330,9 @@ def main():
         perm = np.random.default_rng(1007).permutation(30000)
         sets = [torch.from_numpy(np.stack([perm[i * 8192:i * 8192 + 4096], perm[i * 8192 + 4096:(i + 1) * 8192]],
                                           1).astype(np.int32)).to(dev) for i in range(3)]
-        for i in range(3):
-            mi.attn_copy_blocks(kc, vc, sets[i])
-        torch.cuda.synchronize()
-        ms = per_call_ms(torch, lambda i: mi.attn_copy_blocks(kc, vc, sets[i % 3]), max(12, args.steps))
-        out["copy_blocks"] = dict(ms=ms, bytes=4096 * 2 * HKV * 16 * D * ELT * 2)
-        log(f"bench: copy 4096 blocks {ms * 1e3:.1f} us")
+        t = timed(torch, lambda i: mi.attn_copy_blocks(kc, vc, sets[i % 3]))
+        out["copy_blocks"] = dict(t=t, bytes=4096 * 2 * HKV * 16 * D * ELT * 2)
+        log(f"bench: copy 4096 blocks median {t['median'] * 1e3:.1f} us")
         del kc, vc
 
     # ------------------------------------------------------------------ fused residual + RMSNorm
@@ -313,13 +345,9 @@ def main():
         wgt = torch.ones(1536, dtype=torch.bfloat16, device=dev)
         yb = torch.empty(4224, 1536, dtype=torch.bfloat16, device=dev)
         hb = torch.empty_like(yb)
-        for i in range(3):
-            mi.attn_residual_rms_norm(*sets[i], wgt, y=yb, residual_out=hb)
-        torch.cuda.synchronize()
-        ms = per_call_ms(torch, lambda i: mi.attn_residual_rms_norm(*sets[i % 3], wgt, y=yb, residual_out=hb),
-                         max(12, args.steps))
-        out["rmsnorm"] = dict(ms=ms, bytes=4224 * 1536 * ELT * 4 + 1536 * ELT)
-        log(f"bench: residual + RMSNorm 4224 x 1536 {ms * 1e3:.1f} us")
+        t = timed(torch, lambda i: mi.attn_residual_rms_norm(*sets[i % 3], wgt, y=yb, residual_out=hb))
+        out["rmsnorm"] = dict(t=t, bytes=4224 * 1536 * ELT * 4 + 1536 * ELT)
+        log(f"bench: residual + RMSNorm 4224 x 1536 median {t['median'] * 1e3:.1f} us")
         del sets, yb, hb
 
     # ------------------------------------------------------------------ CPU baseline (oracle)
@@ -409,57 +437,53 @@ def emit(args, out, cpu):
                          "parallelism": "single GPU"}
         dec_s = m["ms_decode"] / 1e3
         gbps = m["B_dec"] / dec_s / 1e9
+        ins = m["in_step"]["decode"]
         res["roofline"] = {"kernel": "paged decode (decode_planned_kernel: partitions and their merge, one launch)",
                            "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                            "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": measured_traffic(),
-                           "algorithmic_bytes_per_launch": m["B_dec"], "avg_launch_us": round(m["ms_decode"] * 1e3, 2)}
-        comps["step_write"] = {"us": round(m["ms_write"] * 1e3, 2), "GB/s": round(m["B_wr"] / (m["ms_write"] / 1e3) / 1e9, 1)}
-        comps["step_chunked_prefill"] = {"us": round(m["ms_prefill"] * 1e3, 2),
-                                         "TFLOP/s": round(m["F"] / (m["ms_prefill"] / 1e3) / 1e12, 1),
-                                         "frac_of_bf16_peak": round(m["F"] / (m["ms_prefill"] / 1e3) / PEAK_BF16_FLOPS, 4)}
-        comps["step_decode"] = {"us": round(m["ms_decode"] * 1e3, 2), "GB/s": round(gbps, 1),
-                                "frac_of_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4)}
+                           "algorithmic_bytes_per_launch": m["B_dec"], "avg_launch_us": round(m["ms_decode"] * 1e3, 2),
+                           "launches_timed": m["stages"][2]["calls"],
+                           "in_step": {"avg_launch_us": round(ins["mean"] * 1e3, 2),
+                                       "median_launch_us": round(ins["median"] * 1e3, 2),
+                                       "frac": round(m["B_dec"] / (ins["mean"] / 1e3) / PEAK_HBM, 4),
+                                       "note": "the same decode inside the timed step, beside the chunked prefill "
+                                               "(events on its stream)"}}
+        st_w, st_p, st_d = m["stages"]
+        comps["step"] = fig(m["t_step"])
+        comps["step"]["frac_of_step_roofline"] = round(m["t_roof"] / (m["t_step"]["median"] / 1e3), 4)
+        comps["step_write"] = fig(st_w, m["B_wr"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
+        comps["step_chunked_prefill"] = fig(st_p, m["F"], "TFLOP/s", PEAK_BF16_FLOPS, "frac_of_bf16_peak")
+        comps["step_decode"] = fig(st_d, m["B_dec"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
+        comps["step_chunked_prefill_in_step"] = fig(m["in_step"]["prefill"], m["F"], "TFLOP/s", PEAK_BF16_FLOPS,
+                                                    "frac_of_bf16_peak")
+        comps["step_decode_in_step"] = fig(m["in_step"]["decode"], m["B_dec"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
         comps["step_roofline_us"] = round(m["t_roof"] * 1e6, 2)
         if m.get("graph_s"):
             comps["step_graph_replay_us"] = round(m["graph_s"] * 1e6, 2)
     if "prefill_c4" in out:
-        p = out["prefill_c4"]
-        tf = p["flops"] / (p["ms"] / 1e3) / 1e12
-        comps["prefill_T16384"] = {"us": round(p["ms"] * 1e3, 1), "TFLOP/s": round(tf, 1),
-                                   "frac_of_bf16_peak": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)}
+        comps["prefill_T16384"] = fig(out["prefill_c4"]["t"], out["prefill_c4"]["flops"], "TFLOP/s", PEAK_BF16_FLOPS,
+                                      "frac_of_bf16_peak")
     if "prefill_c2" in out:
-        p = out["prefill_c2"]
-        tf = p["flops"] / (p["ms"] / 1e3) / 1e12
-        comps["prefill_T2048"] = {"us": round(p["ms"] * 1e3, 1), "TFLOP/s": round(tf, 1),
-                                  "frac_of_bf16_peak": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)}
+        comps["prefill_T2048"] = fig(out["prefill_c2"]["t"], out["prefill_c2"]["flops"], "TFLOP/s", PEAK_BF16_FLOPS,
+                                     "frac_of_bf16_peak")
     if "prefill_masked" in out:
-        p = out["prefill_masked"]
-        tf = p["flops"] / (p["ms"] / 1e3) / 1e12
-        comps["prefill_T2048_additive_mask"] = {"us": round(p["ms"] * 1e3, 1), "TFLOP/s": round(tf, 1),
-                                                "frac_of_bf16_peak": round(tf * 1e12 / PEAK_BF16_FLOPS, 4)}
+        comps["prefill_T2048_additive_mask"] = fig(out["prefill_masked"]["t"], out["prefill_masked"]["flops"],
+                                                   "TFLOP/s", PEAK_BF16_FLOPS, "frac_of_bf16_peak")
     if "decode_c3" in out:
         d = out["decode_c3"]
-        gb = d["bytes"] / (d["ms"] / 1e3) / 1e9
-        comps["decode_64seq_U128_4096"] = {"us": round(d["ms"] * 1e3, 2), "GB/s": round(gb, 1),
-                                           "frac_of_hbm_peak": round(gb * 1e9 / PEAK_HBM, 4), "partition": d["part"]}
+        comps["decode_64seq_U128_4096"] = fig(d["t"], d["bytes"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
+        comps["decode_64seq_U128_4096"]["partition"] = d["part"]
     if "decode_step_c3" in out:
         d = out["decode_step_c3"]
-        comps["decode_only_step_64seq"] = {
-            "bytes": d["bytes"],
-            "write_then_decode_us": round(d["write_then_decode"] * 1e3, 2),
-            "fused_us": round(d["fused"] * 1e3, 2),
-            "fused_GB/s": round(d["bytes"] / (d["fused"] / 1e3) / 1e9, 1),
-            "fused_frac_of_hbm_peak": round(d["bytes"] / (d["fused"] / 1e3) / PEAK_HBM, 4)}
+        comps["decode_only_step_64seq"] = {"bytes": d["bytes"],
+                                           "write_then_decode": fig(d["write_then_decode"]),
+                                           "fused": fig(d["fused"], d["bytes"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")}
     if "rmsnorm" in out:
-        c = out["rmsnorm"]
-        gb = c["bytes"] / (c["ms"] / 1e3) / 1e9
-        comps["residual_rmsnorm_4224x1536"] = {"us": round(c["ms"] * 1e3, 2), "GB/s": round(gb, 1),
-                                               "frac_of_hbm_peak": round(gb * 1e9 / PEAK_HBM, 4)}
+        comps["residual_rmsnorm_4224x1536"] = fig(out["rmsnorm"]["t"], out["rmsnorm"]["bytes"], "GB/s", PEAK_HBM,
+                                                  "frac_of_hbm_peak")
     if "copy_blocks" in out:
-        c = out["copy_blocks"]
-        gb = c["bytes"] / (c["ms"] / 1e3) / 1e9
-        comps["copy_on_write_4096_blocks"] = {"us": round(c["ms"] * 1e3, 2), "GB/s": round(gb, 1),
-                                              "frac_of_hbm_peak": round(gb * 1e9 / PEAK_HBM, 4)}
+        comps["copy_on_write_4096_blocks"] = fig(out["copy_blocks"]["t"], out["copy_blocks"]["bytes"], "GB/s",
+                                                 PEAK_HBM, "frac_of_hbm_peak")
     res["components"] = comps
     if "value" not in res:
         res["value"] = None

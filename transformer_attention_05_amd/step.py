@@ -153,7 +153,15 @@ class MixedStep:
             return torch.cat([self.q[: self.n_prefill], self.q_dec_rot])
         return self.q
 
-    def run(self):
+    def run(self, marks=None):
+        """Enqueue one step.  ``marks``: optional dict of torch.cuda.Event
+        ("prefill0", "prefill1" on the caller's stream and "decode0",
+        "decode1" on the second stream) recorded around the chunked prefill
+        and the decode of the concurrent schedule, to time them inside the
+        step."""
+        def mark(name, stream):
+            if marks is not None:
+                marks[name].record(stream)
         if self._fused():
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)      # the step's inputs come from the caller's stream
@@ -173,10 +181,14 @@ class MixedStep:
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)      # the step's inputs come from the caller's stream
             self.write(0, self.n_prefill)    # the chunk tokens
+            mark("prefill0", main)
             self.prefill(share_cu=True)
+            mark("prefill1", main)
             with torch.cuda.stream(self.side):
                 self.write(self.n_prefill)   # the decode tokens
+                mark("decode0", self.side)
                 self.decode()
+                mark("decode1", self.side)
             main.wait_stream(self.side)
             return
         self.write()
