@@ -12,20 +12,23 @@
 // same code as the decode's fused write).  bf16 outputs are rounded to
 // nearest even.
 //
-// Workgroup = kTok tokens, 512 threads.  A q or k item is four channel pairs
-// of one row (8-byte accesses for bf16; consecutive lanes cover consecutive
-// chunks of a row).  A value item is four channels of one token; the token
-// index runs fastest, so the 16 lanes of a quarter-wave store 16 consecutive
-// tokens' elements of one channel row of the token-minor value block: one
-// contiguous 32-byte run when the tokens' slots are consecutive, instead of
-// 16 isolated 2-byte stores.
+// Workgroup = 512 threads over TOK tokens (16 at D 128, 32 at D 64).  A
+// thread owns one (token, chunk) of the rotation: chunk c is the four pairs
+// 4c .. 4c+3, i.e. channels 4c .. 4c+3 and 4c + D/2 .. +3 of a row, and the
+// thread takes that chunk of every other query/key row of its token (two
+// threads per chunk, rows of alternating parity).  It forms the four
+// (cos, sin) values itself, so threads never wait for each other: there is
+// no table in LDS and no barrier.  A value item is four channels of one
+// token; the token index runs fastest, so the 16 lanes of a quarter-wave
+// store 16 consecutive tokens' elements of one channel row of the
+// token-minor value block (one contiguous 32-byte run when the slots are
+// consecutive).
 //
-// The kernel is a chain of memory round trips, and every workgroup of a
-// launch is resident at once, so its time is the length of that chain.  It
-// has two: the slots and positions, then all of a thread's q, k and v data
-// (up to kItems q/k items per thread and pass), loaded while the angles are
-// computed.  (The query rotates in place, so the compiler could not move a
-// later item's load above an earlier item's store by itself.)
+// Every workgroup of a launch is resident at once, so the kernel takes as
+// long as one thread's chain of memory round trips.  There is one: the
+// position, slot, frequencies and all of a thread's q, k and v data are
+// loaded together (unconditional loads from clamped indexes), then the
+// angles are formed, the rows rotated and everything stored.
 
 #include <math.h>
 
@@ -36,10 +39,9 @@ namespace mi_attn {
 
 namespace {
 
-constexpr int kTok = 16;
 constexpr int kThreads = 512;
-constexpr int kItems = 8;   // q/k items held per thread and pass
-constexpr int kVItems = 2;  // value items held per thread and pass
+constexpr int kRowsPerPass = 8;  // q/k rows held per thread and pass
+constexpr int kVItems = 2;       // value items held per thread and pass
 
 template <typename T>
 struct Vec4;
@@ -55,6 +57,7 @@ struct Vec4<__bf16> {
   static __device__ __forceinline__ void store(__bf16* p, f32x4 v) {
     *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
   }
+  static __device__ __forceinline__ void store_raw(__bf16* p, raw w) { *reinterpret_cast<u32x2*>(p) = w; }
 };
 template <>
 struct Vec4<float> {
@@ -62,154 +65,146 @@ struct Vec4<float> {
   static __device__ __forceinline__ raw load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
   static __device__ __forceinline__ f32x4 widen(raw v) { return v; }
   static __device__ __forceinline__ void store(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+  static __device__ __forceinline__ void store_raw(float* p, raw v) { *reinterpret_cast<f32x4*>(p) = v; }
 };
 
 template <int D, typename T>
 __global__ __launch_bounds__(kThreads) void rope_write_kernel(const RopeWriteArgs a) {
   constexpr int H2 = D / 2;
-  constexpr int CPR = H2 / 4;  // four-pair chunks per row
-  __shared__ double theta[H2];
-  __shared__ float cs[kTok][H2], sn[kTok][H2];
-  __shared__ int32_t slot_sm[kTok], pos_sm[kTok];
-  const int n0 = blockIdx.x * kTok;
+  constexpr int CPR = H2 / 4;         // four-pair chunks per row
+  constexpr int TPT = 2 * CPR;        // threads per token
+  constexpr int TOK = kThreads / TPT;  // tokens per workgroup
   const int tid = threadIdx.x;
-  const int ntok = min(kTok, a.num_tokens - n0);
+  const int n0 = blockIdx.x * TOK;
+  const int last = a.num_tokens - 1;
   const bool rot = a.rope != 0;
 
-  // round trip 1: slots, positions and frequencies, all in flight at once
-  // (unconditional loads from clamped indexes: a load under a lane
-  // condition becomes a branch the compiler waits behind)
-  const int tt = min(tid, ntok - 1);
-  int32_t sl = a.slot_mapping[n0 + tt];
-  const int32_t ps = a.positions[n0 + tt];
-  const double th = a.freqs.theta[tid & (H2 - 1)];
-  if (tid < kTok) {
-    if (tid >= ntok || sl >= a.num_blocks * kBlockSize) sl = -1;  // outside the pool: skipped
-    slot_sm[tid] = sl;
-    pos_sm[tid] = tid < ntok ? ps : 0;
-  }
-  if (rot && tid < H2) theta[tid] = th;
-  __syncthreads();
-
+  // ---- the rotation part: token t, chunk c, row parity h
+  const int t = tid / TPT;
+  const int c = (tid / 2) % CPR;
+  const int h = tid & 1;
+  const int n = min(n0 + t, last);       // clamped: loads stay in range
+  const bool live = n0 + t <= last;
+  // rows 0 .. hq-1 are the query heads (rotated in place), hq .. hq+hkv-1
+  // the key heads (rotated into the cache); without rotation or without q
+  // only the keys are copied
+  const int rlo = (a.q != nullptr && rot) ? 0 : a.hq;
+  const int rows = a.hq + a.hkv;
+  const int32_t pos = a.positions[n];
+  int32_t slot = a.slot_mapping[n];
+  double th[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) th[e] = a.freqs.theta[4 * c + e];
   T* q = static_cast<T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   T* kc = static_cast<T*>(a.k_cache);
   const T* v = static_cast<const T*>(a.v);
   T* vc = static_cast<T*>(a.v_cache);
-  const int rows = a.hq + a.hkv;
-  const int total = ntok * rows * CPR;
-  const int vtotal = a.hkv * (D / 4) * kTok;
 
-  // one q/k item: source, destination (null: skipped) and rotation index
-  struct Item {
-    typename Vec4<T>::raw x1, x2;
-    T* dst;
-    int t, i0;
+  // value items of this pass: token tv (fastest), kv head gv, channels 4 dv ..
+  const int vtotal = TOK * a.hkv * (D / 4);
+  auto v_item = [&](int w, int& tv, int& gv, int& dv) {
+    tv = w % TOK;
+    dv = (w / TOK) % (D / 4);
+    gv = w / (TOK * (D / 4));
   };
-  auto load_item = [&](int w, Item& it) {
-    it.dst = nullptr;
-    it.t = 0;
-    it.i0 = 0;
-    if (w >= total) return;
-    const int t = w / (rows * CPR);
-    const int rr = (w / CPR) % rows;
-    const int i0 = 4 * (w % CPR);
-    const int n = n0 + t;
-    const bool is_q = rr < a.hq;
-    if (is_q && (q == nullptr || !rot)) return;
-    const int32_t sl = slot_sm[t];
-    if (!is_q && sl < 0) return;
-    const T* src = is_q ? q + ((int64_t)n * a.hq + rr) * D : k + ((int64_t)n * a.hkv + (rr - a.hq)) * D;
-    it.x1 = Vec4<T>::load(src + i0);
-    it.x2 = Vec4<T>::load(src + i0 + H2);
-    if (is_q) {
-      it.dst = q + ((int64_t)n * a.hq + rr) * D + i0;
-    } else {
-      const int64_t blk = sl / kBlockSize;
-      it.dst = kc + ((blk * a.hkv + (rr - a.hq)) * kBlockSize + sl % kBlockSize) * D + i0;
-    }
-    it.t = t;
-    it.i0 = i0;
-  };
-  auto store_item = [&](const Item& it) {
-    if (it.dst == nullptr) return;
-    const f32x4 x1 = Vec4<T>::widen(it.x1), x2 = Vec4<T>::widen(it.x2);
-    f32x4 y1 = x1, y2 = x2;
-    if (rot) {
+
+  for (int r0 = rlo + h; r0 < rows || r0 == rlo + h; r0 += 2 * kRowsPerPass) {
+    // loads of this pass: q/k chunks of up to kRowsPerPass rows (row index
+    // clamped into range, the store decides), and, in the first pass, the
+    // value items
+    typename Vec4<T>::raw x1[kRowsPerPass], x2[kRowsPerPass];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float r1, r2;
-        rope_rotate(x1[e], x2[e], cs[it.t][it.i0 + e], sn[it.t][it.i0 + e], r1, r2);
-        y1[e] = r1;
-        y2[e] = r2;
+    for (int u = 0; u < kRowsPerPass; ++u) {
+      const int r = min(r0 + 2 * u, rows - 1);
+      const T* src = r < a.hq ? q + ((int64_t)n * a.hq + r) * D : k + ((int64_t)n * a.hkv + (r - a.hq)) * D;
+      x1[u] = Vec4<T>::load(src + 4 * c);
+      x2[u] = Vec4<T>::load(src + 4 * c + H2);
+    }
+    const bool first = r0 == rlo + h;
+    typename Vec4<T>::raw vx[kVItems];
+    int32_t vslot[kVItems];
+    if (first) {
+#pragma unroll
+      for (int u = 0; u < kVItems; ++u) {
+        int tv, gv, dv;
+        v_item(min(tid + u * kThreads, vtotal - 1), tv, gv, dv);
+        const int nv = min(n0 + tv, last);
+        vslot[u] = a.slot_mapping[nv];
+        vx[u] = Vec4<T>::load(v + ((int64_t)nv * a.hkv + gv) * D + 4 * dv);
       }
     }
-    Vec4<T>::store(it.dst, y1);
-    Vec4<T>::store(it.dst + H2, y2);
-  };
-  // one value item: four channels of one token
-  struct VItem {
-    typename Vec4<T>::raw x;
-    T* dst;
-  };
-  auto load_vitem = [&](int w, VItem& it) {
-    it.dst = nullptr;
-    if (w >= vtotal) return;
-    const int t = w % kTok;
-    const int c = (w / kTok) % (D / 4);
-    const int g = w / (kTok * (D / 4));
-    if (t >= ntok) return;
-    const int32_t sl = slot_sm[t];
-    if (sl < 0) return;
-    it.x = Vec4<T>::load(v + ((int64_t)(n0 + t) * a.hkv + g) * D + 4 * c);
-    const int64_t blk = sl / kBlockSize;
-    it.dst = vc + ((blk * a.hkv + g) * D + 4 * c) * kBlockSize + sl % kBlockSize;
-  };
-  auto store_vitem = [&](const VItem& it) {
-    if (it.dst == nullptr) return;
-    const f32x4 x = Vec4<T>::widen(it.x);
+    // angles of this thread's four pairs (formed while the data arrives)
+    float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
+    if (rot) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) it.dst[e * kBlockSize] = static_cast<T>(x[e]);
-  };
-
-  // round trip 2: the first pass of data, in flight while the angles are formed
-  Item items[kItems];
-  VItem vitems[kVItems];
-#pragma unroll
-  for (int u = 0; u < kItems; ++u) load_item(tid + u * kThreads, items[u]);
-#pragma unroll
-  for (int u = 0; u < kVItems; ++u) load_vitem(tid + u * kThreads, vitems[u]);
-  if (rot) {
-    for (int e = tid; e < ntok * H2; e += kThreads) {
-      const int t = e / H2, i = e % H2;
-      rope_cos_sin(pos_sm[t], theta[i], cs[t][i], sn[t][i]);
+      for (int e = 0; e < 4; ++e) rope_cos_sin(pos, th[e], cs[e], sn[e]);
     }
-  }
-  __syncthreads();
+    if (slot >= a.num_blocks * kBlockSize) slot = -1;  // outside the pool: skipped
 #pragma unroll
-  for (int u = 0; u < kItems; ++u) store_item(items[u]);
+    for (int u = 0; u < kRowsPerPass; ++u) {
+      const int r = r0 + 2 * u;
+      if (!live || r >= rows) continue;
+      T* dst;
+      if (r < a.hq) {
+        dst = q + ((int64_t)n * a.hq + r) * D + 4 * c;
+      } else {
+        if (slot < 0) continue;
+        dst = kc + (((int64_t)(slot / kBlockSize) * a.hkv + (r - a.hq)) * kBlockSize + slot % kBlockSize) * D + 4 * c;
+      }
+      if (rot) {
+        const f32x4 y1 = Vec4<T>::widen(x1[u]), y2 = Vec4<T>::widen(x2[u]);
+        f32x4 z1, z2;
 #pragma unroll
-  for (int u = 0; u < kVItems; ++u) store_vitem(vitems[u]);
-
-  // further passes (more heads than one pass holds)
-  for (int w0 = tid + kItems * kThreads; w0 < total; w0 += kItems * kThreads) {
+        for (int e = 0; e < 4; ++e) {
+          float o1, o2;
+          rope_rotate(y1[e], y2[e], cs[e], sn[e], o1, o2);
+          z1[e] = o1;
+          z2[e] = o2;
+        }
+        Vec4<T>::store(dst, z1);
+        Vec4<T>::store(dst + H2, z2);
+      } else {
+        Vec4<T>::store_raw(dst, x1[u]);
+        Vec4<T>::store_raw(dst + H2, x2[u]);
+      }
+    }
+    if (first) {
 #pragma unroll
-    for (int u = 0; u < kItems; ++u) load_item(w0 + u * kThreads, items[u]);
+      for (int u = 0; u < kVItems; ++u) {
+        const int w = tid + u * kThreads;
+        int tv, gv, dv;
+        v_item(w, tv, gv, dv);
+        const int32_t sl = vslot[u];
+        if (w >= vtotal || n0 + tv > last || sl < 0 || sl >= a.num_blocks * kBlockSize) continue;
+        const f32x4 x = Vec4<T>::widen(vx[u]);
+        T* dst = vc + ((int64_t)(sl / kBlockSize) * a.hkv + gv) * D * kBlockSize + (4 * dv) * kBlockSize + sl % kBlockSize;
 #pragma unroll
-    for (int u = 0; u < kItems; ++u) store_item(items[u]);
-  }
-  for (int w0 = tid + kVItems * kThreads; w0 < vtotal; w0 += kVItems * kThreads) {
+        for (int e = 0; e < 4; ++e) dst[e * kBlockSize] = static_cast<T>(x[e]);
+      }
+      // further value passes (more kv heads than one pass holds)
+      for (int w0 = tid + kVItems * kThreads; w0 < vtotal; w0 += kThreads) {
+        int tv, gv, dv;
+        v_item(w0, tv, gv, dv);
+        const int nv = n0 + tv;
+        if (nv > last) continue;
+        const int32_t sl = a.slot_mapping[nv];
+        if (sl < 0 || sl >= a.num_blocks * kBlockSize) continue;
+        const f32x4 x = Vec4<T>::widen(Vec4<T>::load(v + ((int64_t)nv * a.hkv + gv) * D + 4 * dv));
+        T* dst = vc + ((int64_t)(sl / kBlockSize) * a.hkv + gv) * D * kBlockSize + (4 * dv) * kBlockSize + sl % kBlockSize;
 #pragma unroll
-    for (int u = 0; u < kVItems; ++u) load_vitem(w0 + u * kThreads, vitems[u]);
-#pragma unroll
-    for (int u = 0; u < kVItems; ++u) store_vitem(vitems[u]);
+        for (int e = 0; e < 4; ++e) dst[e * kBlockSize] = static_cast<T>(x[e]);
+      }
+    }
+    if (r0 + 2 * kRowsPerPass >= rows) break;
   }
 }
 
 }  // namespace
 
 hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hipStream_t s) {
-  dim3 grid((a.num_tokens + kTok - 1) / kTok), block(kThreads);
+  const int tok = kThreads / (head_dim / 4);  // tokens per workgroup (16 at D 128, 32 at D 64)
+  dim3 grid((a.num_tokens + tok - 1) / tok), block(kThreads);
   if (bf16) {
     if (head_dim == 128) hipLaunchKernelGGL((rope_write_kernel<128, __bf16>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((rope_write_kernel<64, __bf16>), grid, block, 0, s, a);
