@@ -22,9 +22,11 @@
  *   - Tensors are token-major with the head dimension contiguous.  Strides
  *     are in elements.  Device pointers must be 16-byte aligned and every
  *     stride a multiple of 8 elements (bf16) or 4 elements (f32).
- *   - Supported: head_dim 64 or 128; dtype F32 or BF16 (paged kernels: BF16);
- *     block_size 16; num_q_heads a multiple of num_kv_heads.  Anything else
- *     returns ATTN_E_UNSUPPORTED.
+ *   - Supported: head_dim 64 or 128; dtype F32 or BF16 (attn_decode_paged_rope:
+ *     BF16 only); block_size 16; num_q_heads a multiple of num_kv_heads.
+ *     Anything else returns ATTN_E_UNSUPPORTED.  BF16 runs on the matrix
+ *     cores with fp32 accumulation; F32 runs full-precision VALU kernels
+ *     (for parity work, not a performance path).
  *   - Paged cache layout (one pool per tensor):
  *       k_cache [num_blocks][num_kv_heads][16][head_dim]   (token-major)
  *       v_cache [num_blocks][num_kv_heads][head_dim][16]   (token-minor)
@@ -139,9 +141,9 @@ ATTN_API int attn_prefill_masked(const void* q, const void* k, const void* v, vo
  * sequence s lives in physical block block_table[s][t / 16] at offset t % 16;
  * K[t+1] is not assumed to follow K[t].
  *
- *   q            device bf16 [total_q][num_q_heads][head_dim], sequences packed
+ *   q            device [total_q][num_q_heads][head_dim], sequences packed
  *   k_cache,
- *   v_cache      device bf16 paged pools (layout in the header comment)
+ *   v_cache      device paged pools (layout in the header comment), q's dtype
  *   block_table  device int32 [num_seqs][max_blocks_per_seq]; entries past a
  *                sequence's last block are never read
  *   cu_seqlens_q device int32 [num_seqs + 1]; sequence s owns q rows
@@ -157,7 +159,8 @@ ATTN_API int attn_prefill_masked(const void* q, const void* k, const void* v, vo
  *                longer context is still computed whole, by longer shares.
  *   workspace    optional device scratch of
  *                attn_prefill_paged_workspace_size(...) bytes (same meaning
- *                and rules as attn_prefill's).
+ *                and rules as attn_prefill's).  F32 runs one pass per query
+ *                tile and ignores the workspace and the flags below.
  * ---------------------------------------------------------------------- */
 ATTN_API size_t attn_prefill_paged_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_seqlen_q,
                                          int32_t max_context_len, int32_t num_q_heads,
@@ -237,14 +240,16 @@ ATTN_API int attn_prefill_paged_masked(const void* q, const void* k_cache, const
  * the partitions exactly (each rescaled by exp(m_p - max_p m_p)).  A sequence
  * with one partition needs no combination.  One kernel launch per call.
  *
- *   q            device bf16 [num_seqs][num_q_heads][head_dim]
+ *   q            device [num_seqs][num_q_heads][head_dim] (BF16 or F32; the
+ *                caches and o share its dtype)
  *   block_table  device int32 [num_seqs][max_blocks_per_seq]; entries past
  *                a sequence's last block (within its row) may be read, and
  *                are never used
  *   context_lens device int32 [num_seqs], 1 .. max_context_len (the new
  *                token included)
- *   o            device bf16 [num_seqs][num_q_heads][head_dim], written
- *   partition_size: 0 = automatic, else a multiple of 128, at most 1024.
+ *   o            device [num_seqs][num_q_heads][head_dim], written
+ *   partition_size: 0 = automatic; else BF16: a multiple of 128, at most
+ *                1024; F32: a multiple of 16, at most 65536.
  *   plan         optional device int32 [plan_items][2]: the (sequence,
  *                partition) pairs that attn_decode_paged_plan lists for the
  *                same context lengths, max_context_len, num_kv_heads and
@@ -341,7 +346,8 @@ ATTN_API int attn_decode_paged_rope(void* q_rot_out, const void* q, const void* 
 /* Host-side plan of a decode launch (host memory only, no HIP call): the
  * (sequence, partition) pairs of the sequences' contexts, longest sequences
  * first, partitions in order, with the partition size attn_decode_paged
- * uses for the same arguments.  context_lens: host int32 [num_seqs] (clamped
+ * uses for the same arguments (partition_size 0, or a multiple of 16 up to
+ * 65536; the decode call itself checks its dtype's rule).  context_lens: host int32 [num_seqs] (clamped
  * to max_context_len).  Returns the number of pairs; writes them to items
  * (int32 [count][2]) only when items is non-NULL and capacity (in pairs)
  * holds them all.  Negative attn_status on bad arguments. */

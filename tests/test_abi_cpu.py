@@ -188,9 +188,12 @@ def decode(lib, **kw):
     (dict(q=None), ATTN_E_INVALID),
     (dict(bt=None), ATTN_E_INVALID),
     (dict(bs=32), ATTN_E_UNSUPPORTED),
-    (dict(dtype=ATTN_F32), ATTN_E_UNSUPPORTED),
+    (dict(dtype=7), ATTN_E_UNSUPPORTED),
     (dict(maxb=7), ATTN_E_INVALID),             # 128 tokens need 8 blocks
     (dict(part=100), ATTN_E_INVALID),
+    (dict(part=48), ATTN_E_INVALID),            # bf16 partitions: multiples of 128
+    (dict(part=40, dtype=ATTN_F32), ATTN_E_INVALID),      # fp32 partitions: multiples of 16
+    (dict(part=65536 + 16, dtype=ATTN_F32), ATTN_E_INVALID),
     (dict(part=-128), ATTN_E_INVALID),
     (dict(part=2048), ATTN_E_INVALID),
     (dict(maxctx=0), ATTN_E_INVALID),
@@ -205,6 +208,16 @@ def decode(lib, **kw):
 ])
 def test_decode_rejects(lib, kw, status):
     assert decode(lib, **kw) == status
+
+
+def test_decode_f32_partition_sizes_accepted_by_the_plan():
+    """fp32 decodes take any multiple of 16 as partition size; the host plan
+    lists their partitions (bf16 launches still check multiples of 128)."""
+    lens = np.array([1, 16, 17, 100], np.int32)
+    items = mi.attn_decode_paged_plan(lens, 2, 100, 16)
+    assert len(items) == 1 + 1 + 2 + 7
+    with pytest.raises(mi.AttnError):
+        mi.attn_decode_paged_plan(lens, 2, 100, 24)
 
 
 def decode_rope(lib, **kw):
@@ -310,7 +323,7 @@ def test_decode_plan():
     # lengths beyond max_context_len are clamped, as the kernel clamps them
     assert len(mi.attn_decode_paged_plan(np.array([5000], np.int32), 2, 1024, 512)) == 2
     with pytest.raises(mi.AttnError):
-        mi.attn_decode_paged_plan(lens, 2, 3000, 100)   # not a multiple of 128
+        mi.attn_decode_paged_plan(lens, 2, 3000, 100)   # not a multiple of 16
 
 
 def test_paged_prefill_and_write_reject(lib):
@@ -319,7 +332,7 @@ def test_paged_prefill_and_write_reject(lib):
         a.update(kw)
         return lib.attn_prefill_paged(P, P, P, a["bt"], 8, P, P, P, 2, a["tot"], a["maxq"], a["maxctx"], 12, 2,
                                       128, 16, 100, 0.0, 1, a["dtype"], a["ws"], a["wsb"], None)
-    assert paged(dtype=ATTN_F32) == ATTN_E_UNSUPPORTED
+    assert paged(dtype=7) == ATTN_E_UNSUPPORTED
     assert paged(bt=None) == ATTN_E_INVALID
     assert paged(tot=50) == ATTN_E_INVALID       # max_seqlen_q > total_q
     assert paged(maxctx=-1) == ATTN_E_INVALID
@@ -338,7 +351,7 @@ def test_paged_prefill_and_write_reject(lib):
                                          a["dtype"], flags, a["ws"], a["wsb"], None)
     assert paged_ex(2) == ATTN_E_INVALID
     assert paged_ex(-1) == ATTN_E_INVALID
-    assert paged_ex(mi.ATTN_PREFILL_SHARE_CU, dtype=ATTN_F32) == ATTN_E_UNSUPPORTED
+    assert paged_ex(mi.ATTN_PREFILL_SHARE_CU, dtype=7) == ATTN_E_UNSUPPORTED
     # (the flagged plan fits one workgroup per CU, so it splits into no more
     # shares than the default: a workspace far below either is refused)
     assert paged_ex(mi.ATTN_PREFILL_SHARE_CU, ws=P, wsb=256) == ATTN_E_NOMEM

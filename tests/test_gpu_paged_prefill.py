@@ -16,7 +16,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 
-def paged_setup(seed, cached, new, hq=12, hkv=2, d=128, order="random"):
+def paged_setup(seed, cached, new, hq=12, hkv=2, d=128, order="random", dtype=torch.bfloat16):
     """Sequences with `cached` + `new` tokens laid out in a paged pool."""
     g = rng(seed)
     total = np.asarray(cached) + np.asarray(new)
@@ -29,11 +29,11 @@ def paged_setup(seed, cached, new, hq=12, hkv=2, d=128, order="random"):
     for s, n in enumerate(nblk):
         bt[s, :n] = perm[p:p + n]
         p += n
-    ks = [normal(g, (int(t), hkv, d), torch.bfloat16) for t in total]
-    vs = [normal(g, (int(t), hkv, d), torch.bfloat16) for t in total]
-    qs = [normal(g, (int(n), hq, d), torch.bfloat16) for n in new]
-    kc = torch.full((nb, hkv, BLOCK_SIZE, d), float("nan"), dtype=torch.bfloat16, device=DEV)
-    vc = torch.full((nb, hkv, d, BLOCK_SIZE), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ks = [normal(g, (int(t), hkv, d), dtype) for t in total]
+    vs = [normal(g, (int(t), hkv, d), dtype) for t in total]
+    qs = [normal(g, (int(n), hq, d), dtype) for n in new]
+    kc = torch.full((nb, hkv, BLOCK_SIZE, d), float("nan"), dtype=dtype, device=DEV)
+    vc = torch.full((nb, hkv, d, BLOCK_SIZE), float("nan"), dtype=dtype, device=DEV)
     for s in range(len(total)):
         scatter_to_pool(kc, vc, bt[s], ks[s], vs[s])
     return qs, ks, vs, bt, kc, vc, total

@@ -335,7 +335,9 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, context_l
     if o is None:
         o = torch.empty_like(q)
     bound = int(max_context_len) if max_context_len else block_table.shape[1] * bs
-    need = attn_prefill_paged_workspace_size(s, total_q, int(max_seqlen_q), bound, hq, hkv, d)
+    # (the fp32 kernel runs one pass and takes no workspace)
+    need = 0 if q.dtype == torch.float32 else attn_prefill_paged_workspace_size(s, total_q, int(max_seqlen_q), bound,
+                                                                                  hq, hkv, d)
     ws_ptr, ws_bytes = _workspace(workspace, need, q.device)
     args = (_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_table, "block_table"),
             block_table.shape[1], _dev(cu_seqlens_q, "cu_seqlens_q"), _dev(context_lens, "context_lens"),

@@ -267,7 +267,7 @@ int prefill_common(const char* fn, const void* q, const void* k, const void* v, 
   const int64_t nwg = (int64_t)a.num_m_tiles * num_q_heads * batch;
   if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
   a.num_wg = (uint32_t)nwg;
-  return launched(launch_prefill_f32(a, head_dim, s), fn);
+  return launched(launch_prefill_f32(a, head_dim, false, s), fn);
 }
 }  // namespace
 
@@ -338,7 +338,7 @@ int prefill_paged_common(const char* fn, const PagedMask* pm, const void* q, con
   int st;
   if ((st = check_heads(num_q_heads, num_kv_heads, fn)) != ATTN_OK) return st;
   if ((st = check_head_dim(head_dim, fn)) != ATTN_OK) return st;
-  if (dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "%s: paged kernels take bf16 only", fn);
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_E_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
   if (block_size != kBlockSizeHost) return fail(ATTN_E_UNSUPPORTED, "%s: block_size %d (supported: 16)", fn, block_size);
   float scale_log2;
   if ((st = check_scale(scale, head_dim, &scale_log2, fn)) != ATTN_OK) return st;
@@ -364,6 +364,26 @@ int prefill_paged_common(const char* fn, const PagedMask* pm, const void* q, con
   a.hq = num_q_heads; a.hkv = num_kv_heads; a.group = num_q_heads / num_kv_heads;
   a.causal = causal ? 1 : 0;
   a.scale_log2 = scale_log2;
+  if (dtype == ATTN_F32) {
+    // fp32: the VALU kernel, one pass per 64-query tile and head (no
+    // split, no flags; the workspace is not used)
+    if (pm != nullptr) {
+      a.mask = pm->mask;
+      a.ms_q = pm->strides[0]; a.ms_h = pm->strides[1]; a.ms_b = 0;
+      a.mask_keys = pm->keys;
+      a.mask_scale = (float)((double)kLog2eHost / (double)scale_log2);
+    }
+    a.num_splits = 1;
+    a.num_m_tiles = ceil_div(max_seqlen_q, kPrefillF32BlockM);
+    const int64_t nwg = (int64_t)a.num_m_tiles * num_q_heads * num_seqs;
+    if (nwg > INT32_MAX) return fail(ATTN_E_UNSUPPORTED, "%s: problem too large for one launch", fn);
+    a.num_wg = (uint32_t)nwg;
+    a.block_table = block_table; a.bt_stride = max_blocks_per_seq;
+    a.cu_seqlens_q = cu_seqlens_q; a.context_lens = context_lens;
+    a.num_blocks = num_blocks;
+    a.total_q = total_q;
+    return launched(launch_prefill_f32(a, head_dim, true, reinterpret_cast<hipStream_t>(stream)), fn);
+  }
   // the plan's key bound: the caller's, else what the block table can hold
   const int64_t ctx_bound = max_context_len > 0 ? max_context_len : (int64_t)max_blocks_per_seq * kBlockSizeHost;
   PrefillPlan p = plan_prefill(max_seqlen_q, ctx_bound, num_q_heads, a.group, num_seqs, head_dim, true,
@@ -443,6 +463,7 @@ extern "C" int32_t attn_decode_paged_auto_partition(int32_t num_seqs, int32_t nu
 }
 
 namespace {
+constexpr int32_t kMaxF32Partition = 65536;
 // Decode workspace, used only when a context can span several partitions:
 // the arrival counters (one int32 per sequence and kv head slice, zero
 // between calls), then the partial outputs, then the (m, l) pairs.
@@ -483,8 +504,8 @@ extern "C" int64_t attn_decode_paged_plan(const int32_t* context_lens, int32_t n
   static const char* fn = "attn_decode_paged_plan";
   if (num_seqs < 0 || num_kv_heads < 1 || max_context_len < 1 || capacity < 0 || (num_seqs > 0 && !context_lens))
     return fail(ATTN_E_INVALID, "%s: bad argument", fn);
-  if (partition_size < 0 || partition_size % 128 != 0 || partition_size > 1024)
-    return fail(ATTN_E_INVALID, "%s: partition_size must be 0 or a multiple of 128 up to 1024", fn);
+  if (partition_size < 0 || partition_size % 16 != 0 || partition_size > kMaxF32Partition)
+    return fail(ATTN_E_INVALID, "%s: partition_size must be 0 or a multiple of 16 up to %d", fn, kMaxF32Partition);
   const int32_t part = partition_size > 0 ? partition_size
                                           : attn_decode_paged_auto_partition(num_seqs, num_kv_heads, max_context_len);
   // the kernel's own view of a context: clamped to max_context_len
@@ -541,13 +562,18 @@ int decode_common(const char* fn, const DecodeWrite* w, const void* q, const voi
   int st;
   if ((st = check_heads(num_q_heads, num_kv_heads, fn)) != ATTN_OK) return st;
   if ((st = check_head_dim(head_dim, fn)) != ATTN_OK) return st;
-  if (dtype != ATTN_BF16) return fail(ATTN_E_UNSUPPORTED, "%s: paged kernels take bf16 only", fn);
+  if (dtype != ATTN_BF16 && dtype != ATTN_F32) return fail(ATTN_E_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  if (dtype == ATTN_F32 && w != nullptr)
+    return fail(ATTN_E_UNSUPPORTED, "%s: the decode with the new token's write fused takes bf16 only", fn);
   if (block_size != kBlockSizeHost) return fail(ATTN_E_UNSUPPORTED, "%s: block_size %d (supported: 16)", fn, block_size);
   if (max_blocks_per_seq < ceil_div(max_context_len, kBlockSizeHost))
     return fail(ATTN_E_INVALID, "%s: max_blocks_per_seq %d cannot hold max_context_len %d", fn,
                 max_blocks_per_seq, max_context_len);
-  if (partition_size < 0 || partition_size % 128 != 0 || partition_size > 1024)
-    return fail(ATTN_E_INVALID, "%s: partition_size must be 0 or a multiple of 128 up to 1024", fn);
+  if (dtype == ATTN_BF16 && (partition_size < 0 || partition_size % 128 != 0 || partition_size > 1024))
+    return fail(ATTN_E_INVALID, "%s: bf16 partition_size must be 0 or a multiple of 128 up to 1024", fn);
+  if (dtype == ATTN_F32 && (partition_size < 0 || partition_size % 16 != 0 || partition_size > kMaxF32Partition))
+    return fail(ATTN_E_INVALID, "%s: fp32 partition_size must be 0 or a multiple of 16 up to %d", fn,
+                kMaxF32Partition);
   float scale_log2;
   if ((st = check_scale(scale, head_dim, &scale_log2, fn)) != ATTN_OK) return st;
   const void* ptrs[] = {q, k_cache, v_cache, o};
@@ -605,6 +631,7 @@ int decode_common(const char* fn, const DecodeWrite* w, const void* q, const voi
     a.rope = w->rope_base > 0.f;
     if (a.rope) a.freqs = rope_freqs(w->rope_base, head_dim);
   }
+  if (dtype == ATTN_F32) return launched(launch_decode_f32(a, head_dim, reinterpret_cast<hipStream_t>(stream)), fn);
   return launched(launch_decode(a, head_dim, w != nullptr, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 }  // namespace

@@ -67,7 +67,7 @@ __device__ __forceinline__ void load_block(BlockRegs<D>& r, const __bf16* kb, co
 // O = sum_p f_p O_p / sum_p f_p l_p with f_p = exp(m_p - max m), taken as one
 // online pass over batches of MK partitions whose loads are all in flight at
 // once (the merge is bound by load latency).  Thread = (head, four channels).
-template <int D>
+template <int D, typename TO = __bf16>
 __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int head0, int nh, int nparts,
                                                int tid, int nthreads) {
   constexpr int CG = D / 4;  // four-channel groups per head
@@ -112,8 +112,12 @@ __device__ __forceinline__ void merge_partials(const DecodeArgs& a, int s, int h
       mx = mn;
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + row * D + 4 * cg) =
-        u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    if constexpr (sizeof(TO) == 4) {
+      *reinterpret_cast<f32x4*>(static_cast<float*>(a.o) + row * D + 4 * cg) = acc * inv;
+    } else {
+      *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.o) + row * D + 4 * cg) =
+          u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+    }
   }
 }
 
@@ -411,6 +415,141 @@ __global__ __launch_bounds__(64 * DW) void decode_planned_kernel(const DecodeArg
 }
 
 // ---------------------------------------------------------------------------
+// fp32 decode (full-precision parity runs): the same partitions, workspace
+// and in-launch merge as the bf16 kernel, on the VALU.  Workgroup = 256
+// threads for one (partition, kv head x 16-head slice, sequence); thread
+// (h, x) = (tid / 16, tid % 16) forms the score of head h against token x
+// of each 16-token block and accumulates output channels x*D/16 .. +D/16-1
+// of head h.  The weights of a block pass between the 16 threads of a head
+// by lane shuffles.  K and V blocks are staged through LDS, the next
+// block's loads in flight while the current one is consumed.  Partitions
+// may be any multiple of 16 tokens.
+template <int D>
+__global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
+  constexpr int DPT = D / 16;        // output channels per thread
+  constexpr int KV4 = 16 * D / 4;    // float4 per K (or V) block of one kv head
+  constexpr int LPT = KV4 / 256;     // float4 per thread and block, each of K and V
+  __shared__ float qs[16][D];
+  __shared__ float ks[16][D + 1];
+  __shared__ float vs[D][17];
+  __shared__ int flag;
+  int p, yy, s;
+  if (a.plan != nullptr) {
+    const int Y = a.hkv * a.head_groups;
+    yy = (int)(blockIdx.x % (uint32_t)Y);
+    const int it = (int)(blockIdx.x / (uint32_t)Y);
+    s = a.plan[2 * it];
+    p = a.plan[2 * it + 1];
+    if (s < 0 || s >= a.num_seqs || p < 0 || p >= a.max_parts) return;
+  } else {
+    p = blockIdx.x;
+    yy = blockIdx.y;
+    s = blockIdx.z;
+  }
+  const int kvh = yy / a.head_groups;
+  const int hgi = yy % a.head_groups;
+  const int head0 = kvh * a.group + hgi * 16;
+  const int nh = min(16, a.group - hgi * 16);
+  const int ctx = min(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize));
+  const int nparts = (ctx + a.part_size - 1) / a.part_size;
+  if (p >= nparts) return;  // uniform
+  const int tok_begin = p * a.part_size;
+  const int tok_end = min(ctx, tok_begin + a.part_size);
+  const int tid = threadIdx.x;
+  const int h = tid >> 4, x = tid & 15;
+  const float* q = static_cast<const float*>(a.q);
+  const float* kc = static_cast<const float*>(a.k_cache);
+  const float* vc = static_cast<const float*>(a.v_cache);
+  const int32_t* bt = a.block_table + (int64_t)s * a.bt_stride;
+  for (int e = tid; e < 16 * D; e += 256) {
+    const int hh = e / D, d = e % D;
+    qs[hh][d] = hh < nh ? q[((int64_t)s * a.hq + head0 + hh) * D + d] : 0.f;
+  }
+  // this thread's share of a block: float4 e = tid + 256 i of the K block
+  // (row e / (D/4)) and of the token-minor V block (channel e / 4, tokens
+  // 4 (e % 4) .. +3)
+  f32x4 kr[LPT], vr[LPT];
+  auto load_block = [&](int blk) {
+    const int32_t phys = safe_block(bt[blk], a.num_blocks);
+    const int64_t base = ((int64_t)phys * a.hkv + kvh) * (kBlockSize * D);
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int e = tid + 256 * i;
+      kr[i] = *reinterpret_cast<const f32x4*>(kc + base + 4 * e);
+      vr[i] = *reinterpret_cast<const f32x4*>(vc + base + 4 * e);
+    }
+  };
+  const float c2 = a.scale_log2;
+  float m_run = -INFINITY, l_run = 0.f;
+  float o[DPT];
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) o[j] = 0.f;
+  const int b0 = tok_begin >> 4, b1 = (tok_end + 15) >> 4;
+  load_block(b0);
+  for (int blk = b0; blk < b1; ++blk) {
+    __syncthreads();  // the previous block is consumed
+    const int t0 = blk * kBlockSize;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int e = tid + 256 * i;
+      const int row = e / (D / 4), c4 = e % (D / 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ks[row][4 * c4 + j] = kr[i][j];
+      const int d = e / 4, tq = 4 * (e % 4);
+      // tokens past the partition hold other data or arbitrary bits (0 * NaN
+      // is NaN): zero them
+#pragma unroll
+      for (int j = 0; j < 4; ++j) vs[d][tq + j] = t0 + tq + j < tok_end ? vr[i][j] : 0.f;
+    }
+    __syncthreads();
+    if (blk + 1 < b1) load_block(blk + 1);
+    // score of head h against token x (raw units), masked past the partition
+    float sc = 0.f;
+#pragma unroll 16
+    for (int d = 0; d < D; ++d) sc = fmaf(qs[h][d], ks[x][d], sc);
+    if (h >= nh || t0 + x >= tok_end) sc = -INFINITY;
+    float tmax = sc;
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, m, 16));
+    const float m_new = fmaxf(m_run, tmax);
+    const float mu = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f((m_run - mu) * c2);  // 0 while m_run is -inf
+    const float pw = __builtin_amdgcn_exp2f((sc - mu) * c2);        // 0 for masked keys
+    float psum = pw;
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) psum += __shfl_xor(psum, m, 16);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int j = 0; j < DPT; ++j) o[j] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float pt = __shfl(pw, t, 16);
+#pragma unroll
+      for (int j = 0; j < DPT; ++j) o[j] = fmaf(pt, vs[x * DPT + j][t], o[j]);
+    }
+  }
+  const int64_t row = (int64_t)s * a.hq + head0 + h;
+  if (nparts == 1) {
+    if (h < nh) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+#pragma unroll
+      for (int j = 0; j < DPT; ++j) static_cast<float*>(a.o)[row * D + x * DPT + j] = o[j] * inv;
+    }
+    return;
+  }
+  if (h < nh) {
+    const int64_t slot = row * a.max_parts + p;
+#pragma unroll
+    for (int j = 0; j < DPT; j += 2) store_coherent(a.ws_o + slot * D + x * DPT + j, o[j], o[j + 1]);
+    if (x == 0) store_coherent(a.ws_ml + slot * 2, m_run, l_run);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  if (!arrive_last(a.counters + (int64_t)s * (a.hkv * a.head_groups) + yy, nparts, &flag)) return;
+  merge_partials<D, float>(a, s, head0, nh, nparts, tid, 256);
+}
+
+// ---------------------------------------------------------------------------
 // Fixed decode scratch for attn_decode_paged_noalloc: the same workspace
 // layout (arrival counters, partial outputs, (m, l) pairs) in a device array
 // of the library's own, so that a call allocates nothing.  Each GPU holds
@@ -460,6 +599,19 @@ static void launch_decode_t(const DecodeArgs& a, hipStream_t st) {
   }
   const dim3 grid(a.max_parts | 1, a.hkv * a.head_groups, a.num_seqs);
   hipLaunchKernelGGL((decode_partition_kernel<D, FUSED>), grid, dim3(64 * DW), 0, st, a);
+}
+
+hipError_t launch_decode_f32(const DecodeArgs& a, int head_dim, hipStream_t st) {
+  dim3 grid;
+  if (a.plan != nullptr) {
+    if (a.plan_items == 0) return hipSuccess;
+    grid = dim3((uint32_t)a.plan_items * (uint32_t)(a.hkv * a.head_groups));
+  } else {
+    grid = dim3(a.max_parts, a.hkv * a.head_groups, a.num_seqs);
+  }
+  if (head_dim == 128) hipLaunchKernelGGL(decode_f32_kernel<128>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(decode_f32_kernel<64>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStream_t st) {

@@ -126,8 +126,10 @@ struct RmsNormArgs {
 // 4-wavefront tiles): a three-deep V ring, one workgroup per CU.
 hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, int hpw, int wph, bool deep_v,
                                hipStream_t s);
-hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s);
+hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, bool paged, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStream_t s);
+// fp32 decode (no fused write); partitions may be any multiple of 16 tokens
+hipError_t launch_decode_f32(const DecodeArgs& a, int head_dim, hipStream_t s);
 // The library's fixed decode scratch on the current device (32 MiB, found
 // and zero-filled on `s` on the first call per device), for
 // attn_decode_paged_noalloc.

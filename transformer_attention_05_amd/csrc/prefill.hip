@@ -785,7 +785,9 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(const PrefillArgs a)
 
 // ---------------------------------------------------------------------------
 // f32 VALU kernel: LPQ = D / 64 lanes per query, each holding 64 channels.
-template <int D>
+// PAGED: packed queries (cu_seqlens_q) over keys and values gathered
+// through the block table (K blocks token-major, V blocks token-minor).
+template <int D, bool PAGED>
 __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const PrefillArgs a) {
   constexpr int LPQ = D / 64;
   constexpr int TN = 32;  // keys per tile
@@ -800,23 +802,47 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
   const int b = (int)(rem / a.hq);
   const int h = (int)(rem % a.hq);
   const int g = h / a.group;
-  const int tq = a.tq, tk = a.tk, off = tk - tq;
+  int tq, tk;
+  int64_t q_row0 = 0;
+  const int32_t* bt_row = nullptr;
+  if constexpr (PAGED) {
+    const int32_t c0 = a.cu_seqlens_q[b];
+    // a malformed cu_seqlens / context_lens can shrink the work, never widen
+    // the memory it touches
+    tq = max(0, min(a.cu_seqlens_q[b + 1], a.total_q) - max(c0, 0));
+    tk = min(a.context_lens[b], a.bt_stride * kBlockSize);
+    q_row0 = max(c0, 0);
+    bt_row = a.block_table + (int64_t)b * a.bt_stride;
+  } else {
+    tq = a.tq;
+    tk = a.tk;
+  }
+  const int off = tk - tq;
   const int m0 = mt * QM;
   if (m0 >= tq) return;
 
   const int tid = threadIdx.x;
   const int qi = m0 + tid / LPQ;
   const int part = tid % LPQ;
-  const float* qp = static_cast<const float*>(a.q) + b * a.qs_b + h * a.qs_h;
-  const float* kp = static_cast<const float*>(a.k) + b * a.ks_b + g * a.ks_h;
-  const float* vp = static_cast<const float*>(a.v) + b * a.vs_b + g * a.vs_h;
-  float* op = static_cast<float*>(a.o) + b * a.os_b + h * a.os_h;
-  // additive mask row of this query (rows past the queries read the last row)
-  const float* mrow = a.mask ? a.mask + b * a.ms_b + h * a.ms_h + (int64_t)min(qi, tq - 1) * a.ms_q : nullptr;
+  const int64_t q_stride = PAGED ? (int64_t)a.hq * D : a.qs_t;
+  const int64_t o_stride = PAGED ? (int64_t)a.hq * D : a.os_t;
+  const float* qp = static_cast<const float*>(a.q) + (PAGED ? (q_row0 * a.hq + h) * D : b * a.qs_b + h * a.qs_h);
+  float* op = static_cast<float*>(a.o) + (PAGED ? (q_row0 * a.hq + h) * D : b * a.os_b + h * a.os_h);
+  const float* kp = static_cast<const float*>(a.k);
+  const float* vp = static_cast<const float*>(a.v);
+  // additive mask row of this query (rows past the queries read the last
+  // row); paged rows hold mask_keys entries, later keys count as masked
+  const float* mrow = nullptr;
+  int mk = tk;
+  if (a.mask != nullptr) {
+    const int64_t mq = (PAGED ? q_row0 : 0) + min(qi, tq - 1);
+    mrow = a.mask + (PAGED ? 0 : b * a.ms_b) + h * a.ms_h + mq * a.ms_q;
+    if (PAGED) mk = min(tk, a.mask_keys);
+  }
 
   float qr[64];
 #pragma unroll
-  for (int d = 0; d < 64; ++d) qr[d] = qi < tq ? qp[(int64_t)qi * a.qs_t + part * 64 + d] : 0.f;
+  for (int d = 0; d < 64; ++d) qr[d] = qi < tq ? qp[(int64_t)qi * q_stride + part * 64 + d] : 0.f;
   float acc[64];
 #pragma unroll
   for (int d = 0; d < 64; ++d) acc[d] = 0.f;
@@ -832,8 +858,16 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
       const int key = n0 + row;
       float4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
       if (key < tk) {
-        kv = *reinterpret_cast<const float4*>(kp + (int64_t)key * a.ks_t + 4 * c4);
-        vv = *reinterpret_cast<const float4*>(vp + (int64_t)key * a.vs_t + 4 * c4);
+        if constexpr (PAGED) {
+          const int64_t base = ((int64_t)safe_block(bt_row[key >> 4], a.num_blocks) * a.hkv + g) * (kBlockSize * D);
+          kv = *reinterpret_cast<const float4*>(kp + base + (key & 15) * D + 4 * c4);
+          // value blocks are token-minor: channel d of token t at d * 16 + t
+          const float* vb = vp + base + (4 * c4) * kBlockSize + (key & 15);
+          vv = float4{vb[0], vb[kBlockSize], vb[2 * kBlockSize], vb[3 * kBlockSize]};
+        } else {
+          kv = *reinterpret_cast<const float4*>(kp + b * a.ks_b + (int64_t)key * a.ks_t + g * a.ks_h + 4 * c4);
+          vv = *reinterpret_cast<const float4*>(vp + b * a.vs_b + (int64_t)key * a.vs_t + g * a.vs_h + 4 * c4);
+        }
       }
       *reinterpret_cast<float4*>(&ks[row][4 * c4]) = kv;
       *reinterpret_cast<float4*>(&vs[row][4 * c4]) = vv;
@@ -851,7 +885,7 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
       // scores are kept in log2 units (scale * log2 e folded in once), so the
       // exponent below is a plain difference of stored values and the row
       // maximum gets weight exactly 1
-      if (mrow != nullptr && n0 + j <= lim) dot = fmaf(mrow[n0 + j], a.mask_scale, dot);
+      if (mrow != nullptr && n0 + j <= lim) dot = n0 + j < mk ? fmaf(mrow[n0 + j], a.mask_scale, dot) : -INFINITY;
       s[j] = (n0 + j <= lim) ? dot * c2 : -INFINITY;
       tmax = fmaxf(tmax, s[j]);
     }
@@ -873,8 +907,8 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
   if (qi < tq) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-    for (int d = 0; d < 64; ++d) op[(int64_t)qi * a.os_t + part * 64 + d] = acc[d] * inv;
-    if (a.lse != nullptr && part == 0)
+    for (int d = 0; d < 64; ++d) op[(int64_t)qi * o_stride + part * 64 + d] = acc[d] * inv;
+    if (!PAGED && a.lse != nullptr && part == 0)
       a.lse[((int64_t)b * a.hq + h) * tq + qi] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
   }
 }
@@ -928,10 +962,15 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, i
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, hipStream_t s) {
+hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, bool paged, hipStream_t s) {
   dim3 grid(a.num_wg);
-  if (head_dim == 128) hipLaunchKernelGGL((prefill_f32_kernel<128>), grid, dim3(128), 0, s, a);
-  else hipLaunchKernelGGL((prefill_f32_kernel<64>), grid, dim3(64), 0, s, a);
+  if (paged) {
+    if (head_dim == 128) hipLaunchKernelGGL((prefill_f32_kernel<128, true>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((prefill_f32_kernel<64, true>), grid, dim3(64), 0, s, a);
+  } else {
+    if (head_dim == 128) hipLaunchKernelGGL((prefill_f32_kernel<128, false>), grid, dim3(128), 0, s, a);
+    else hipLaunchKernelGGL((prefill_f32_kernel<64, false>), grid, dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 
