@@ -16,9 +16,9 @@
 // thread owns one (token, chunk) of the rotation: chunk c is the four pairs
 // 4c .. 4c+3, i.e. channels 4c .. 4c+3 and 4c + D/2 .. +3 of a row, and the
 // thread takes that chunk of every other query/key row of its token (two
-// threads per chunk, rows of alternating parity).  It forms the four
-// (cos, sin) values itself, so threads never wait for each other: there is
-// no table in LDS and no barrier.  A value item is four channels of one
+// threads per chunk, rows of alternating parity).  The two threads of a
+// chunk (neighbouring lanes) form two of its four (cos, sin) values each and
+// swap them by a lane shuffle: no table in LDS, no barrier.  A value item is four channels of one
 // token; the token index runs fastest, so the 16 lanes of a quarter-wave
 // store 16 consecutive tokens' elements of one channel row of the
 // token-minor value block (one contiguous 32-byte run when the slots are
@@ -92,9 +92,9 @@ __global__ __launch_bounds__(kThreads) void rope_write_kernel(const RopeWriteArg
   const int rows = a.hq + a.hkv;
   const int32_t pos = a.positions[n];
   int32_t slot = a.slot_mapping[n];
-  double th[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) th[e] = a.freqs.theta[4 * c + e];
+  // this thread forms the angles of pairs 4c + 2h and 4c + 2h + 1; the
+  // other thread of the chunk (lane ^ 1) forms the other two
+  const double th0 = a.freqs.theta[4 * c + 2 * h], th1 = a.freqs.theta[4 * c + 2 * h + 1];
   T* q = static_cast<T*>(a.q);
   const T* k = static_cast<const T*>(a.k);
   T* kc = static_cast<T*>(a.k_cache);
@@ -134,11 +134,20 @@ __global__ __launch_bounds__(kThreads) void rope_write_kernel(const RopeWriteArg
         vx[u] = Vec4<T>::load(v + ((int64_t)nv * a.hkv + gv) * D + 4 * dv);
       }
     }
-    // angles of this thread's four pairs (formed while the data arrives)
+    // angles of the chunk's four pairs (formed while the data arrives): two
+    // here, two from the neighbouring lane
     float cs[4] = {1.f, 1.f, 1.f, 1.f}, sn[4] = {0.f, 0.f, 0.f, 0.f};
     if (rot) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rope_cos_sin(pos, th[e], cs[e], sn[e]);
+      float c0, s0, c1, s1;
+      rope_cos_sin(pos, th0, c0, s0);
+      rope_cos_sin(pos, th1, c1, s1);
+      const float d0 = __shfl_xor(c0, 1), e0 = __shfl_xor(s0, 1), d1 = __shfl_xor(c1, 1), e1 = __shfl_xor(s1, 1);
+      // (selects, not an index by h: a lane-dependent index would move the
+      // arrays to memory)
+      cs[0] = h ? d0 : c0; sn[0] = h ? e0 : s0;
+      cs[1] = h ? d1 : c1; sn[1] = h ? e1 : s1;
+      cs[2] = h ? c0 : d0; sn[2] = h ? s0 : e0;
+      cs[3] = h ? c1 : d1; sn[3] = h ? s1 : e1;
     }
     if (slot >= a.num_blocks * kBlockSize) slot = -1;  // outside the pool: skipped
 #pragma unroll
