@@ -12,11 +12,15 @@ its own tokens.
 Inputs are synthetic and already resident in HBM when timing starts.
 
 Timing: the headline times --steps steps after --warmup untimed ones,
-between two device synchronisations.  Every component figure takes 20
-untimed calls and then 100 timed calls in samples of 5 back-to-back calls
-between a pair of HIP events on the launching stream; it reports the median
-(`us`), the min and the mean per call.  The decode roofline uses the mean
-(the average launch duration), as the profiler summary does.
+between two device synchronisations (eager launches).  Every component
+figure takes 20 untimed calls and then 100 timed calls in samples of 5
+back-to-back calls between a pair of HIP events on the launching stream,
+the 5 calls captured once in a HIP graph and replayed per sample (so the
+binding's host-side cost does not pace short kernels); it reports the
+median (`us`), the min and the mean per call.  The decode roofline uses
+the mean (the average launch duration), as the profiler summary does; the
+step is also timed eagerly in samples of 5 and inside the step the decode
+and the chunked prefill are timed by events on their own streams.
 
 value = percent of the step's roofline time reached:
     100 * max(F / 2.5 PFLOP/s, B / 8 TB/s) / measured step time
@@ -99,38 +103,55 @@ def write_bytes(n_tokens):
 WARM_CALLS, TIMED_CALLS, PER_SAMPLE = 20, 100, 5
 
 
-def timed(torch, fn, warm=None, calls=None, per=PER_SAMPLE):
+def timed(torch, fn, warm=None, calls=None, per=PER_SAMPLE, graph=True):
     """Per-call duration of fn(i), in ms: `warm` untimed calls, then `calls`
     timed ones as calls / per samples, each a pair of HIP events on the
-    current stream (the stream the calls launch on) around `per` back-to-back
-    calls.  (An event recorded between two kernels leaves the GPU idle for
-    several microseconds on this stack, so an event pair around every single
-    call would inflate short kernels.)  Returns mean, median and min over the
+    current stream around `per` back-to-back calls.  With `graph`, the `per`
+    calls are captured once in a HIP graph and each sample replays it: the
+    kernels then run back to back on the GPU whatever the host-side cost of
+    a call (the Python binding's argument checks take longer than the
+    shortest kernels), so the figure is the GPU time per call, as a profiler
+    trace reports it.  (An event recorded between two kernels leaves the GPU
+    idle for several microseconds on this stack, so there is no event pair
+    around every single call.)  Returns mean, median and min over the
     samples, and the call counts."""
     warm = WARM_CALLS if warm is None else warm
     calls = TIMED_CALLS if calls is None else calls
     for i in range(warm):
         fn(i)
     torch.cuda.synchronize()
+    g = None
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for j in range(per):
+                fn(j)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
     samples = []
     for k in range(calls // per):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for j in range(per):
-            fn(k * per + j)
+        if g is not None:
+            g.replay()
+        else:
+            for j in range(per):
+                fn(k * per + j)
         b.record()
         torch.cuda.synchronize()
         samples.append(a.elapsed_time(b) / per)
     return dict(mean=float(np.mean(samples)), median=float(np.median(samples)), min=float(np.min(samples)),
-                warm=warm, calls=(calls // per) * per, per_sample=per)
+                warm=warm, calls=(calls // per) * per, per_sample=per, graph=g is not None)
 
 
 def fig(t, work=None, unit=None, peak=None, key="frac_of_peak"):
     """A component figure: median us (the primary), min and mean us, the
     iteration counts, and the median's rate (and fraction of peak)."""
+    how = "graph replays of" if t.get("graph") else "eager,"
     d = {"us": round(t["median"] * 1e3, 2), "us_min": round(t["min"] * 1e3, 2), "us_mean": round(t["mean"] * 1e3, 2),
-         "iters": f"{t['warm']} warm-up + {t['calls']} timed calls ({t['per_sample']} per event pair)"}
+         "iters": f"{t['warm']} warm-up + {t['calls']} timed calls ({how} {t['per_sample']} calls per event pair)"}
     if work is not None:
         rate = work / (t["median"] / 1e3)
         d[unit] = round(rate / (1e12 if unit == "TFLOP/s" else 1e9), 1)
@@ -202,7 +223,7 @@ def main():
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) / args.steps
         # the step again, event-timed (median and min over samples)
-        t_step = timed(torch, lambda i: step.run())
+        t_step = timed(torch, lambda i: step.run(), graph=False)
         # the prefill and the decode inside the step: events on each stream
         # around each of them (each event adds a few microseconds of idle
         # time to its stream, so these are slight overestimates)
