@@ -476,6 +476,31 @@ ATTN_API int attn_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                      attn_dtype dtype, attn_stream_t stream);
 
+/* -------------------------------------------------------------------------
+ * Debug library.  Every kernel keeps its accesses inside the buffers whatever
+ * the device-side inputs hold: block-table entries outside the pool read
+ * block 0, slots and copy pairs outside the pool are skipped, lengths are cut
+ * to what the block-table row and the launch cover.  The release library
+ * does this silently.  The debug library (libmi_attn_debug.so, built from the
+ * same sources with MI_ATTN_DEBUG=1; the Python binding loads it instead of
+ * libmi_attn.so when the environment variable MI_ATTN_DEBUG is 1) also
+ * records, per device, which kinds of malformed input the kernels met:
+ * ---------------------------------------------------------------------- */
+#define ATTN_DEBUG_BLOCK_ID 1u  /* a block-table entry a kernel needed lies outside [0, num_blocks) */
+#define ATTN_DEBUG_SLOT 2u      /* a slot_mapping entry below -1 or at or past num_blocks * block_size */
+#define ATTN_DEBUG_CONTEXT 4u   /* a context length below 0, or beyond the block-table row
+                                   (max_blocks_per_seq * block_size) or the decode launch
+                                   (max_context_len rounded up to the partition) */
+#define ATTN_DEBUG_COPY_PAIR 8u /* an attn_copy_blocks pair with an id outside [0, num_blocks) */
+#define ATTN_DEBUG_SEQLENS 16u  /* cu_seqlens_q not starting at 0, falling, or past total_q */
+
+/* Debug library: waits for the current device (hipDeviceSynchronize), ORs
+ * the recorded bits of that device into *flags_out (host) and, when
+ * clear != 0, forgets them.  Release library: *flags_out = 0 and
+ * ATTN_E_UNSUPPORTED.  ATTN_E_INVALID for a NULL flags_out, ATTN_E_DEVICE
+ * if a HIP call fails. */
+ATTN_API int attn_debug_flags(uint32_t* flags_out, int clear);
+
 #ifdef __cplusplus
 }
 #endif

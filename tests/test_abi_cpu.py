@@ -58,13 +58,45 @@ def test_binding_signatures_match_header():
         assert len(mi._SIGNATURES[name][1]) == n, (name, len(mi._SIGNATURES[name][1]), n)
 
 
-def test_library_exports_every_declared_symbol(lib):
+@pytest.mark.parametrize("debug", [False, True], ids=["release", "debug"])
+def test_library_exports_every_declared_symbol(debug):
+    lib = mi.load(debug=debug)
     for name in declared_symbols():
         assert hasattr(lib, name), name
     # and nothing else: the build hides internal symbols
-    out = os.popen(f"nm -D --defined-only {mi.lib_path()}").read()
+    out = os.popen(f"nm -D --defined-only {mi.lib_path(debug)}").read()
     exported = sorted(set(re.findall(r" T (attn_\w+)", out)))
     assert exported == declared_symbols()
+
+
+def test_debug_flags_entry_point():
+    """The release library has no debug record (UNSUPPORTED, flags 0); both
+    reject a NULL output before any HIP call."""
+    rel, dbg = mi.load(debug=False), mi.load(debug=True)
+    out = ctypes.c_uint32(123)
+    assert rel.attn_debug_flags(ctypes.byref(out), 1) == ATTN_E_UNSUPPORTED and out.value == 0
+    assert "release library" in rel.attn_last_error().decode()
+    for lib in (rel, dbg):
+        assert lib.attn_debug_flags(None, 0) == ATTN_E_INVALID
+
+
+def test_library_selection(monkeypatch):
+    """MI_ATTN_DEBUG=1 selects the debug library; debug_library() overrides
+    the variable for a block and restores the previous choice."""
+    monkeypatch.delenv("MI_ATTN_DEBUG", raising=False)
+    assert mi.lib_path().endswith("libmi_attn.so")
+    monkeypatch.setenv("MI_ATTN_DEBUG", "1")
+    assert mi.lib_path().endswith("libmi_attn_debug.so")
+    with mi.debug_library(False) as lib:
+        assert mi.lib_path().endswith("libmi_attn.so") and lib is mi.load(debug=False)
+        with mi.debug_library() as dlib:
+            assert dlib is mi.load(debug=True) and mi.load() is dlib
+        assert mi.load() is lib
+    assert mi.lib_path().endswith("libmi_attn_debug.so")
+    monkeypatch.setenv("MI_ATTN_DEBUG", "0")
+    assert mi.lib_path().endswith("libmi_attn.so")
+    with pytest.raises(mi.AttnError, match="release library"):
+        mi.attn_debug_flags()
 
 
 # fake, aligned device addresses: never dereferenced on the error path

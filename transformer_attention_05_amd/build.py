@@ -1,9 +1,12 @@
-"""Build the HIP library libmi_attn.so in-tree for gfx950.
+"""Build the HIP libraries in-tree for gfx950.
 
     python -m transformer_attention_05_amd.build
 
-Every source is compiled (in parallel) on each call; the shared object lands
-next to this file, where the Python binding loads it.
+libmi_attn.so is the release library; libmi_attn_debug.so is built from the
+same sources with MI_ATTN_DEBUG=1 (the kernels also record malformed
+device-side inputs, read back by attn_debug_flags).  Every source is compiled
+(in parallel) on each call; the shared objects land next to this file, where
+the Python binding loads them.
 """
 
 from __future__ import annotations
@@ -20,6 +23,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmi_attn.so")
+LIB_DEBUG = os.path.join(PKG, "libmi_attn_debug.so")
 
 SOURCES = ["prefill.hip", "decode.hip", "rope_write.hip", "copy_blocks.hip", "rmsnorm.hip", "api.cpp", "pool.cpp"]
 ARCH = "gfx950"
@@ -43,27 +47,42 @@ def _flags(src: str):
     return common + ["-D__HIP_PLATFORM_AMD__"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, debug = job
+    out_dir = os.path.join(BUILD, "debug") if debug else BUILD
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *_flags(src), *(["-DMI_ATTN_DEBUG=1"] if debug else []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str):
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False, debug: bool = True) -> str:
+    """Compile and link the release library (and, with `debug`, the debug
+    library); returns the release library's path."""
+    os.makedirs(os.path.join(BUILD, "debug"), exist_ok=True)
+    variants = (False, True) if debug else (False,)
+    jobs = [(src, d) for d in variants for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(_compile, jobs))
+    n = len(SOURCES)
+    _link(objs[:n], LIB)
     if verbose:
         print(f"built {LIB}")
+    if debug:
+        _link(objs[n:], LIB_DEBUG)
+        if verbose:
+            print(f"built {LIB_DEBUG}")
     return LIB
 
 

@@ -770,3 +770,26 @@ extern "C" int attn_residual_rms_norm(const void* x, const void* residual, const
   a.rows = rows; a.hidden = hidden; a.eps = eps;
   return launched(launch_residual_rms_norm(a, dtype == ATTN_BF16, reinterpret_cast<hipStream_t>(stream)), fn);
 }
+
+// ---------------------------------------------------------------------------
+extern "C" int attn_debug_flags(uint32_t* flags_out, int clear) {
+  static const char* fn = "attn_debug_flags";
+  if (!flags_out) return fail(ATTN_E_INVALID, "%s: flags_out must be non-NULL", fn);
+  *flags_out = 0;
+#if MI_ATTN_DEBUG
+  hipError_t e = hipDeviceSynchronize();
+  uint32_t acc = 0;
+  const bool c = clear != 0;
+  if (e == hipSuccess) e = debug_take_prefill(&acc, c);
+  if (e == hipSuccess) e = debug_take_decode(&acc, c);
+  if (e == hipSuccess) e = debug_take_rope_write(&acc, c);
+  if (e == hipSuccess) e = debug_take_copy_blocks(&acc, c);
+  if (e != hipSuccess) return fail(ATTN_E_DEVICE, "%s: %s", fn, hipGetErrorString(e));
+  *flags_out = acc;
+  return ok();
+#else
+  (void)clear;
+  return fail(ATTN_E_UNSUPPORTED, "%s: this is the release library (the debug one is built with MI_ATTN_DEBUG=1)",
+              fn);
+#endif
+}

@@ -20,6 +20,8 @@ constexpr int kCopyThreads = 256;
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(const CopyBlocksArgs a) {
   const int p = (int)blockIdx.x;
   const int32_t src = a.pairs[2 * p], dst = a.pairs[2 * p + 1];
+  DEBUG_ONLY(debug_report(threadIdx.x == 0 && (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks),
+                          kDebugCopyPair));
   if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks || src == dst) return;
   char* base = static_cast<char*>(blockIdx.y == 0 ? a.k_cache : a.v_cache);
   const u32x4* s = reinterpret_cast<const u32x4*>(base + (int64_t)src * a.block_bytes);
@@ -45,5 +47,8 @@ hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(copy_blocks_kernel, dim3((uint32_t)a.num_pairs, 2), dim3(kCopyThreads), 0, st, a);
   return hipGetLastError();
 }
+
+// debug builds: this file's report word (nothing in release builds)
+hipError_t debug_take_copy_blocks(uint32_t* acc, bool clear) { return debug_take_word(acc, clear); }
 
 }  // namespace mi_attn

@@ -160,6 +160,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, co
 
   // the grid and the block table bound what a malformed length can reach
   const int ctx = min(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize));
+  DEBUG_ONLY(debug_check_length(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize)));
   const int nparts = (ctx + a.part_size - 1) / a.part_size;
   // (a partition past the context leaves after the wait below: a branch
   // here would let the compiler sink the loads above behind the length)
@@ -220,6 +221,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, const int p, co
     // the slot before they read the partition's blocks; the other
     // partitions never read that block.  Wave 0, lane i: pair (i, i + D/2).
     const int32_t slot = a.slot_mapping[s];
+    DEBUG_ONLY(debug_check_slot(p == nparts - 1 && tid == 0, slot, a.num_blocks));
     if (p == nparts - 1 && slot >= 0 && slot < a.num_blocks * kBlockSize) {
       if (wave == 0 && lane < D / 2) {
         const int64_t src = ((int64_t)s * a.hkv + kvh) * D;
@@ -451,6 +453,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
   const int head0 = kvh * a.group + hgi * 16;
   const int nh = min(16, a.group - hgi * 16);
   const int ctx = min(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize));
+  DEBUG_ONLY(debug_check_length(a.context_lens[s], min(a.max_parts * a.part_size, a.bt_stride * kBlockSize)));
   const int nparts = (ctx + a.part_size - 1) / a.part_size;
   if (p >= nparts) return;  // uniform
   const int tok_begin = p * a.part_size;
@@ -624,5 +627,8 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStrea
   }
   return hipGetLastError();
 }
+
+// debug builds: this file's report word (nothing in release builds)
+hipError_t debug_take_decode(uint32_t* acc, bool clear) { return debug_take_word(acc, clear); }
 
 }  // namespace mi_attn

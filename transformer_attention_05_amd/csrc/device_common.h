@@ -121,9 +121,77 @@ __device__ __forceinline__ bool arrive_last(int32_t* counter, int n, int* flag) 
   return *flag != 0;
 }
 
+// ---- debug builds (compiled with MI_ATTN_DEBUG=1)
+// The kernels keep every access in bounds whatever the caller passes (block
+// ids are clamped, bad slots and pairs skipped, lengths cut to what the
+// launch covers).  A debug build also says that it happened: each kernel ORs
+// a bit per kind of malformed input it met (ATTN_DEBUG_* in mi_attn.h) into
+// a word of its translation unit, which attn_debug_flags reads back.  In a
+// release build the checks compile to nothing.
+#ifndef MI_ATTN_DEBUG
+#define MI_ATTN_DEBUG 0
+#endif
+constexpr uint32_t kDebugBlockId = 1u;   // a block-table entry in use outside [0, num_blocks)
+constexpr uint32_t kDebugSlot = 2u;      // a slot below -1 or at or past num_blocks * 16
+constexpr uint32_t kDebugContext = 4u;   // a length below 0 or beyond what the table row / launch covers
+constexpr uint32_t kDebugCopyPair = 8u;  // a copy pair with an id outside [0, num_blocks)
+constexpr uint32_t kDebugSeqlens = 16u;  // cu_seqlens_q not rising from 0 to at most total_q
+
+// DEBUG_ONLY(statement): the statement in debug builds, nothing at all in
+// release builds (whose code is then exactly what it is without the checks).
+#if MI_ATTN_DEBUG
+#define DEBUG_ONLY(...) __VA_ARGS__
+static __device__ uint32_t debug_word;
+
+__device__ __forceinline__ void debug_report(bool bad, uint32_t bit) {
+  if (bad) atomicOr(&debug_word, bit);
+}
+// Checks of per-sequence inputs, made by thread 0 of a workgroup: a length
+// against the tokens the launch (or table row) covers, and a paged
+// prefill's query offsets.
+__device__ __forceinline__ void debug_check_length(int32_t len, int32_t bound) {
+  debug_report(threadIdx.x == 0 && (len < 0 || len > bound), kDebugContext);
+}
+__device__ __forceinline__ void debug_check_seqlens(const int32_t* cu_seqlens_q, int b, int32_t total_q) {
+  if (threadIdx.x == 0) {
+    const int32_t c0 = cu_seqlens_q[b], c1 = cu_seqlens_q[b + 1];
+    debug_report((b == 0 && c0 != 0) || c1 < c0 || c1 > total_q, kDebugSeqlens);
+  }
+}
+// A slot of the paged cache: -1 (skip) or in [0, num_blocks * 16).
+__device__ __forceinline__ void debug_check_slot(bool live, int32_t slot, int32_t num_blocks) {
+  debug_report(live && (slot < -1 || slot >= num_blocks * kBlockSize), kDebugSlot);
+}
+#else
+#define DEBUG_ONLY(...)
+#endif
+
+// Host side: OR this translation unit's word on the current device into
+// *acc, and zero it when `clear` (synchronous; the caller has synchronised
+// the device).  Release builds: nothing.
+static inline hipError_t debug_take_word(uint32_t* acc, bool clear) {
+#if MI_ATTN_DEBUG
+  uint32_t w = 0;
+  hipError_t e = hipMemcpyFromSymbol(&w, HIP_SYMBOL(debug_word), sizeof(w), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  *acc |= w;
+  if (clear && w != 0) {
+    const uint32_t zero = 0;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(debug_word), &zero, sizeof(zero), 0, hipMemcpyHostToDevice);
+  }
+  return e;
+#else
+  (void)acc;
+  (void)clear;
+  return hipSuccess;
+#endif
+}
+
 // A block-table entry outside the pool is replaced by block 0 so that a
-// corrupt table can never address memory outside the cache.
+// corrupt table can never address memory outside the cache.  Callers pass
+// only entries the kernel needs (debug builds report the others).
 __device__ __forceinline__ int32_t safe_block(int32_t blk, int32_t num_blocks) {
+  DEBUG_ONLY(debug_report(blk < 0 || blk >= num_blocks, kDebugBlockId));
   return (blk >= 0 && blk < num_blocks) ? blk : 0;
 }
 

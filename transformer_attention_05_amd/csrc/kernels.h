@@ -71,7 +71,7 @@ struct DecodeArgs {
   int32_t* counters;    // [S][Hkv * head_groups] partitions finished (zero between calls)
   int32_t num_seqs, hq, hkv, group, head_groups;
   int32_t part_size, max_parts;
-  int32_t num_blocks;  // pool size; out-of-range table entries read as zeros
+  int32_t num_blocks;  // pool size; out-of-range table entries are redirected to block 0
   float scale_log2;
   const int32_t* plan;  // [plan_items][2] (sequence, partition), or null: padded grid
   int32_t plan_items;
@@ -128,6 +128,7 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, int head_dim, bool paged, i
                                hipStream_t s);
 hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, bool paged, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool fused, hipStream_t s);
+
 // fp32 decode (no fused write); partitions may be any multiple of 16 tokens
 hipError_t launch_decode_f32(const DecodeArgs& a, int head_dim, hipStream_t s);
 // The library's fixed decode scratch on the current device (32 MiB, found
@@ -143,5 +144,12 @@ hipError_t launch_residual_rms_norm(const RmsNormArgs& a, bool bf16, hipStream_t
 constexpr int kPrefillBlockN = 64;
 constexpr int kPrefillF32BlockM = 64;
 constexpr int kBlockSizeHost = 16;  // paged KV block, in tokens
+
+// Debug builds: OR the report word of each kernel file on the current device
+// into *acc (and zero it when `clear`); release builds leave *acc alone.
+hipError_t debug_take_prefill(uint32_t* acc, bool clear);
+hipError_t debug_take_decode(uint32_t* acc, bool clear);
+hipError_t debug_take_rope_write(uint32_t* acc, bool clear);
+hipError_t debug_take_copy_blocks(uint32_t* acc, bool clear);
 
 }  // namespace mi_attn

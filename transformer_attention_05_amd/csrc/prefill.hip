@@ -148,6 +148,8 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     tk = min(a.context_lens[b], a.bt_stride * kBlockSize);
     q_row0 = max(c0, 0);
     bt_row = a.block_table + (int64_t)b * a.bt_stride;
+    DEBUG_ONLY(debug_check_seqlens(a.cu_seqlens_q, b, a.total_q));
+    DEBUG_ONLY(debug_check_length(a.context_lens[b], a.bt_stride * kBlockSize));
   } else {
     tq = a.tq;
     tk = a.tk;
@@ -813,6 +815,8 @@ __global__ __launch_bounds__(64 * (D / 64)) void prefill_f32_kernel(const Prefil
     tk = min(a.context_lens[b], a.bt_stride * kBlockSize);
     q_row0 = max(c0, 0);
     bt_row = a.block_table + (int64_t)b * a.bt_stride;
+    DEBUG_ONLY(debug_check_seqlens(a.cu_seqlens_q, b, a.total_q));
+    DEBUG_ONLY(debug_check_length(a.context_lens[b], a.bt_stride * kBlockSize));
   } else {
     tq = a.tq;
     tk = a.tk;
@@ -973,5 +977,8 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, int head_dim, bool paged, hi
   }
   return hipGetLastError();
 }
+
+// debug builds: this file's report word (nothing in release builds)
+hipError_t debug_take_prefill(uint32_t* acc, bool clear) { return debug_take_word(acc, clear); }
 
 }  // namespace mi_attn

@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kThreads) void rope_write_kernel(const RopeWriteArg
       cs[2] = h ? c0 : d0; sn[2] = h ? s0 : e0;
       cs[3] = h ? c1 : d1; sn[3] = h ? s1 : e1;
     }
+    DEBUG_ONLY(debug_check_slot(first && live && c == 0 && h == 0, slot, a.num_blocks));
     if (slot >= a.num_blocks * kBlockSize) slot = -1;  // outside the pool: skipped
 #pragma unroll
     for (int u = 0; u < kRowsPerPass; ++u) {
@@ -223,5 +224,8 @@ hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hi
   }
   return hipGetLastError();
 }
+
+// debug builds: this file's report word (nothing in release builds)
+hipError_t debug_take_rope_write(uint32_t* acc, bool clear) { return debug_take_word(acc, clear); }
 
 }  // namespace mi_attn
