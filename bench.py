@@ -262,8 +262,7 @@ def main():
         t_roof = max(F / PEAK_BF16_FLOPS, (B_dec + B_wr + B_pre) / PEAK_HBM)
         out["mixed"] = dict(wall_s=wall, ms_write=ms_wr, ms_prefill=ms_pre, ms_decode=ms_dec, stages=stages,
                             t_step=t_step, in_step=in_step, F=F, B_dec=B_dec,
-                            B_wr=B_wr, B_pre=B_pre, t_roof=t_roof, n_new=n_new, part=mi.attn_decode_paged_auto_partition(
-                                len(case.dec_lengths), HKV, int(case.dec_lengths.max())),
+                            B_wr=B_wr, B_pre=B_pre, t_roof=t_roof, n_new=n_new, part=step.partition_size,
                             dec_tokens=int(case.dec_lengths.sum()), pool_blocks=case.num_blocks,
                             graph_s=graph_s)
         log(f"bench: mixed step wall {wall * 1e3:.3f} ms | write {ms_wr:.3f} prefill {ms_pre:.3f} "
@@ -310,13 +309,16 @@ def main():
         bt = torch.from_numpy(dc.block_tables).to(dev)
         cl = torch.from_numpy(dc.lengths.astype(np.int32)).to(dev)
         mx = int(dc.lengths.max())
-        ws = torch.zeros(max(256, mi.attn_decode_paged_workspace_size(64, HQ, HKV, D, mx)), dtype=torch.uint8,
+        # the partition chosen from the lengths (host side, as the plan is)
+        part = mi.attn_decode_paged_partition_for(dc.lengths, HQ, HKV, D)
+        ws = torch.zeros(max(256, mi.attn_decode_paged_workspace_size(64, HQ, HKV, D, mx, part)), dtype=torch.uint8,
                          device=dev)
         o = torch.empty_like(qd)
-        plan = torch.from_numpy(mi.attn_decode_paged_plan(dc.lengths, HKV, mx)).to(dev)
-        t = timed(torch, lambda i: mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, workspace=ws, plan=plan))
+        plan = torch.from_numpy(mi.attn_decode_paged_plan(dc.lengths, HKV, mx, part)).to(dev)
+        t = timed(torch, lambda i: mi.attn_decode_paged(qd, *pools[i % 3], bt, cl, mx, o=o, partition_size=part,
+                                                        workspace=ws, plan=plan))
         by = decode_bytes(dc.lengths)
-        out["decode_c3"] = dict(t=t, bytes=by, part=mi.attn_decode_paged_auto_partition(64, HKV, mx))
+        out["decode_c3"] = dict(t=t, bytes=by, part=part)
         log(f"bench: decode C3 median {t['median'] * 1e3:.1f} us  {by / t['median'] / 1e6:.0f} GB/s")
         # a decode-only serving step: each sequence's new token (the last of
         # its context) rotated and written into its slot, then the decode;
@@ -332,11 +334,11 @@ def main():
 
         def two_launches(i):
             mi.attn_kv_cache_write_rope(q_w, k_new, v_new, pos, slots, *pools[i % 3])
-            mi.attn_decode_paged(q_w, *pools[i % 3], bt, cl, mx, o=o, workspace=ws, plan=plan)
+            mi.attn_decode_paged(q_w, *pools[i % 3], bt, cl, mx, o=o, partition_size=part, workspace=ws, plan=plan)
 
         def one_launch(i):
             mi.attn_decode_paged_rope(qd, k_new, v_new, pos, slots, *pools[i % 3], bt, cl, mx, o=o, q_rot_out=q_rot,
-                                      workspace=ws, plan=plan)
+                                      partition_size=part, workspace=ws, plan=plan)
         step_t = {name: timed(torch, fn) for name, fn in (("write_then_decode", two_launches), ("fused", one_launch))}
         out["decode_step_c3"] = dict(bytes=by + write_bytes(64), **step_t)
         log(f"bench: decode-only step C3: write + decode {step_t['write_then_decode']['median'] * 1e3:.1f} us, "

@@ -359,6 +359,18 @@ ATTN_API int64_t attn_decode_paged_plan(const int32_t* context_lens, int32_t num
 ATTN_API int32_t attn_decode_paged_auto_partition(int32_t num_seqs, int32_t num_kv_heads,
                                          int32_t max_context_len);
 
+/* A partition size chosen from the contexts themselves (host int32
+ * context_lens[num_seqs], no HIP call): the shortest of 128, 256, ..., 1024
+ * tokens (multiples of 128, valid for every dtype) whose workgroups, one per
+ * (sequence, partition) item, kv head and slice of 16 query heads, all fit on
+ * the GPU at once (two per CU at head_dim 128, four at 64), so that the
+ * longest item is as short as possible without a second round; 1024 when no
+ * size fits.  Pass it to attn_decode_paged_plan and attn_decode_paged alike
+ * (the automatic size of partition_size 0 sees only the longest context).
+ * Negative attn_status on bad arguments. */
+ATTN_API int32_t attn_decode_paged_partition_for(const int32_t* context_lens, int32_t num_seqs,
+                                        int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
+
 /* -------------------------------------------------------------------------
  * attn_kv_cache_write_rope -- fused rotary embedding + paged cache write.
  *

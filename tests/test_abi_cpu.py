@@ -517,3 +517,40 @@ def test_wrappers_refuse_cpu_tensors():
     q = torch.zeros(1, 64, 1, 64)
     with pytest.raises(ValueError, match="GPU"):
         mi.attn_prefill(q, q, q)
+
+
+def test_partition_for_lengths():
+    """attn_decode_paged_partition_for: the shortest multiple of 128 (up to
+    1024) whose items x kv heads x 16-head slices fit in 256 CUs x 2 (D 128)
+    or x 4 (D 64) workgroups; 1024 when none does (host logic, no GPU)."""
+    def brute(lengths, hq, hkv, d):
+        slots = 256 * (2 if d == 128 else 4)
+        per = hkv * ((hq // hkv + 15) // 16)
+        for p in range(128, 1025, 128):
+            if sum((max(int(L), 0) + p - 1) // p for L in lengths) * per <= slots:
+                return p
+        return 1024
+    g = np.random.default_rng(5)
+    cases = [
+        (g.integers(128, 4097, 64), 12, 2, 128),
+        (np.full(256, 1024), 12, 2, 128),
+        (np.full(257, 1024), 12, 2, 128),
+        (np.full(64, 100), 12, 2, 128),
+        (np.exp(g.uniform(np.log(16), np.log(32768), 128)).astype(int), 12, 2, 128),
+        (g.integers(1, 3000, 40), 12, 12, 128),
+        (g.integers(1, 3000, 40), 32, 1, 64),
+        (np.array([0, -5, 7]), 12, 2, 128),
+        (np.zeros(0), 12, 2, 128),
+    ]
+    for lengths, hq, hkv, d in cases:
+        assert mi.attn_decode_paged_partition_for(lengths, hq, hkv, d) == brute(lengths, hq, hkv, d), (len(lengths), hq, hkv, d)
+    # the uniform-context decode batch of 64 sequences, U[128, 4096] (seed 1002)
+    from workloads import decode_case
+    dc = decode_case(1002, 64, 128, 4096)
+    assert mi.attn_decode_paged_partition_for(dc.lengths, 12, 2, 128) == 640
+    assert mi.attn_decode_paged_partition_for(np.full(256, 1024), 12, 2, 128) == 1024
+    lib = mi.load()
+    assert lib.attn_decode_paged_partition_for(None, 3, 12, 2, 128) == ATTN_E_INVALID
+    arr = (ctypes.c_int32 * 2)(5, 6)
+    for hq, hkv, d in ((12, 2, 96), (12, 5, 128), (1, 2, 128), (12, 0, 128)):
+        assert lib.attn_decode_paged_partition_for(arr, 2, hq, hkv, d) == ATTN_E_INVALID

@@ -27,6 +27,7 @@ __all__ = [
     "attn_copy_blocks",
     "attn_decode_paged",
     "attn_decode_paged_auto_partition",
+    "attn_decode_paged_partition_for",
     "attn_decode_paged_noalloc",
     "attn_decode_paged_rope",
     "attn_decode_paged_plan",
@@ -81,6 +82,7 @@ _SIGNATURES = {
                                                  _c_i32, ctypes.c_float, _c_i32, ctypes.c_int, _vp]),
     "attn_decode_paged_workspace_size": (ctypes.c_size_t, [_c_i32] * 6),
     "attn_decode_paged_auto_partition": (_c_i32, [_c_i32] * 3),
+    "attn_decode_paged_partition_for": (_c_i32, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32]),
     "attn_decode_paged": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                          _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp, _c_i32,
                                          _vp, ctypes.c_size_t, _vp]),
@@ -452,6 +454,17 @@ def attn_decode_paged_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_d
 
 def attn_decode_paged_auto_partition(num_seqs, num_kv_heads, max_context_len) -> int:
     return int(load().attn_decode_paged_auto_partition(num_seqs, num_kv_heads, max_context_len))
+
+
+def attn_decode_paged_partition_for(context_lens, num_q_heads, num_kv_heads, head_dim=128) -> int:
+    """Partition size for these (host) context lengths: the shortest multiple
+    of 128 up to 1024 whose workgroups all fit on the GPU at once."""
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    r = int(load().attn_decode_paged_partition_for(cl.ctypes.data_as(_c_i32p), cl.shape[0], int(num_q_heads),
+                                                    int(num_kv_heads), int(head_dim)))
+    if r < 0:
+        raise AttnError(r, attn_last_error())
+    return r
 
 
 def attn_decode_paged_plan(context_lens, num_kv_heads, max_context_len, partition_size=0):

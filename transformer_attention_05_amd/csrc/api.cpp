@@ -462,6 +462,33 @@ extern "C" int32_t attn_decode_paged_auto_partition(int32_t num_seqs, int32_t nu
   return 128;
 }
 
+extern "C" int32_t attn_decode_paged_partition_for(const int32_t* context_lens, int32_t num_seqs,
+                                                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  static const char* fn = "attn_decode_paged_partition_for";
+  if (num_seqs < 0 || (num_seqs > 0 && !context_lens) || num_kv_heads < 1 || num_q_heads < num_kv_heads ||
+      num_q_heads % num_kv_heads != 0 || (head_dim != 64 && head_dim != 128))
+    return fail(ATTN_E_INVALID, "%s: bad argument", fn);
+  // Workgroups resident at once: the decode kernel holds two per CU at
+  // head_dim 128 (232 VGPRs per wavefront) and four at 64.  A sweep on MI355X
+  // over six batches (16 to 256 sequences, contexts up to 16384) found the
+  // fastest partition to be the shortest one whose items all fit in one round,
+  // or within 2 % of it (64 sequences U[128, 4096]: 640 tokens, 32.9 us,
+  // against 34.5 at 768 and 36.5 at 512, whose 566 workgroups need a second
+  // round).
+  const int64_t slots = (int64_t)kCUs * (head_dim == 128 ? 2 : 4);
+  const int64_t per_item = (int64_t)num_kv_heads * ((num_q_heads / num_kv_heads + 15) / 16);
+  for (int32_t p = 128; p <= 1024; p += 128) {
+    int64_t items = 0;
+    for (int32_t s = 0; s < num_seqs; ++s) items += (std::max(context_lens[s], 0) + p - 1) / p;
+    if (items * per_item <= slots) {
+      ok();
+      return p;
+    }
+  }
+  ok();
+  return 1024;
+}
+
 namespace {
 constexpr int32_t kMaxF32Partition = 65536;
 // Decode workspace, used only when a context can span several partitions:

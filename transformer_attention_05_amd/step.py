@@ -27,9 +27,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (Pool, attn_decode_paged, attn_decode_paged_plan, attn_decode_paged_rope,
-               attn_decode_paged_workspace_size, attn_kv_cache_write_rope, attn_prefill_paged,
-               attn_prefill_paged_workspace_size)
+from . import (Pool, attn_decode_paged, attn_decode_paged_partition_for, attn_decode_paged_plan,
+               attn_decode_paged_rope, attn_decode_paged_workspace_size, attn_kv_cache_write_rope,
+               attn_prefill_paged, attn_prefill_paged_workspace_size)
 
 
 class MixedStep:
@@ -71,6 +71,10 @@ class MixedStep:
         cu = np.arange(R + 1, dtype=np.int32) * case.chunk
         self.cu_seqlens_q = torch.from_numpy(cu).to(device)
         self.max_dec_ctx = int(case.dec_lengths.max()) if S else 1
+        # 0: the partition chosen from the decode lengths (host side), passed
+        # explicitly to the plan and to every decode call
+        if partition_size == 0 and S:
+            partition_size = attn_decode_paged_partition_for(case.dec_lengths, case.hq, hkv, d)
         self.partition_size = partition_size
         self.o_prefill = torch.empty(self.n_prefill, case.hq, d, dtype=dt, device=device)
         self.o_decode = torch.empty(S, case.hq, d, dtype=dt, device=device)
