@@ -106,7 +106,7 @@ __device__ __forceinline__ int vt_swz(int d) {   // V^T rows (paged): the two 16
 // additive mask M to every score and carries the weights P of the PV
 // product as a bf16 pair (rounded value and rounded remainder).
 template <int D, bool PAGED, int HPW, int WPH, bool MASKED = false, bool DEEP_V = false>
-__global__ __launch_bounds__(64 * HPW * WPH) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * HPW * WPH) __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
 void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NW = HPW * WPH;
   constexpr int BM = 32 * WPH;
@@ -123,7 +123,12 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // (96 KiB) for a paged launch that shares the GPU with a decode: one such
   // workgroup per CU leaves the rest of the CU to a decode workgroup.
   constexpr int NVB = (NW == 4 && !DEEP_V) ? 2 : 3;
-  __shared__ __attribute__((aligned(1024))) __bf16 sm[(3 + NVB) * TILE];
+  // MASKED: a two-slot ring of mask tiles after the K/V rings, one 32-row x
+  // BN-key fp32 sub-tile per wavefront and slot (144 KiB in all at D 128:
+  // one workgroup per CU, which also gives the masked variant's extra
+  // registers room without spilling to memory)
+  constexpr int MSUB = 32 * BN;  // floats of one sub-tile
+  __shared__ __attribute__((aligned(1024))) __bf16 sm[(3 + NVB) * TILE + (MASKED ? 2 * NW * MSUB * 2 : 0)];
 
   // split-KV share index fastest: all shares of the longest query tiles
   // (dispatched first) start together
@@ -324,6 +329,30 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     }
   };
   auto tail_tile = [&](int t) { return PAGED && t == n_all - 1 && (t + 1) * BN > tk; };
+  // MASKED: the wavefront's 32 mask rows x BN keys of key tile src_t, by DMA
+  // into ring slot slot_t % 2 (its own sub-tile; no other wavefront reads
+  // it).  Row r of a sub-tile keeps 16-byte chunk c at position c ^ (r & 15),
+  // so the reads of mask_tile (32 rows, one chunk each) hit distinct banks.
+  // A chunk not wholly inside the row's first mk keys is not fetched (the
+  // lane reads a harmless address inside q) and mask_tile loads those keys
+  // one by one.
+  const float* const mbase = MASKED ? a.mask + (PAGED ? 0 : b * a.ms_b) + h * a.ms_h : nullptr;
+  const int mask_k = PAGED ? min(tk, a.mask_keys) : tk;
+  const uint32_t mring_lds = sm_lds + 2u * (uint32_t)((3 + NVB) * TILE);
+  auto issue_mask = [&](int slot_t, int src_t) {
+    if constexpr (MASKED) {
+      const uint32_t l0 = mring_lds + 4u * (uint32_t)(((slot_t & 1) * NW + wave) * MSUB);
+#pragma unroll
+      for (int ii = 0; ii < 8; ++ii) {
+        const int r = 4 * ii + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        const int64_t mq = PAGED ? q_row0 + min(wq0 + r, tq - 1) : (int64_t)min(wq0 + r, tq - 1);
+        const int k0 = src_t * BN + 4 * c;
+        const float* src = k0 + 4 <= mask_k ? mbase + mq * a.ms_q + k0 : static_cast<const float*>(a.q);
+        dma16(src, l0 + ii * 1024);
+      }
+    }
+  };
 
   const float c2 = a.scale_log2;
   const float tau_raw = kLazyTau / c2;
@@ -501,9 +530,19 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       // Paged: the row of packed query q_row0 + qi, keys = positions in the
       // sequence's context; entries at or past mask_keys are never read and
       // those keys are masked out.
+      // Chunks wholly inside the first mk keys come from this wavefront's
+      // sub-tile in LDS (issue_mask); the others, only in a row's last tile,
+      // are loaded here key by key.  The sub-tile of tile t was issued an
+      // iteration earlier: only this iteration's DMA (2 * LPW K/V and 8 mask
+      // instructions) may still be in flight.
+      {
+        constexpr int AFTER = 2 * LPW + 8;
+        __builtin_amdgcn_s_waitcnt(0x0f70 | (AFTER & 15) | ((AFTER >> 4) << 14));
+      }
       const int64_t mq = PAGED ? q_row0 + min(qi, tq - 1) : (int64_t)min(qi, tq - 1);
-      const float* mrow = a.mask + (PAGED ? 0 : b * a.ms_b) + h * a.ms_h + mq * a.ms_q;
-      const int mk = PAGED ? min(tk, a.mask_keys) : tk;
+      const float* mrow = mbase + mq * a.ms_q;
+      const int mk = mask_k;
+      const float* msub = reinterpret_cast<const float*>(sm + (3 + NVB) * TILE) + ((t & 1) * NW + wave) * MSUB;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         f32x4 mv[4];
@@ -511,7 +550,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         for (int g4 = 0; g4 < 4; ++g4) {
           const int key0 = t * BN + kt * 32 + 8 * g4 + 4 * hh;
           if (key0 + 4 <= mk) {
-            mv[g4] = *reinterpret_cast<const f32x4*>(mrow + key0);
+            mv[g4] = *reinterpret_cast<const f32x4*>(msub + lq * BN + 4 * ((kt * 8 + 2 * g4 + hh) ^ (lq & 15)));
           } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) mv[g4][j] = key0 + j < mk ? mrow[key0 + j] : (key0 + j < tk ? -INFINITY : 0.f);
@@ -552,8 +591,9 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   };
   // DMA instructions of the current iteration that may still be in flight
   // at its end: K(j+3) and V(j+2) with the three-deep V ring; only K(j+3)
-  // with the two-deep one (its V(j+1) is issued first and must land)
-  constexpr int PENDING = NVB == 3 ? 2 * LPW : LPW;
+  // with the two-deep one (its V(j+1) is issued first and must land); and
+  // the mask tile j+2 (issued last, read in the next iteration)
+  constexpr int PENDING = (NVB == 3 ? 2 * LPW : LPW) + (MASKED ? 8 : 0);
   auto tile_barrier = [&]() {
     // s_waitcnt vmcnt(PENDING) (expcnt and lgkmcnt fields at their no-wait maximum)
     __builtin_amdgcn_s_waitcnt(0x0f70 | (PENDING & 15) | ((PENDING >> 4) << 14));
@@ -586,6 +626,8 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       issue_k(kring + TILE, T0 + min(1, n_tiles - 1), b1);
       if constexpr (NVB == 3) issue_v(vring + TILE, T0 + min(1, n_tiles - 1), b1);
       issue_k(kring + 2 * TILE, T0 + min(2, n_tiles - 1), blk_v);
+      issue_mask(T0, T0);
+      issue_mask(T0 + 1, T0 + min(1, n_tiles - 1));
 #pragma unroll
       for (int i = 0; i < 4; ++i) blk_v1[i] = b1[i];
     }
@@ -620,6 +662,8 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       issue_v(vring + vnext * TILE, T0 + min(j + 1, n_tiles - 1), blk_v1);
       issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
     }
+    // slot from the tile's own index, source clamped like the K/V tiles
+    issue_mask(T0 + j + 2, T0 + min(j + 2, n_tiles - 1));
     if constexpr (PAGED) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
