@@ -374,9 +374,9 @@ ATTN_API int32_t attn_decode_paged_partition_for(const int32_t* context_lens, in
 /* -------------------------------------------------------------------------
  * attn_kv_cache_write_rope -- fused rotary embedding + paged cache write.
  *
- * §Operator Fusion lists two fusions this kernel performs in one pass:
- * applying rotary position embeddings to queries and keys, and updating the
- * KV cache while transforming keys and values.  For token n with position
+ * This kernel performs in one pass two of the fusions §Operator Fusion
+ * lists: the rotary embedding of queries and keys, and the KV-cache update
+ * made as keys and values are transformed.  For token n with position
  * positions[n]: each pair (x[i], x[i + D/2]), i < D/2, of every query and key
  * head is rotated by angle positions[n] * rope_base^(-2i/D) (the angle is
  * formed and reduced modulo 2 pi in double precision, its sine and cosine
@@ -419,10 +419,10 @@ ATTN_API int attn_residual_rms_norm(const void* x, const void* residual, const v
                            attn_stream_t stream);
 
 /* -------------------------------------------------------------------------
- * Block pool (host only).  §Paged Attention Kernels: fixed-size blocks are
- * allocated on demand, returned to a pool when a request ends and may be
- * shared by sequences with a common prefix; a block table maps a sequence's
- * logical blocks to physical ones.  The pool is a LIFO free list with a
+ * Block pool (host only).  §Paged Attention Kernels: the cache is cut into
+ * fixed-size blocks, handed out as requests grow, given back when a request
+ * finishes, and possibly held by several sequences that begin with the same
+ * tokens; a block table maps a sequence's logical blocks to physical ones.  The pool is a LIFO free list with a
  * reference count per block.  Not thread-safe: callers serialise access.
  * ---------------------------------------------------------------------- */
 typedef struct attn_pool attn_pool;
@@ -452,8 +452,8 @@ ATTN_API int attn_pool_refcount(const attn_pool* pool, int32_t id);
 ATTN_API int attn_seq_reserve(attn_pool* pool, int32_t* block_table_row, int32_t max_blocks,
                      int32_t cur_len, int32_t n_new, int32_t* slot_mapping_out);
 
-/* Prefix sharing.  §Paged Attention Kernels: blocks are shared when
- * sequences have a common prefix.  attn_seq_fork gives child_row (host,
+/* Prefix sharing.  §Paged Attention Kernels: sequences that begin with the
+ * same tokens may hold the same blocks.  attn_seq_fork gives child_row (host,
  * max_blocks entries) the first ceil(len / block_size) entries of parent_row,
  * each block retained once more; parent and child then read the same
  * physical blocks.  On error nothing changes. */

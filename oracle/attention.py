@@ -192,8 +192,8 @@ def round_bf16(x):
 def rope(x, positions, base=10000.0):
     """Rotary position embedding in float64.
 
-    §Operator Fusion lists "applying rotary position embeddings to queries
-    and keys" as a fusion target but gives no formula; the reading used here
+    §Operator Fusion counts the rotary embedding of queries and keys among
+    its fusion targets but gives no formula; the reading used here
     is the half-split form: for i < D/2, the pair (x[i], x[i + D/2]) is
     rotated by angle pos * base**(-2i/D).  x is [N, H, D], positions [N].
     """
@@ -214,8 +214,9 @@ def kv_cache_write_expected(k_cache, v_cache, k, v, positions, slot_mapping,
                             rope_base=10000.0, bf16=True):
     """Expected paged caches after the fused RoPE + KV-cache write.
 
-    §Operator Fusion names "updating the KV cache while transforming key and
-    value tensors"; §Paged Attention Kernels fixes the storage as fixed-size
+    §Operator Fusion counts the KV-cache update made as keys and values are
+    transformed among its fusion targets; §Paged Attention Kernels fixes the
+    storage as fixed-size
     blocks addressed through a table.  Token n with slot s >= 0 lands in
     physical block s // bs at offset s % bs.  Cache layouts (the library's):
     k_cache [NB, Hkv, bs, D] and v_cache [NB, Hkv, D, bs] (values stored

@@ -1,7 +1,8 @@
 // Copy of whole paged-cache blocks: the copy-on-write step of prefix sharing.
 //
 // "Fast Attention Kernels and Operator Fusion", §Paged Attention Kernels:
-// blocks are shared when sequences have a common prefix.  A sequence that
+// sequences that begin with the same tokens may hold the same blocks.  A
+// sequence that
 // appends into a partly filled shared block first gets its own copy of that
 // block (attn_seq_reserve_cow names the pair); this kernel makes the copies.
 // One (block, pool) is contiguous, [Hkv][16][D] for keys and [Hkv][D][16]

@@ -1,10 +1,11 @@
 // Paged decode for gfx950: one query token per sequence against its paged
 // KV cache, split into partitions of the context that are merged in the same launch.
 //
-// "Fast Attention Kernels and Operator Fusion": decode has one or a few new
-// queries per request and is dominated by reading the growing KV cache
-// (§FlashAttention-Style Kernels); the kernel follows the block table and
-// cannot assume K[t+1] sits next to K[t] (§Paged Attention Kernels).  The
+// "Fast Attention Kernels and Operator Fusion": a decode step brings only a
+// query or two per request, so its cost is the read of the ever longer KV
+// cache (§FlashAttention-Style Kernels); the kernel goes through the block
+// table and never takes K[t+1] to follow K[t] in memory (§Paged Attention
+// Kernels).  The
 // partition statistics are the running max and sum of the online softmax,
 // merged exactly by rescaling each partition with exp(m_p - max m).
 //

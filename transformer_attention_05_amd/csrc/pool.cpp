@@ -1,10 +1,10 @@
 // Host block pool and block-table growth.
 //
 // "Fast Attention Kernels and Operator Fusion", §Paged Attention Kernels: the
-// KV cache is split into fixed-size blocks that are allocated on demand,
-// returned to a pool when a request ends and shared between sequences with a
-// common prefix; a sequence's block table maps its logical blocks to physical
-// ones.  The pool is a LIFO stack of free ids plus one reference count per
+// KV cache is cut into fixed-size blocks, handed out as requests grow, given
+// back when a request finishes, and possibly held by several sequences that
+// begin with the same tokens; a sequence's block table maps its logical
+// blocks to physical ones.  The pool is a LIFO stack of free ids plus one reference count per
 // block.  All operations validate completely before changing anything.
 
 #include <cstdint>

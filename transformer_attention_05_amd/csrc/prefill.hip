@@ -1,9 +1,10 @@
 // Prefill attention for gfx950: O = softmax(Q K^T * scale + M) V computed
 // tile by tile with an online softmax, as "Fast Attention Kernels and
 // Operator Fusion" (§FlashAttention-Style Kernels) describes FlashAttention:
-// each workgroup owns a tile of queries, walks the key/value tiles, forms a
-// block of scores, updates the running row max and row sum and accumulates
-// the output on chip.  The Tq x Tk score matrix never reaches HBM.
+// a workgroup owns a tile of queries and walks the key/value tiles; per tile
+// it forms the scores, folds them into the running row max and row sum, and
+// adds their share to the output kept on chip.  The Tq x Tk score matrix
+// never reaches HBM.
 //
 // bf16 path (both contractions on MFMA, fp32 accumulate):
 //   * workgroup = HPW query heads of one kv group x WPH wavefronts; each

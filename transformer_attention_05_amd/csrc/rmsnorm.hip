@@ -3,9 +3,9 @@
 // "Fast Attention Kernels and Operator Fusion", §Operator Fusion: adding the
 // residual and applying RMSNorm is a fusion target; its example adds the
 // residual to the input, divides each row by the root mean square of the sum
-// (eps under the root) and scales by a weight vector, returning the
-// normalised rows and the updated residual.  A fused kernel reads each input
-// once and writes the two outputs: HBM-bound, one pass.
+// (eps under the root) and scales by a weight vector; it has two outputs,
+// the normalised rows and the new residual.  Fused, one pass reads every
+// input once and writes both: HBM-bound.
 //
 // One wavefront per row (four rows per workgroup, no barriers): lane l holds
 // the 8-element chunks l, l + 64, ... of the row in registers (CPL chunks at
