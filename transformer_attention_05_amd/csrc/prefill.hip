@@ -21,7 +21,9 @@
 //     permuted order.  Each lane owns one query of O^T, so the rescale by
 //     exp(m_old - m_new) is lane-local.
 //   * software pipeline: the MFMAs of S(j+1) run interleaved with the
-//     exponentials of S(j), the PV MFMAs of tile j with the row max of S(j+1).
+//     exponentials of S(j), the PV MFMAs of tile j with the row max of S(j+1);
+//     the running-max update for S(j+1) waits until the MFMAs of S(j+2) are
+//     issued.
 //   * K/V tiles of 64 keys cycle through LDS rings fed by global->LDS DMA one
 //     or two iterations ahead.  With 4 wavefronts a workgroup needs 80 KiB,
 //     so two workgroups share a CU and overlap each other's phases.
@@ -439,9 +441,13 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // from S(cur).  Eight chunks; each issues NS/8 MFMAs, reads the K operands
   // of the next chunk and does half a key step of the exponentials.
   // sched_barrier(0) between chunks keeps the operand registers bounded.
+  // before_exp runs once the first chunk's MFMAs are issued: the running
+  // max update for S(cur) (its row max comes from the previous phase B), so
+  // the max's cross-lane step, vote and branch overlap those MFMAs instead
+  // of ending the previous iteration.
   constexpr int SPC = NS / 8;  // S MFMAs per chunk
-  auto phase_a = [&](const __bf16* sk, const f32x16 (&s)[2], f32x16 (&sn)[2]) {
-    float lsum = l_run;
+  auto phase_a = [&](const __bf16* sk, const f32x16 (&s)[2], f32x16 (&sn)[2], auto&& before_exp) {
+    float lsum = 0.f;
     bf16x8 kcur[SPC], knxt[SPC];
 #pragma unroll
     for (int u = 0; u < SPC; ++u) kcur[u] = k_op(sk, u & 1, u >> 1);
@@ -460,19 +466,24 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         const int c = m >> 1, kt = m & 1;
         sn[kt] = mfma32(kcur[u], qreg[c], c == 0 ? f32x16{} : sn[kt]);
       }
+      if (q == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+        before_exp();
+        lsum = l_run;
+      }
       exp_half(s, q >> 1, q & 1, lsum);
-      // keep the exponentials in this chunk: without a use here, code motion
-      // above the scheduler sinks them to the PV product that consumes them
       if (q & 1) asm volatile("" : "+v"(pb[q >> 1]));
       if constexpr (MASKED) {
         if (q & 1) asm volatile("" : "+v"(pl[q >> 1]));
       }
       asm volatile("" : "+v"(lsum));
+      if (q > 0) {
 #pragma unroll
-      for (int u = 0; u < SPC; ++u) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if (q < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (next chunk)
-        __builtin_amdgcn_sched_group_barrier(0x002, 12 / SPC, 0);  // VALU
+        for (int u = 0; u < SPC; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          if (q < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (next chunk)
+          __builtin_amdgcn_sched_group_barrier(0x002, 12 / SPC, 0);  // VALU
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       if (q < 7) {
@@ -653,6 +664,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // masked, so it changes nothing and the loop body has a single form.
   // r0, r1, r2 = j % 3, (j + 1) % 3, (j + 2) % 3.
   int r0 = 0, r1 = 1, r2 = 2;
+  float pend = -INFINITY;  // row max of the newest S, applied at the start of the next phase A
   auto iteration = [&](int j, const f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int vcur = NVB == 3 ? r0 : (j & 1);  // ring buffer of V(j)
     const int vnext = NVB == 3 ? r1 : (vcur ^ 1);  // of V(j+1)
@@ -673,11 +685,10 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       }
       tile_blocks(T0 + min(j + 4, n_tiles - 1), blk_k);
     }
-    phase_a(kring + r1 * TILE, sc, sn);
+    phase_a(kring + r1 * TILE, sc, sn, [&]() { update_max(fmaxf(pend, xor32(pend))); });
     if (MASKED || needs_mask(T0 + j + 1)) mask_tile(sn, T0 + j + 1);
-    float tmax = -INFINITY;
-    phase_b(vring + vcur * TILE, sn, tmax);
-    update_max(fmaxf(tmax, xor32(tmax)));
+    pend = -INFINITY;
+    phase_b(vring + vcur * TILE, sn, pend);
     tile_barrier();
     if (tail_tile(T0 + j + 1)) {
       zero_tail(vring + vnext * TILE, T0 + j + 1);
