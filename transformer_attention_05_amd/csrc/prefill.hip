@@ -34,7 +34,8 @@
 //     receives an equal share of heavy and light tiles; workgroups that start
 //     together walk the same key tiles, so K/V is still shared in each L2.
 //   * P is rounded to bf16 for the PV MFMA and the row sum l accumulates the
-//     same rounded values, so the output weights stay exactly normalised.
+//     same rounded values (v_dot2 in the PV phase, whose VALU is otherwise
+//     idle), so the output weights stay exactly normalised.
 // The paged variant is the same loop with K/V rows gathered through the
 // block table (16-token blocks): token t of sequence s lives in block
 // block_table[s][t / 16] at offset t % 16.  Its V^T tile stays block-major
@@ -376,8 +377,6 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NC = D / 16;        // contraction steps of S (16 channels each)
   constexpr int NS = 2 * NC;        // S MFMAs per tile
   constexpr int NP = 4 * (D / 32);  // PV MFMAs per tile
-  constexpr int EXP_VALU = 96;      // 32 x (fma + exp) + 16 cvt + 16 dot2 per lane per tile
-  constexpr int VPS = EXP_VALU / NS;
 
   // K operand of S^T = K Q^T: row kt*32 + lq, channels 16c + 8hh .. +7
   auto k_op = [&](const __bf16* sk, int kt, int c) -> bf16x8 {
@@ -419,7 +418,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   };
   // P = 2^(S c2 - m c2) for half h of key step kc, rounded to bf16, and
   // the row sum of exactly those rounded weights
-  auto exp_half = [&](const f32x16 (&s)[2], int kc, int h, float& lsum) {
+  auto exp_half = [&](const f32x16 (&s)[2], int kc, int h) {
 #pragma unroll
     for (int i = 4 * h; i < 4 * h + 4; ++i) {
       const float p = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], c2, -mc));
@@ -427,13 +426,17 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       // p - bf16(p) is exact in fp32
       if constexpr (MASKED) pl[kc][i] = static_cast<__bf16>(p - static_cast<float>(pb[kc][i]));
     }
+  };
+  // the row sum of exactly the rounded weights of key step kc (and of their
+  // remainders, MASKED), in the order the weights were formed
+  auto row_sum = [&](int kc) {
 #pragma unroll
-    for (int i = 2 * h; i < 2 * h + 2; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const bf16x2 pr = {pb[kc][2 * i], pb[kc][2 * i + 1]};
-      lsum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum, false);
+      l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
       if constexpr (MASKED) {
         const bf16x2 pq = {pl[kc][2 * i], pl[kc][2 * i + 1]};
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pq, ones, lsum, false);
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pq, ones, l_run, false);
       }
     }
   };
@@ -447,7 +450,6 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // of ending the previous iteration.
   constexpr int SPC = NS / 8;  // S MFMAs per chunk
   auto phase_a = [&](const __bf16* sk, const f32x16 (&s)[2], f32x16 (&sn)[2], auto&& before_exp) {
-    float lsum = 0.f;
     bf16x8 kcur[SPC], knxt[SPC];
 #pragma unroll
     for (int u = 0; u < SPC; ++u) kcur[u] = k_op(sk, u & 1, u >> 1);
@@ -469,20 +471,18 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       if (q == 0) {
         __builtin_amdgcn_sched_barrier(0);
         before_exp();
-        lsum = l_run;
       }
-      exp_half(s, q >> 1, q & 1, lsum);
+      exp_half(s, q >> 1, q & 1);
       if (q & 1) asm volatile("" : "+v"(pb[q >> 1]));
       if constexpr (MASKED) {
         if (q & 1) asm volatile("" : "+v"(pl[q >> 1]));
       }
-      asm volatile("" : "+v"(lsum));
       if (q > 0) {
 #pragma unroll
         for (int u = 0; u < SPC; ++u) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
           if (q < 7) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read (next chunk)
-          __builtin_amdgcn_sched_group_barrier(0x002, 12 / SPC, 0);  // VALU
+          __builtin_amdgcn_sched_group_barrier(0x002, 10 / SPC, 0);  // VALU
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -491,7 +491,6 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         for (int u = 0; u < SPC; ++u) kcur[u] = knxt[u];
       }
     }
-    l_run = lsum;
   };
   // Phase B: O^T += V^T P^T, one key step per chunk, V^T operands read a
   // chunk ahead; the VALU takes the row max of S(next) meanwhile.
@@ -513,11 +512,12 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, sn[kc >> 1][8 * (kc & 1) + r]);
+      row_sum(kc);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         __builtin_amdgcn_sched_group_barrier(0x008, MASKED ? 2 : 1, 1);  // MFMA
         if (kc < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // DS reads (next chunk)
-        __builtin_amdgcn_sched_group_barrier(0x002, 1, 1);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 3 : 2, 1);  // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kc < 3) {
