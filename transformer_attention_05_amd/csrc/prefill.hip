@@ -23,7 +23,9 @@
 //   * software pipeline: the MFMAs of S(j+1) run interleaved with the
 //     exponentials of S(j), the PV MFMAs of tile j with the row max of S(j+1);
 //     the running-max update for S(j+1) waits until the MFMAs of S(j+2) are
-//     issued.
+//     issued.  The exponent of each score, s * scale * log2 e - m, is formed
+//     in place in the PV phase, whose VALU is otherwise nearly idle; when the
+//     max update moves m, it shifts those exponents by the change.
 //   * K/V tiles of 64 keys cycle through LDS rings fed by global->LDS DMA one
 //     or two iterations ahead.  With 4 wavefronts a workgroup needs 80 KiB,
 //     so two workgroups share a CU and overlap each other's phases.
@@ -421,7 +423,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   auto exp_half = [&](const f32x16 (&s)[2], int kc, int h) {
 #pragma unroll
     for (int i = 4 * h; i < 4 * h + 4; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[kc >> 1][8 * (kc & 1) + i], c2, -mc));
+      const float p = __builtin_amdgcn_exp2f(s[kc >> 1][8 * (kc & 1) + i]);
       pb[kc][i] = static_cast<__bf16>(p);
       // p - bf16(p) is exact in fp32
       if constexpr (MASKED) pl[kc][i] = static_cast<__bf16>(p - static_cast<float>(pb[kc][i]));
@@ -495,7 +497,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // Phase B: O^T += V^T P^T, one key step per chunk, V^T operands read a
   // chunk ahead; the VALU takes the row max of S(next) meanwhile.
   constexpr int DT = D / 32;
-  auto phase_b = [&](const __bf16* sv, const f32x16 (&sn)[2], float& tmax) {
+  auto phase_b = [&](const __bf16* sv, f32x16 (&sn)[2], float& tmax) {
     bf16x8 vcur[DT], vnxt[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vcur[dt] = v_op(sv, dt, 0);
@@ -512,12 +514,17 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < 8; ++r) tmax = fmaxf(tmax, sn[kc >> 1][8 * (kc & 1) + r]);
+      // the exponent of the next tile, s * scale * log2 e - m (log2 units),
+      // formed here where the VALU is idle; the max update at the start of
+      // the next phase A corrects it when m moves
+#pragma unroll
+      for (int r = 0; r < 8; ++r) sn[kc >> 1][8 * (kc & 1) + r] = fmaf(sn[kc >> 1][8 * (kc & 1) + r], c2, -mc);
       row_sum(kc);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         __builtin_amdgcn_sched_group_barrier(0x008, MASKED ? 2 : 1, 1);  // MFMA
         if (kc < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);  // DS reads (next chunk)
-        __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 3 : 2, 1);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, MASKED ? 5 : 4, 1);  // VALU
       }
       __builtin_amdgcn_sched_barrier(0);
       if (kc < 3) {
@@ -590,7 +597,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     return fmaxf(tmax, xor32(tmax));
   };
   // online softmax: the reference max moves only when it grows by > 2^8
-  auto update_max = [&](float tmax) {
+  auto update_max = [&](float tmax, f32x16* formed) {
     if (__any(tmax > m_run + tau_raw)) {
       const float m_new = fmaxf(m_run, tmax);
       const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c2);
@@ -598,7 +605,14 @@ void prefill_bf16_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) oacc[dt] *= alpha;
       m_run = m_new;
-      mc = (m_run == -INFINITY ? 0.f : m_run) * c2;
+      const float mc_new = (m_run == -INFINITY ? 0.f : m_run) * c2;
+      if (formed != nullptr) {
+        // exponents formed with the old reference: shift them to the new one
+        const float dm = mc_new - mc;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) formed[kt] -= dm;
+      }
+      mc = mc_new;
     }
   };
   // DMA instructions of the current iteration that may still be in flight
@@ -648,7 +662,11 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     if (tail_tile(T0)) zero_tail(vring, T0);
     s_mfma(kring, sa);
     if (MASKED || needs_mask(T0)) mask_tile(sa, T0);
-    update_max(row_max(sa));
+    update_max(row_max(sa), nullptr);
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sa[kt][r] = fmaf(sa[kt][r], c2, -mc);
     __syncthreads();
   }
   // Q^T is in registers by now (the wait above retired its loads), but the
@@ -665,7 +683,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // r0, r1, r2 = j % 3, (j + 1) % 3, (j + 2) % 3.
   int r0 = 0, r1 = 1, r2 = 2;
   float pend = -INFINITY;  // row max of the newest S, applied at the start of the next phase A
-  auto iteration = [&](int j, const f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  auto iteration = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     const int vcur = NVB == 3 ? r0 : (j & 1);  // ring buffer of V(j)
     const int vnext = NVB == 3 ? r1 : (vcur ^ 1);  // of V(j+1)
     if constexpr (NVB == 3) {
@@ -685,7 +703,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       }
       tile_blocks(T0 + min(j + 4, n_tiles - 1), blk_k);
     }
-    phase_a(kring + r1 * TILE, sc, sn, [&]() { update_max(fmaxf(pend, xor32(pend))); });
+    phase_a(kring + r1 * TILE, sc, sn, [&]() { update_max(fmaxf(pend, xor32(pend)), sc); });
     if (MASKED || needs_mask(T0 + j + 1)) mask_tile(sn, T0 + j + 1);
     pend = -INFINITY;
     phase_b(vring + vcur * TILE, sn, pend);
