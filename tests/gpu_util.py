@@ -46,6 +46,28 @@ def bf16_ulp(x):
     return np.exp2(np.floor(np.log2(x)) - 7)
 
 
+def check_bf16_output(out, ref, what=""):
+    """A bf16 output against the exact value at the bf16 bar: max |err| <=
+    1e-2 on every element with |O| < 4, mean |err| <= 1e-3 over all.  Where
+    |O| >= 4 no bf16 number is guaranteed within 1e-2 of the exact value
+    (half an ulp there is 1/64), so those elements must be faithfully
+    rounded: one of the two bf16 neighbours of the exact value, i.e. less
+    than one ulp away."""
+    out = np.asarray(out, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert np.all(np.isfinite(out)), f"{what}: non-finite output"
+    err = np.abs(out - ref)
+    small = np.abs(ref) < 4.0
+    mx = float(err[small].max()) if small.any() else 0.0
+    big = ~small
+    worst = float((err[big] / bf16_ulp(ref[big])).max()) if big.any() else 0.0
+    say(f"  {what}: max |err| {mx:.3e} where |O| < 4, mean |err| {err.mean():.3e}; "
+        f"{int(big.sum())} elements with |O| >= 4, worst err/ulp {worst:.3f}")
+    assert mx <= BF16_MAX, f"{what}: max err {mx:.3e} > {BF16_MAX} where |O| < 4"
+    assert err.mean() <= BF16_MEAN, f"{what}: mean err {err.mean():.3e} > {BF16_MEAN}"
+    assert worst < 1.0, f"{what}: an element with |O| >= 4 is not faithfully rounded ({worst:.3f} ulp)"
+
+
 def check_stored(out, exact, dtype, what=""):
     """Values the method computes in fp32 and stores in `dtype` (rotated q
     and k): compared with the exact fp64 value.  bf16 storage: at most half a

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import transformer_attention_05_amd as mi
-from tests.gpu_util import DEV, check, f64, say
+from tests.gpu_util import DEV, check, check_bf16_output, f64, say
 from workloads import prefill_case, rng, to_f64
 
 pytestmark = [pytest.mark.gpu,
@@ -105,6 +105,49 @@ def test_ragged_shapes(case, dtype):
     ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=causal)
     check(f64(o), ref, dtype, f"ragged {case}")
     check_lse(f64(lse), ref_lse, dtype, "ragged")
+
+
+# Key counts a multiple of the 64-key tile at D 128 (bf16, no mask): every key
+# tile is whole, and the kernel issues each K tile's loads spread over the
+# preceding tile's PV phase.  Fewer key tiles than the ring is deep, one query
+# row, tq < tk and tq > tk, non-causal, MHA (odd group: the 1 x 4 tile) and
+# batches of two.
+WHOLE_TILE_CASES = [
+    # (batch, tq, tk, hq, hkv, causal)
+    (2, 64, 64, 12, 2, True),
+    (1, 128, 192, 6, 1, True),
+    (1, 1, 1024, 12, 2, True),
+    (2, 256, 256, 5, 5, False),
+    (1, 100, 640, 4, 2, False),
+    (1, 700, 320, 12, 2, False),
+    (2, 511, 1024, 12, 2, True),
+]
+
+
+@pytest.mark.parametrize("case", WHOLE_TILE_CASES, ids=[f"b{c[0]}_tq{c[1]}_tk{c[2]}_h{c[3]}x{c[4]}_{'c' if c[5] else 'nc'}"
+                                                        for c in WHOLE_TILE_CASES])
+def test_whole_key_tiles(case):
+    b, tq, tk, hq, hkv, causal = case
+    say(f"case: whole key tiles {case}")
+    q, k, v = prefill_case(5000 + WHOLE_TILE_CASES.index(case), b, tq, hq, hkv, 128, torch.bfloat16, seqlen_k=tk)
+    o, lse = run(q, k, v, causal=causal, want_lse=True)
+    ref, ref_lse = oracle.attention(to_f64(q), to_f64(k), to_f64(v), causal=causal)
+    check_bf16_output(f64(o), ref, f"whole tiles {case}")
+    check_lse(f64(lse), ref_lse, torch.bfloat16, "whole tiles")
+
+
+def test_whole_key_tiles_head_major_strides():
+    """(B, H, T, D) = (2, 8, 512, 128) passed through strides (head-major),
+    causal: the spread K loads with token strides other than H*D."""
+    say("case: whole key tiles, head-major")
+    g = rng(8)
+    shape = (2, 8, 512, 128)
+    q, k, v = (torch.from_numpy(g.standard_normal(shape, dtype=np.float32)).to(torch.bfloat16) for _ in range(3))
+    qd, kd, vd = (t.to(DEV).transpose(1, 2) for t in (q, k, v))
+    o = mi.attn_prefill(qd, kd, vd, causal=True)
+    torch.cuda.synchronize()
+    ref, _ = oracle.attention(to_f64(q.transpose(1, 2)), to_f64(k.transpose(1, 2)), to_f64(v.transpose(1, 2)))
+    check_bf16_output(f64(o), ref, "head-major D 128")
 
 
 SPLIT_CASES = [

@@ -110,8 +110,13 @@ __device__ __forceinline__ int vt_swz(int d) {   // V^T rows (paged): the two 16
 // Tile geometry: HPW query heads share every K/V tile (same kv head under
 // GQA); each head has WPH wavefronts of 32 queries.  MASKED adds the caller's
 // additive mask M to every score and carries the weights P of the PV
-// product as a bf16 pair (rounded value and rounded remainder).
-template <int D, bool PAGED, int HPW, int WPH, bool MASKED = false, bool DEEP_V = false>
+// product as a bf16 pair (rounded value and rounded remainder).  K_SPREAD
+// (contiguous, unmasked, D 128, two-deep V ring, every key tile whole: the
+// key count a multiple of the tile) issues each K tile's DMAs one per PV
+// chunk of the iteration instead of all at its top, so their issue overlaps
+// the matrix work; the DMA stream keeps its order (V(j+1), then K(j+3)), so
+// every wait on it holds.
+template <int D, bool PAGED, int HPW, int WPH, bool MASKED = false, bool DEEP_V = false, bool K_SPREAD = false>
 __global__ __launch_bounds__(64 * HPW * WPH) __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
 void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NW = HPW * WPH;
@@ -129,6 +134,8 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // (96 KiB) for a paged launch that shares the GPU with a decode: one such
   // workgroup per CU leaves the rest of the CU to a decode workgroup.
   constexpr int NVB = (NW == 4 && !DEEP_V) ? 2 : 3;
+  static_assert(!K_SPREAD || (D == 128 && !PAGED && !MASKED && NVB == 2 && LPW == 4),
+                "K_SPREAD: contiguous, unmasked, D 128, two-deep V ring (one K DMA per PV chunk)");
   // MASKED: a two-slot ring of mask tiles after the K/V rings, one 32-row x
   // BN-key fp32 sub-tile per wavefront and slot (144 KiB in all at D 128:
   // one workgroup per CU, which also gives the masked variant's extra
@@ -497,7 +504,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // Phase B: O^T += V^T P^T, one key step per chunk, V^T operands read a
   // chunk ahead; the VALU takes the row max of S(next) meanwhile.
   constexpr int DT = D / 32;
-  auto phase_b = [&](const __bf16* sv, f32x16 (&sn)[2], float& tmax) {
+  auto phase_b = [&](const __bf16* sv, f32x16 (&sn)[2], float& tmax, auto&& per_chunk) {
     bf16x8 vcur[DT], vnxt[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vcur[dt] = v_op(sv, dt, 0);
@@ -520,6 +527,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) sn[kc >> 1][8 * (kc & 1) + r] = fmaf(sn[kc >> 1][8 * (kc & 1) + r], c2, -mc);
       row_sum(kc);
+      per_chunk(kc);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         __builtin_amdgcn_sched_group_barrier(0x008, MASKED ? 2 : 1, 1);  // MFMA
@@ -691,7 +699,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       issue_v(vring + r2 * TILE, T0 + min(j + 2, n_tiles - 1), blk_v);
     } else {
       issue_v(vring + vnext * TILE, T0 + min(j + 1, n_tiles - 1), blk_v1);
-      issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
+      if constexpr (!K_SPREAD) issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
     }
     // slot from the tile's own index, source clamped like the K/V tiles
     issue_mask(T0 + j + 2, T0 + min(j + 2, n_tiles - 1));
@@ -706,7 +714,13 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     phase_a(kring + r1 * TILE, sc, sn, [&]() { update_max(fmaxf(pend, xor32(pend)), sc); });
     if (MASKED || needs_mask(T0 + j + 1)) mask_tile(sn, T0 + j + 1);
     pend = -INFINITY;
-    phase_b(vring + vcur * TILE, sn, pend);
+    phase_b(vring + vcur * TILE, sn, pend, [&](int kc) {
+      if constexpr (K_SPREAD) {
+        // K(j+3), a whole tile: this wavefront's DMA kc of it
+        const __bf16* tb = kb0 + (int64_t)((T0 + min(j + 3, n_tiles - 1)) * BN) * a.ks_t;
+        dma16s(tb + krow[kc], koff[kc], lds_of(kring + r0 * TILE) + (wave * LPW + kc) * 1024);
+      }
+    });
     tile_barrier();
     if (tail_tile(T0 + j + 1)) {
       zero_tail(vring + vnext * TILE, T0 + j + 1);
@@ -1014,7 +1028,15 @@ static void launch_one(const PrefillArgs& a, bool deep_v, hipStream_t s) {
       return;
     }
   }
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, HPW, WPH>), grid, dim3(64 * HPW * WPH), 0, s, a);
+  bool spread = false;
+  if constexpr (D == 128 && !PAGED && HPW * WPH == 4) {
+    // every key tile whole: the K DMAs spread over the PV phase
+    spread = a.tk % BN == 0;
+    if (spread)
+      hipLaunchKernelGGL((prefill_bf16_kernel<D, false, HPW, WPH, false, false, true>), grid, dim3(64 * HPW * WPH), 0,
+                         s, a);
+  }
+  if (!spread) hipLaunchKernelGGL((prefill_bf16_kernel<D, PAGED, HPW, WPH>), grid, dim3(64 * HPW * WPH), 0, s, a);
   if (a.num_splits > 1)
     hipLaunchKernelGGL((prefill_merge_kernel<D, PAGED, HPW, WPH>), dim3(a.num_wg * merge_parts<D, HPW, WPH>()),
                        dim3(256), 0, s, a);
