@@ -110,13 +110,14 @@ __device__ __forceinline__ int vt_swz(int d) {   // V^T rows (paged): the two 16
 // Tile geometry: HPW query heads share every K/V tile (same kv head under
 // GQA); each head has WPH wavefronts of 32 queries.  MASKED adds the caller's
 // additive mask M to every score and carries the weights P of the PV
-// product as a bf16 pair (rounded value and rounded remainder).  K_SPREAD
+// product as a bf16 pair (rounded value and rounded remainder).  SPREAD
 // (contiguous, unmasked, D 128, two-deep V ring, every key tile whole: the
-// key count a multiple of the tile) issues each K tile's DMAs one per PV
-// chunk of the iteration instead of all at its top, so their issue overlaps
+// key count a multiple of the tile) issues an iteration's tile DMAs inside
+// its two phases instead of all at its top, V(j+1) one per odd chunk of the
+// S phase and K(j+3) one per chunk of the PV phase, so their issue overlaps
 // the matrix work; the DMA stream keeps its order (V(j+1), then K(j+3)), so
 // every wait on it holds.
-template <int D, bool PAGED, int HPW, int WPH, bool MASKED = false, bool DEEP_V = false, bool K_SPREAD = false>
+template <int D, bool PAGED, int HPW, int WPH, bool MASKED = false, bool DEEP_V = false, bool SPREAD = false>
 __global__ __launch_bounds__(64 * HPW * WPH) __attribute__((amdgpu_waves_per_eu(MASKED ? 1 : 2)))
 void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NW = HPW * WPH;
@@ -134,8 +135,8 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // (96 KiB) for a paged launch that shares the GPU with a decode: one such
   // workgroup per CU leaves the rest of the CU to a decode workgroup.
   constexpr int NVB = (NW == 4 && !DEEP_V) ? 2 : 3;
-  static_assert(!K_SPREAD || (D == 128 && !PAGED && !MASKED && NVB == 2 && LPW == 4),
-                "K_SPREAD: contiguous, unmasked, D 128, two-deep V ring (one K DMA per PV chunk)");
+  static_assert(!SPREAD || (D == 128 && !PAGED && !MASKED && NVB == 2 && LPW == 4),
+                "SPREAD: contiguous, unmasked, D 128, two-deep V ring (four DMAs of each tile per wavefront)");
   // MASKED: a two-slot ring of mask tiles after the K/V rings, one 32-row x
   // BN-key fp32 sub-tile per wavefront and slot (144 KiB in all at D 128:
   // one workgroup per CU, which also gives the masked variant's extra
@@ -458,7 +459,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
   // the max's cross-lane step, vote and branch overlap those MFMAs instead
   // of ending the previous iteration.
   constexpr int SPC = NS / 8;  // S MFMAs per chunk
-  auto phase_a = [&](const __bf16* sk, const f32x16 (&s)[2], f32x16 (&sn)[2], auto&& before_exp) {
+  auto phase_a = [&](const __bf16* sk, const f32x16 (&s)[2], f32x16 (&sn)[2], auto&& before_exp, auto&& per_chunk) {
     bf16x8 kcur[SPC], knxt[SPC];
 #pragma unroll
     for (int u = 0; u < SPC; ++u) kcur[u] = k_op(sk, u & 1, u >> 1);
@@ -482,6 +483,7 @@ void prefill_bf16_kernel(const PrefillArgs a) {
         before_exp();
       }
       exp_half(s, q >> 1, q & 1);
+      per_chunk(q);
       if (q & 1) asm volatile("" : "+v"(pb[q >> 1]));
       if constexpr (MASKED) {
         if (q & 1) asm volatile("" : "+v"(pl[q >> 1]));
@@ -697,9 +699,9 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     if constexpr (NVB == 3) {
       issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
       issue_v(vring + r2 * TILE, T0 + min(j + 2, n_tiles - 1), blk_v);
-    } else {
+    } else if constexpr (!SPREAD) {
       issue_v(vring + vnext * TILE, T0 + min(j + 1, n_tiles - 1), blk_v1);
-      if constexpr (!K_SPREAD) issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
+      issue_k(kring + r0 * TILE, T0 + min(j + 3, n_tiles - 1), blk_k);
     }
     // slot from the tile's own index, source clamped like the K/V tiles
     issue_mask(T0 + j + 2, T0 + min(j + 2, n_tiles - 1));
@@ -711,11 +713,19 @@ void prefill_bf16_kernel(const PrefillArgs a) {
       }
       tile_blocks(T0 + min(j + 4, n_tiles - 1), blk_k);
     }
-    phase_a(kring + r1 * TILE, sc, sn, [&]() { update_max(fmaxf(pend, xor32(pend)), sc); });
+    phase_a(kring + r1 * TILE, sc, sn, [&]() { update_max(fmaxf(pend, xor32(pend)), sc); }, [&](int q) {
+      if constexpr (SPREAD) {
+        if (q & 1) {  // V(j+1), a whole tile: this wavefront's DMA q/2 of it
+          const int i = q >> 1;
+          const __bf16* tb = vb0 + (int64_t)((T0 + min(j + 1, n_tiles - 1)) * BN) * a.vs_t;
+          dma16s(tb + vrow[i], voff[i], lds_of(vring + vnext * TILE) + (wave * LPW + i) * 1024);
+        }
+      }
+    });
     if (MASKED || needs_mask(T0 + j + 1)) mask_tile(sn, T0 + j + 1);
     pend = -INFINITY;
     phase_b(vring + vcur * TILE, sn, pend, [&](int kc) {
-      if constexpr (K_SPREAD) {
+      if constexpr (SPREAD) {
         // K(j+3), a whole tile: this wavefront's DMA kc of it
         const __bf16* tb = kb0 + (int64_t)((T0 + min(j + 3, n_tiles - 1)) * BN) * a.ks_t;
         dma16s(tb + krow[kc], koff[kc], lds_of(kring + r0 * TILE) + (wave * LPW + kc) * 1024);
