@@ -68,7 +68,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // completion is ordered by the explicit vmcnt waits before the barriers that
 // publish a tile, and the LDS ring buffers can then live in one array
 // addressed by a uniform buffer offset.
-// `lds` is the LDS byte address (uniform).
+// `lds` is the LDS byte address (uniform); the instruction takes it in M0.
+// The compiler warns that M0, a register it reserves, is clobbered here: in
+// these kernels nothing else uses M0 (every M0 write in their ISA is one of
+// these DMAs), so no value of the compiler's lives in it across the asm.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   lds = __builtin_amdgcn_readfirstlane(lds);
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds) : "memory", "m0");
