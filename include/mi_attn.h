@@ -248,8 +248,9 @@ ATTN_API int attn_prefill_paged_masked(const void* q, const void* k_cache, const
  *   context_lens device int32 [num_seqs], 1 .. max_context_len (the new
  *                token included)
  *   o            device [num_seqs][num_q_heads][head_dim], written
- *   partition_size: 0 = automatic; else BF16: a multiple of 128, at most
- *                1024; F32: a multiple of 16, at most 65536.
+ *   partition_size: 0 = automatic; else a multiple of 16 (whole blocks), at
+ *                most 1024 for BF16 (one block-table entry per lane of a
+ *                wavefront) and 65536 for F32.
  *   plan         optional device int32 [plan_items][2]: the (sequence,
  *                partition) pairs that attn_decode_paged_plan lists for the
  *                same context lengths, max_context_len, num_kv_heads and

@@ -223,7 +223,8 @@ def decode(lib, **kw):
     (dict(dtype=7), ATTN_E_UNSUPPORTED),
     (dict(maxb=7), ATTN_E_INVALID),             # 128 tokens need 8 blocks
     (dict(part=100), ATTN_E_INVALID),
-    (dict(part=48), ATTN_E_INVALID),            # bf16 partitions: multiples of 128
+    (dict(part=40), ATTN_E_INVALID),            # partitions: multiples of 16
+    (dict(part=1024 + 16), ATTN_E_INVALID),     # bf16 partitions: at most 1024
     (dict(part=40, dtype=ATTN_F32), ATTN_E_INVALID),      # fp32 partitions: multiples of 16
     (dict(part=65536 + 16, dtype=ATTN_F32), ATTN_E_INVALID),
     (dict(part=-128), ATTN_E_INVALID),
@@ -243,8 +244,8 @@ def test_decode_rejects(lib, kw, status):
 
 
 def test_decode_f32_partition_sizes_accepted_by_the_plan():
-    """fp32 decodes take any multiple of 16 as partition size; the host plan
-    lists their partitions (bf16 launches still check multiples of 128)."""
+    """Decodes take any multiple of 16 as partition size (bf16 up to 1024);
+    the host plan lists their partitions."""
     lens = np.array([1, 16, 17, 100], np.int32)
     items = mi.attn_decode_paged_plan(lens, 2, 100, 16)
     assert len(items) == 1 + 1 + 2 + 7

@@ -40,10 +40,12 @@ def test_c3_decode():
     check(f64(o), oracle_decode(case), torch.bfloat16, "C3")
 
 
-@pytest.mark.parametrize("part", [128, 256, 512, 1024])
+@pytest.mark.parametrize("part", [16, 32, 48, 128, 256, 512, 1024])
 def test_split_kv_partition_sizes(part):
-    """Merging P partitions equals the single pass, for every partition size;
-    sequences shorter than the longest leave empty partitions in the grid."""
+    """Merging P partitions equals the single pass, for every partition size
+    (16 and 32: one or two blocks, so most wavefronts of a partition have no
+    block); sequences shorter than the longest leave empty partitions in the
+    grid."""
     say(f"case: split-KV partition {part}")
     case = decode_case(31, 24, 1, 4096, lengths=np.array([1, 2, 15, 16, 17, 127, 128, 129, 255, 256, 257, 511, 512,
                                                            513, 1000, 1023, 1024, 1025, 2047, 2048, 3000, 4095, 4096,

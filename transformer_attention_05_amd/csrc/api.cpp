@@ -596,8 +596,8 @@ int decode_common(const char* fn, const DecodeWrite* w, const void* q, const voi
   if (max_blocks_per_seq < ceil_div(max_context_len, kBlockSizeHost))
     return fail(ATTN_E_INVALID, "%s: max_blocks_per_seq %d cannot hold max_context_len %d", fn,
                 max_blocks_per_seq, max_context_len);
-  if (dtype == ATTN_BF16 && (partition_size < 0 || partition_size % 128 != 0 || partition_size > 1024))
-    return fail(ATTN_E_INVALID, "%s: bf16 partition_size must be 0 or a multiple of 128 up to 1024", fn);
+  if (dtype == ATTN_BF16 && (partition_size < 0 || partition_size % 16 != 0 || partition_size > 1024))
+    return fail(ATTN_E_INVALID, "%s: bf16 partition_size must be 0 or a multiple of 16 up to 1024", fn);
   if (dtype == ATTN_F32 && (partition_size < 0 || partition_size % 16 != 0 || partition_size > kMaxF32Partition))
     return fail(ATTN_E_INVALID, "%s: fp32 partition_size must be 0 or a multiple of 16 up to %d", fn,
                 kMaxF32Partition);
