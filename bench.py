@@ -13,11 +13,14 @@ Inputs are synthetic and already resident in HBM when timing starts.
 
 Timing: the headline times --steps steps after --warmup untimed ones,
 between two device synchronisations (eager launches).  Every component
-figure takes 20 untimed calls and then 100 timed calls in samples of 5
+figure takes 20 untimed calls and then 100 timed calls in samples of 20
 back-to-back calls between a pair of HIP events on the launching stream,
-the 5 calls captured once in a HIP graph and replayed per sample (so the
+the 20 calls captured once in a HIP graph and replayed per sample (so the
 binding's host-side cost does not pace short kernels); it reports the
-median (`us`), the min and the mean per call.  The decode roofline uses
+median (`us`), the min and the mean per call.  A graph replay costs about
+22 us before its first kernel starts (measured on MI355X: a replay of one
+near-empty kernel takes 28 us, each further one adds 1.1 us), so a sample
+of 20 calls charges each call about 1.1 us of it.  The decode roofline uses
 the mean (the average launch duration), as the profiler summary does; the
 step is also timed eagerly in samples of 5 and inside the step the decode
 and the chunked prefill are timed by events on their own streams.
@@ -100,7 +103,8 @@ def write_bytes(n_tokens):
 
 # ----------------------------------------------------------------------------- timing helpers
 
-WARM_CALLS, TIMED_CALLS, PER_SAMPLE = 20, 100, 5
+WARM_CALLS, TIMED_CALLS, PER_SAMPLE = 20, 100, 20
+IN_STEP_SAMPLES = 20  # steps timed with events on each stream (one sample each)
 
 
 def timed(torch, fn, warm=None, calls=None, per=PER_SAMPLE, graph=True):
@@ -110,13 +114,15 @@ def timed(torch, fn, warm=None, calls=None, per=PER_SAMPLE, graph=True):
     calls are captured once in a HIP graph and each sample replays it: the
     kernels then run back to back on the GPU whatever the host-side cost of
     a call (the Python binding's argument checks take longer than the
-    shortest kernels), so the figure is the GPU time per call, as a profiler
-    trace reports it.  (An event recorded between two kernels leaves the GPU
-    idle for several microseconds on this stack, so there is no event pair
-    around every single call.)  Returns mean, median and min over the
-    samples, and the call counts."""
+    shortest kernels), so the figure is the GPU time per call plus a share
+    of the replay's start (about 22 us over the `per` calls).  (An event
+    recorded between two kernels leaves the GPU idle for several
+    microseconds on this stack, so there is no event pair around every
+    single call.)  Returns mean, median and min over the samples, and the
+    call counts."""
     warm = WARM_CALLS if warm is None else warm
     calls = TIMED_CALLS if calls is None else calls
+    per = min(per, calls)
     for i in range(warm):
         fn(i)
     torch.cuda.synchronize()
@@ -176,7 +182,7 @@ def main():
                     help="timed calls per component figure (default 100; fewer for profiler runs)")
     ap.add_argument("--warm-calls", type=int, default=WARM_CALLS, help="untimed calls before each figure (default 20)")
     args = ap.parse_args()
-    WARM_CALLS, TIMED_CALLS = max(0, args.warm_calls), max(PER_SAMPLE, args.calls)
+    WARM_CALLS, TIMED_CALLS = max(0, args.warm_calls), max(1, args.calls)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(multi-GPU sharding is a design note, not implemented)"}))
@@ -229,7 +235,7 @@ def main():
         # time to its stream, so these are slight overestimates)
         names = ("prefill0", "prefill1", "decode0", "decode1")
         in_pre, in_dec = [], []
-        for _ in range(WARM_CALLS + TIMED_CALLS // PER_SAMPLE):
+        for _ in range(WARM_CALLS + IN_STEP_SAMPLES):
             marks = {n: torch.cuda.Event(enable_timing=True) for n in names}
             step.run(marks)
             torch.cuda.synchronize()
