@@ -670,9 +670,20 @@ void prefill_bf16_kernel(const PrefillArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) blk_v1[i] = b1[i];
     }
-    __builtin_amdgcn_s_waitcnt(0);   // also retires the Q loads
+    if constexpr (MASKED) {
+      __builtin_amdgcn_s_waitcnt(0);  // also retires the Q loads
+    } else {
+      // Q and K(0) only (the Q loads came first): S(0) overlaps the other
+      // tiles' arrival.  s_waitcnt vmcnt(N) (expcnt, lgkmcnt at no-wait)
+      constexpr int N0 = (NVB == 3 ? 4 : 3) * LPW;  // V(0), K(1), [V(1)], K(2)
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (N0 & 15) | ((N0 >> 4) << 14));
+    }
     __syncthreads();
-    if (tail_tile(T0)) zero_tail(vring, T0);
+    if (tail_tile(T0)) {  // uniform: V(0) is zeroed past the context once it has landed
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      zero_tail(vring, T0);
+    }
     s_mfma(kring, sa);
     if (MASKED || needs_mask(T0)) mask_tile(sa, T0);
     update_max(row_max(sa), nullptr);
@@ -680,6 +691,11 @@ void prefill_bf16_kernel(const PrefillArgs a) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sa[kt][r] = fmaf(sa[kt][r], c2, -mc);
+    if constexpr (!MASKED) {
+      // iteration 0 reads K(1) and V(0); K(2) may still be in flight
+      constexpr int N1 = LPW;
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (N1 & 15) | ((N1 >> 4) << 14));
+    }
     __syncthreads();
   }
   // Q^T is in registers by now (the wait above retired its loads), but the
