@@ -28,7 +28,10 @@
 //     max update moves m, it shifts those exponents by the change.
 //   * K/V tiles of 64 keys cycle through LDS rings fed by global->LDS DMA one
 //     or two iterations ahead.  With 4 wavefronts a workgroup needs 80 KiB,
-//     so two workgroups share a CU and overlap each other's phases.
+//     so two workgroups share a CU and overlap each other's phases.  When
+//     every key tile is whole (contiguous, unmasked, D 128), an iteration's
+//     DMAs are issued inside its two phases rather than at its top.  The
+//     workgroup start waits only for Q and the first K tile.
 //   * causal tiles wholly above the diagonal are never loaded; masking runs
 //     only on tiles that cross the diagonal or the sequence end.
 //   * workgroups are ordered heaviest first (last query tile first).  The
