@@ -373,6 +373,73 @@ ATTN_API int32_t attn_decode_paged_partition_for(const int32_t* context_lens, in
                                         int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim);
 
 /* -------------------------------------------------------------------------
+ * attn_prefill_decode_paged -- a chunked prefill and a decode over the same
+ * paged cache in one launch.
+ *
+ * A serving step runs both regimes the tutorial separates, many queries per
+ * request (prefill, bound by the matrix work) and one (decode, bound by
+ * reading the cache) (§FlashAttention-Style Kernels, §Paged Attention
+ * Kernels).  The two only read the cache (apart from the decode's own new
+ * tokens) and write disjoint outputs, so one grid holds the workgroups of
+ * both: no second stream, no join, and the CUs are shared in an order the
+ * library chooses.  The results are those of attn_prefill_paged (prefill
+ * part) and attn_decode_paged, or attn_decode_paged_rope when the decode part
+ * carries the new tokens, bit for bit.
+ *
+ *   prefill   the chunked prefill: the arguments of attn_prefill_paged
+ *             (num_seqs 0: no prefill part).  It runs on the default tile in
+ *             one pass (no split-KV workspace, no mask).
+ *   decode    the decode: the arguments of attn_decode_paged, its workspace
+ *             and plan contract included (num_seqs 0: no decode part).  With
+ *             k_new, v_new, positions and slot_mapping set (q_rot_out and
+ *             rope_base as for attn_decode_paged_rope) the decode also
+ *             rotates and writes each sequence's new token; all four NULL:
+ *             the new tokens are already in the cache.  A new token's slot
+ *             must not be one that the prefill part reads.
+ *   k_cache, v_cache, num_q_heads, num_kv_heads, head_dim, block_size,
+ *   num_blocks, scale: shared by both parts, as in those calls.
+ *   dtype     BF16 only (ATTN_E_UNSUPPORTED otherwise).
+ * Errors as for the two calls; nothing is launched unless both parts are
+ * valid.  The launch allocates nothing and can be captured in a HIP graph.
+ * ---------------------------------------------------------------------- */
+typedef struct attn_paged_prefill_part {
+  const void* q;                 /* [total_q][num_q_heads][head_dim] */
+  const int32_t* block_table;    /* [num_seqs][max_blocks_per_seq] */
+  int32_t max_blocks_per_seq;
+  const int32_t* cu_seqlens_q;   /* [num_seqs + 1] */
+  const int32_t* context_lens;   /* [num_seqs], new tokens included */
+  void* o;                       /* [total_q][num_q_heads][head_dim] */
+  int32_t num_seqs, total_q, max_seqlen_q, max_context_len;
+  int32_t causal;
+} attn_paged_prefill_part;
+
+typedef struct attn_paged_decode_part {
+  const void* q;                 /* [num_seqs][num_q_heads][head_dim] */
+  const int32_t* block_table;    /* [num_seqs][max_blocks_per_seq] */
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;   /* [num_seqs] */
+  void* o;                       /* [num_seqs][num_q_heads][head_dim] */
+  int32_t num_seqs, max_context_len, partition_size;
+  const int32_t* plan;           /* optional, as for attn_decode_paged */
+  int32_t plan_items;
+  void* workspace;
+  size_t workspace_bytes;
+  /* optional fused write of each sequence's new token */
+  const void* k_new;
+  const void* v_new;
+  const int32_t* positions;
+  const int32_t* slot_mapping;
+  void* q_rot_out;
+  float rope_base;
+} attn_paged_decode_part;
+
+ATTN_API int attn_prefill_decode_paged(const attn_paged_prefill_part* prefill,
+                              const attn_paged_decode_part* decode, void* k_cache, void* v_cache,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, float scale, attn_dtype dtype,
+                              attn_stream_t stream);
+
+/* -------------------------------------------------------------------------
  * attn_kv_cache_write_rope -- fused rotary embedding + paged cache write.
  *
  * This kernel performs in one pass two of the fusions §Operator Fusion

@@ -555,3 +555,46 @@ def test_partition_for_lengths():
     arr = (ctypes.c_int32 * 2)(5, 6)
     for hq, hkv, d in ((12, 2, 96), (12, 5, 128), (1, 2, 128), (12, 0, 128)):
         assert lib.attn_decode_paged_partition_for(arr, 2, hq, hkv, d) == ATTN_E_INVALID
+
+
+def mixed_parts(**kw):
+    """Valid-looking parts for attn_prefill_decode_paged (fake device
+    pointers: only calls that fail validation or have nothing to launch are
+    made on the CPU)."""
+    pre = mi._PrefillPart(q=P, block_table=P, max_blocks_per_seq=8, cu_seqlens_q=P, context_lens=P, o=P,
+                          num_seqs=2, total_q=100, max_seqlen_q=50, max_context_len=128, causal=1)
+    dec = mi._DecodePart(q=P, block_table=P, max_blocks_per_seq=8, context_lens=P, o=P, num_seqs=4,
+                         max_context_len=128, partition_size=0, plan=None, plan_items=0, workspace=P,
+                         workspace_bytes=1 << 30)
+    for k, v in kw.items():
+        part, field = k.split("__")
+        setattr(pre if part == "pre" else dec, field, v)
+    return pre, dec
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pre__num_seqs=-1), ATTN_E_INVALID),
+    (dict(pre__max_seqlen_q=101), ATTN_E_INVALID),          # longer than total_q
+    (dict(dec__partition_size=40), ATTN_E_INVALID),
+    (dict(dec__q_rot_out=P), ATTN_E_INVALID),               # rotated queries without the token write
+    (dict(dec__k_new=P), ATTN_E_INVALID),                   # an incomplete token write
+    (dict(dec__max_blocks_per_seq=7), ATTN_E_INVALID),      # 128 tokens need 8 blocks
+    (dict(dec__plan=P, dec__plan_items=-1), ATTN_E_INVALID),
+])
+def test_prefill_decode_rejects(lib, kw, status):
+    pre, dec = mixed_parts(**kw)
+    st = lib.attn_prefill_decode_paged(ctypes.byref(pre), ctypes.byref(dec), P, P, 12, 2, 128, 16, 100, 0.0,
+                                       ATTN_BF16, None)
+    assert st == status
+    assert lib.attn_last_error().decode().startswith("attn_prefill_decode_paged")
+
+
+def test_prefill_decode_argument_rules(lib):
+    pre, dec = mixed_parts()
+    args = (P, P, 12, 2, 128, 16, 100, 0.0)
+    assert lib.attn_prefill_decode_paged(None, ctypes.byref(dec), *args, ATTN_BF16, None) == ATTN_E_INVALID
+    assert lib.attn_prefill_decode_paged(ctypes.byref(pre), ctypes.byref(dec), *args, ATTN_F32, None) == \
+        ATTN_E_UNSUPPORTED
+    # both parts empty: nothing to launch, success
+    pre, dec = mixed_parts(pre__num_seqs=0, pre__total_q=0, pre__max_seqlen_q=0, dec__num_seqs=0)
+    assert lib.attn_prefill_decode_paged(ctypes.byref(pre), ctypes.byref(dec), *args, ATTN_BF16, None) == 0

@@ -157,8 +157,9 @@ def mixed_reference(case):
     return pre, dec, q_rot
 
 
-def run_mixed(case, partition_size=0):
-    step = MixedStep(case, assign_blocks, DEV, partition_size=partition_size, scatter=scatter_to_pool)
+def run_mixed(case, partition_size=0, single_launch=False):
+    step = MixedStep(case, assign_blocks, DEV, partition_size=partition_size, scatter=scatter_to_pool,
+                     single_launch=single_launch)
     step.run()
     torch.cuda.synchronize()
     return step
@@ -178,18 +179,20 @@ def test_mixed_step_small():
     assert not used & set(case.foreign.tolist())
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_concurrent_step_equals_serial(fused):
+@pytest.mark.parametrize("schedule", ["two streams", "two streams, fused decode write", "single launch"])
+def test_concurrent_step_equals_serial(schedule):
     """The two-stream schedule (the decode tokens written and decoded on a
     second stream beside the chunk write and prefill, or with the decode
-    writing its own tokens) gives the serial order's outputs, rotated queries
-    and caches bit for bit."""
-    say(f"case: concurrent vs serial step, fused decode write {fused}")
+    writing its own tokens) and the single launch of prefill and decode
+    workgroups give the serial order's outputs, rotated queries and caches
+    bit for bit."""
+    say(f"case: {schedule} vs serial step")
     case = mixed_case(78, num_req=3, chunk=200, cached_max=900, num_dec=20, dec_lo=1, dec_hi=5000)
     steps = []
     for conc in (False, True):
         st = MixedStep(case, assign_blocks, DEV, scatter=scatter_to_pool, concurrent=conc,
-                       fuse_decode_write=fused)
+                       fuse_decode_write=schedule.endswith("fused decode write"),
+                       single_launch=conc and schedule == "single launch")
         st.run()
         torch.cuda.synchronize()
         steps.append(st)
@@ -201,18 +204,18 @@ def test_concurrent_step_equals_serial(fused):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16)), name
 
 
-@pytest.mark.parametrize("fused", [False, True])
-def test_graph_replay_equals_eager(fused):
+@pytest.mark.parametrize("fused,single", [(False, False), (True, False), (False, True)])
+def test_graph_replay_equals_eager(fused, single):
     """The step captured in a HIP graph and replayed three times, with eager
     work (restoring the unrotated queries) and synchronisations between the
     replays: every replay matches the oracle (outputs at the bf16 bar, rotated
     queries within the storage bound) and gives the eager step's outputs,
     rotated queries and caches bit for bit."""
-    say(f"case: graph-captured step, fused decode write {fused}")
+    say(f"case: graph-captured step, fused decode write {fused}, single launch {single}")
     case = mixed_case(79, num_req=3, chunk=150, cached_max=700, num_dec=17, dec_lo=1, dec_hi=6000)
     pre, dec, q_rot = mixed_reference(case)
     q_exact = oracle.rope(to_f64(case.q_new), case.positions, case.rope_base)
-    st = MixedStep(case, assign_blocks, DEV, scatter=scatter_to_pool, fuse_decode_write=fused)
+    st = MixedStep(case, assign_blocks, DEV, scatter=scatter_to_pool, fuse_decode_write=fused, single_launch=single)
     q0 = st.q.clone()
     st.run()
     torch.cuda.synchronize()
@@ -237,13 +240,15 @@ def test_graph_replay_equals_eager(fused):
         assert torch.equal(st.rotated_q().view(torch.int16), eager["rotated_q"].view(torch.int16)), rep
 
 
-def test_c5_mixed_step():
+@pytest.mark.parametrize("single", [True, False])
+def test_c5_mixed_step(single):
     """8 chunks of 512 new tokens on 0-2048 cached tokens + 128 decode
     sequences with context log-U[16, 32768], RoPE base 10000, fragmented pool
-    (seed 1004), in the benchmark's launch configuration."""
-    say("case: C5 mixed step")
+    (seed 1004), in the benchmark's launch configuration (the single launch)
+    and in the two-stream one."""
+    say(f"case: C5 mixed step, single launch {single}")
     case = mixed_case(1004)
-    step = run_mixed(case)
+    step = run_mixed(case, single_launch=single)
     say(f"  pool {case.num_blocks} blocks, decode tokens {int(case.dec_lengths.sum())}")
     pre, dec, _ = mixed_reference(case)
     check(f64(step.o_prefill), pre, torch.bfloat16, "C5 prefill")

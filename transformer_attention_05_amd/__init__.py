@@ -61,6 +61,22 @@ _c_i64p = ctypes.POINTER(ctypes.c_int64)
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 _vp = ctypes.c_void_p
 
+class _PrefillPart(ctypes.Structure):
+    """attn_paged_prefill_part (mi_attn.h)."""
+    _fields_ = [("q", _vp), ("block_table", _vp), ("max_blocks_per_seq", _c_i32), ("cu_seqlens_q", _vp),
+                ("context_lens", _vp), ("o", _vp), ("num_seqs", _c_i32), ("total_q", _c_i32),
+                ("max_seqlen_q", _c_i32), ("max_context_len", _c_i32), ("causal", _c_i32)]
+
+
+class _DecodePart(ctypes.Structure):
+    """attn_paged_decode_part (mi_attn.h)."""
+    _fields_ = [("q", _vp), ("block_table", _vp), ("max_blocks_per_seq", _c_i32), ("context_lens", _vp),
+                ("o", _vp), ("num_seqs", _c_i32), ("max_context_len", _c_i32), ("partition_size", _c_i32),
+                ("plan", _vp), ("plan_items", _c_i32), ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+                ("k_new", _vp), ("v_new", _vp), ("positions", _vp), ("slot_mapping", _vp), ("q_rot_out", _vp),
+                ("rope_base", ctypes.c_float)]
+
+
 _SIGNATURES = {
     "attn_last_error": (ctypes.c_char_p, []),
     "attn_prefill_workspace_size": (ctypes.c_size_t, [_c_i32] * 6 + [ctypes.c_int]),
@@ -94,6 +110,9 @@ _SIGNATURES = {
                                               _c_i32, ctypes.c_float, ctypes.c_int, _vp, _c_i32, _vp,
                                               ctypes.c_size_t, _vp]),
     "attn_decode_paged_plan": (ctypes.c_int64, [_c_i32p, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32p, ctypes.c_int64]),
+    "attn_prefill_decode_paged": (ctypes.c_int, [ctypes.POINTER(_PrefillPart), ctypes.POINTER(_DecodePart), _vp,
+                                                 _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_float,
+                                                 ctypes.c_int, _vp]),
     "attn_kv_cache_write_rope": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32,
                                                 _c_i32, _c_i32, ctypes.c_float, ctypes.c_int, _vp]),
     "attn_pool_create": (ctypes.c_int, [_c_i32, _c_i32, ctypes.POINTER(_vp)]),
@@ -580,6 +599,93 @@ def attn_decode_paged_rope(q, k_new, v_new, positions, slot_mapping, k_cache, v_
         ws_ptr, ws_bytes, _stream(q))
     _check(st)
     return o
+
+
+def attn_prefill_decode_paged(k_cache, v_cache, prefill=None, decode=None, scale=0.0):
+    """A chunked prefill and a decode over the same paged caches in one
+    launch (attn_prefill_decode_paged); bit-identical to attn_prefill_paged
+    and attn_decode_paged (or attn_decode_paged_rope) called one after the
+    other.
+
+    ``prefill``: dict with q, block_table, cu_seqlens_q, context_lens,
+    max_seqlen_q, and optional o, causal (True), max_context_len (0) -- the
+    arguments of attn_prefill_paged (no split-KV workspace, no mask).
+    ``decode``: dict with q, block_table, context_lens, max_context_len, and
+    optional o, partition_size, workspace, plan -- those of attn_decode_paged
+    -- plus, for the fused write of each sequence's new token, k_new, v_new,
+    positions, slot_mapping and optional q_rot_out, rope_base (10000).
+    Either may be None.  Returns (prefill output, decode output)."""
+    _tensor(k_cache, "k_cache")
+    pp, dp = _PrefillPart(), _DecodePart()
+    ref = None
+    o_pre = o_dec = None
+    if prefill is not None:
+        q = prefill["q"]
+        total_q, hq, d, nb, hkv, bs, s = _check_paged(q, prefill.get("o"), k_cache, v_cache, prefill["block_table"],
+                                                      prefill["context_lens"])
+        _int32(prefill["cu_seqlens_q"], "cu_seqlens_q", (s + 1,))
+        o_pre = prefill.get("o")
+        if o_pre is None:
+            o_pre = torch.empty_like(q)
+        pp.q, pp.block_table = _dev(q, "q"), _dev(prefill["block_table"], "block_table")
+        pp.max_blocks_per_seq = prefill["block_table"].shape[1]
+        pp.cu_seqlens_q, pp.context_lens = _dev(prefill["cu_seqlens_q"], "cu_seqlens_q"), _dev(
+            prefill["context_lens"], "context_lens")
+        pp.o, pp.num_seqs, pp.total_q = _dev(o_pre, "o"), s, total_q
+        pp.max_seqlen_q, pp.max_context_len = int(prefill["max_seqlen_q"]), int(prefill.get("max_context_len", 0))
+        pp.causal = 1 if prefill.get("causal", True) else 0
+        ref = q
+    if decode is not None:
+        q = decode["q"]
+        s, hq, d, nb, hkv, bs, s_bt = _check_paged(q, decode.get("o"), k_cache, v_cache, decode["block_table"],
+                                                   decode["context_lens"])
+        if s_bt != s:
+            raise ValueError(f"block_table has {s_bt} rows for {s} queries")
+        if ref is not None and (ref.dtype != q.dtype or ref.shape[1:] != q.shape[1:]):
+            raise ValueError("the prefill and decode queries must share dtype, heads and head_dim")
+        plan = decode.get("plan")
+        if plan is not None:
+            _int32(plan, "plan")
+            if plan.dim() != 2 or plan.shape[1] != 2:
+                raise ValueError("plan must be [n, 2] (sequence, partition)")
+        o_dec = decode.get("o")
+        if o_dec is None:
+            o_dec = torch.empty_like(q)
+        part, mx = int(decode.get("partition_size", 0)), int(decode["max_context_len"])
+        need = attn_decode_paged_workspace_size(s, hq, hkv, d, mx, part)
+        ws = decode.get("workspace")
+        if ws is None and need > 0:
+            ws = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        dp.q, dp.block_table = _dev(q, "q"), _dev(decode["block_table"], "block_table")
+        dp.max_blocks_per_seq = decode["block_table"].shape[1]
+        dp.context_lens, dp.o = _dev(decode["context_lens"], "context_lens"), _dev(o_dec, "o")
+        dp.num_seqs, dp.max_context_len, dp.partition_size = s, mx, part
+        dp.plan = _dev(plan, "plan") if plan is not None else None
+        dp.plan_items = int(plan.shape[0]) if plan is not None else 0
+        dp.workspace = _dev(ws, "workspace") if ws is not None else None
+        dp.workspace_bytes = _workspace_bytes(ws) if ws is not None else 0
+        if decode.get("k_new") is not None:
+            _like(decode["k_new"], "k_new", (s, hkv, d), q.dtype)
+            _like(decode["v_new"], "v_new", (s, hkv, d), q.dtype)
+            _int32(decode["positions"], "positions", (s,))
+            _int32(decode["slot_mapping"], "slot_mapping", (s,))
+            dp.k_new, dp.v_new = _dev(decode["k_new"], "k_new"), _dev(decode["v_new"], "v_new")
+            dp.positions = _dev(decode["positions"], "positions")
+            dp.slot_mapping = _dev(decode["slot_mapping"], "slot_mapping")
+            dp.rope_base = float(decode.get("rope_base", 10000.0))
+        qr = decode.get("q_rot_out")
+        if qr is not None:  # (without the token write the library refuses it)
+            _like(qr, "q_rot_out", (s, hq, d), q.dtype)
+            dp.q_rot_out = _dev(qr, "q_rot_out")
+        ref = q if ref is None else ref
+    if ref is None:
+        return None, None
+    nb, hkv, bs = _caches(k_cache, v_cache, ref.dtype, ref.shape[2])
+    st = load().attn_prefill_decode_paged(ctypes.byref(pp), ctypes.byref(dp), _dev(k_cache, "k_cache"),
+                                          _dev(v_cache, "v_cache"), ref.shape[1], hkv, ref.shape[2], bs, nb,
+                                          float(scale), _dtype_code(ref), _stream(ref))
+    _check(st)
+    return o_pre, o_dec
 
 
 def attn_residual_rms_norm(x, residual, weight, eps=1e-6, y=None, residual_out=None):

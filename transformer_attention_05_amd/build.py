@@ -25,7 +25,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmi_attn.so")
 LIB_DEBUG = os.path.join(PKG, "libmi_attn_debug.so")
 
-SOURCES = ["prefill.hip", "decode.hip", "rope_write.hip", "copy_blocks.hip", "rmsnorm.hip", "api.cpp", "pool.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "mixed.hip", "rope_write.hip", "copy_blocks.hip", "rmsnorm.hip", "api.cpp",
+           "pool.cpp"]
 ARCH = "gfx950"
 
 

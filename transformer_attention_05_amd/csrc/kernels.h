@@ -136,6 +136,23 @@ hipError_t launch_decode_f32(const DecodeArgs& a, int head_dim, hipStream_t s);
 // attn_decode_paged_noalloc.
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 hipError_t decode_scratch(hipStream_t s, void** out);
+// One launch running a paged prefill's workgroups (num_wg of them, no
+// split, the 4-wavefront tile hpw x (4 / hpw)) and a decode's (planned, or
+// the padded grid when da.plan is null): grid = [gp prefill, gd decode] x
+// groups, then the remaining decode workgroups.
+struct MixedSched {
+  int32_t n_pre;   // prefill workgroups
+  int32_t n_dec;   // decode workgroups
+  int32_t gp, gd;  // workgroups of each kind per interleaved group
+  int32_t groups;  // ceil(n_pre / gp)
+};
+inline uint32_t mixed_grid(const MixedSched& m) {
+  const int64_t head = (int64_t)m.groups * (m.gp + m.gd);
+  const int64_t rest = m.n_dec - (int64_t)m.groups * m.gd;
+  return (uint32_t)(head + (rest > 0 ? rest : 0));
+}
+hipError_t launch_mixed(const PrefillArgs& pa, const DecodeArgs& da, const MixedSched& m, int head_dim, int hpw,
+                        bool fused, hipStream_t s);
 hipError_t launch_rope_write(const RopeWriteArgs& a, int head_dim, bool bf16, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t s);
 hipError_t launch_residual_rms_norm(const RmsNormArgs& a, bool bf16, hipStream_t s);
@@ -151,5 +168,6 @@ hipError_t debug_take_prefill(uint32_t* acc, bool clear);
 hipError_t debug_take_decode(uint32_t* acc, bool clear);
 hipError_t debug_take_rope_write(uint32_t* acc, bool clear);
 hipError_t debug_take_copy_blocks(uint32_t* acc, bool clear);
+hipError_t debug_take_mixed(uint32_t* acc, bool clear);
 
 }  // namespace mi_attn

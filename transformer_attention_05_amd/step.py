@@ -17,6 +17,12 @@ small workgroups spread over every CU (enqueued the other way round, the
 prefill waits for the decode to drain and the step takes ~250 us instead of
 ~212 us on MI355X).
 
+With ``single_launch`` (the default of the benchmark) the step is two
+launches on the caller's stream: the chunk tokens' write, then one launch
+whose grid holds the chunked prefill's workgroups and the decode's (which
+writes its own tokens), interleaved (attn_prefill_decode_paged): no second
+stream, no cross-stream start or join, same results bit for bit.
+
 The host side (block pool, block tables, slot mapping) is built once in
 ``__init__``; ``run()`` only enqueues the launches, so the same buffers can be
 replayed step after step.
@@ -29,7 +35,7 @@ import torch
 
 from . import (Pool, attn_decode_paged, attn_decode_paged_partition_for, attn_decode_paged_plan,
                attn_decode_paged_rope, attn_decode_paged_workspace_size, attn_kv_cache_write_rope,
-               attn_prefill_paged, attn_prefill_paged_workspace_size)
+               attn_prefill_decode_paged, attn_prefill_paged, attn_prefill_paged_workspace_size)
 
 
 class MixedStep:
@@ -42,9 +48,10 @@ class MixedStep:
     """
 
     def __init__(self, case, assign, device="cuda", partition_size=0, scatter=None, concurrent=True,
-                 fuse_decode_write=False):
+                 fuse_decode_write=False, single_launch=False):
         self.case = case
         self.concurrent = concurrent
+        self.single_launch = single_launch
         self.fuse_decode_write = fuse_decode_write
         self.device = device
         self.pool = Pool(case.num_blocks)
@@ -130,6 +137,20 @@ class MixedStep:
                                rope_base=self.case.rope_base, partition_size=self.partition_size,
                                workspace=self.workspace, plan=self.plan)
 
+    def prefill_and_decode(self):
+        """The chunked prefill and the decode (which rotates and writes the
+        decode tokens itself) in one launch; the chunk tokens are written."""
+        R, n = self.R, self.n_prefill
+        pre = dict(q=self.q[:n], block_table=self.tables[:R], cu_seqlens_q=self.cu_seqlens_q,
+                   context_lens=self.context_lens[:R], max_seqlen_q=self.case.chunk, o=self.o_prefill, causal=True,
+                   max_context_len=self.max_pre_ctx) if R else None
+        dec = dict(q=self.q[n:], block_table=self.tables[R:], context_lens=self.context_lens[R:],
+                   max_context_len=self.max_dec_ctx, o=self.o_decode, partition_size=self.partition_size,
+                   workspace=self.workspace, plan=self.plan, k_new=self.k[n:], v_new=self.v[n:],
+                   positions=self.positions[n:], slot_mapping=self.slots[n:], q_rot_out=self.q_dec_rot,
+                   rope_base=self.case.rope_base) if self.S else None
+        attn_prefill_decode_paged(self.k_cache, self.v_cache, prefill=pre, decode=dec)
+
     def capture(self):
         """Record run() into a HIP graph (torch.cuda.CUDAGraph) for replay().
 
@@ -149,7 +170,7 @@ class MixedStep:
         self.graph.replay()
 
     def _fused(self):
-        return self.concurrent and self.fuse_decode_write and self.R and self.S
+        return (self.single_launch or (self.concurrent and self.fuse_decode_write)) and self.R and self.S
 
     def rotated_q(self):
         """Rotated queries of every new token after run()."""
@@ -161,11 +182,17 @@ class MixedStep:
         """Enqueue one step.  ``marks``: optional dict of torch.cuda.Event
         ("prefill0", "prefill1" on the caller's stream and "decode0",
         "decode1" on the second stream) recorded around the chunked prefill
-        and the decode of the concurrent schedule, to time them inside the
-        step."""
+        and the decode of the concurrent schedule, or ("mixed0", "mixed1")
+        around the single launch, to time them inside the step."""
         def mark(name, stream):
-            if marks is not None:
+            if marks is not None and name in marks:
                 marks[name].record(stream)
+        if self.single_launch and self.R and self.S:
+            self.write(0, self.n_prefill)    # the chunk tokens
+            mark("mixed0", torch.cuda.current_stream())
+            self.prefill_and_decode()
+            mark("mixed1", torch.cuda.current_stream())
+            return
         if self._fused():
             main = torch.cuda.current_stream()
             self.side.wait_stream(main)      # the step's inputs come from the caller's stream
