@@ -20,18 +20,20 @@ binding's host-side cost does not pace short kernels); it reports the
 median (`us`), the min and the mean per call.  A graph replay costs about
 22 us before its first kernel starts (measured on MI355X: a replay of one
 near-empty kernel takes 28 us, each further one adds 1.1 us), so a sample
-of 20 calls charges each call about 1.1 us of it.  The decode roofline uses
-the mean (the average launch duration), as the profiler summary does; the
-step is also timed eagerly in samples of 5 and inside the step the decode
-and the chunked prefill are timed by events on their own streams.
+of 20 calls charges each call about 1.1 us of it.  The roofline figure
+(the mixed launch) uses the mean (the average launch duration), as the
+profiler summary does; the step is also timed eagerly in samples of 20, and
+the mixed launch inside runs of 20 back-to-back steps, by events around it.
 
 value = percent of the step's roofline time reached:
     100 * max(F / 2.5 PFLOP/s, B / 8 TB/s) / measured step time
 with F the chunked-prefill flops (4 * D per unmasked query-key pair) and B the
 algorithmic HBM bytes of the write, the chunked prefill and the decode (the
 chunked prefill and the decode run at once, so the bound is the busier of
-the two resources).  The line also carries the roofline of
-the dominant kernel (the paged decode), the oracle timed on the host cores
+the two resources).  The step is two launches on one stream: the chunk
+tokens' RoPE write, then one launch that runs the chunked prefill's and the
+decode's workgroups together (the decode writing its own tokens).  The line
+also carries the roofline of that dominant launch, the oracle timed on the host cores
 and the per-stage figures, plus the contiguous long prefill (T 16384) and the
 uniform-context decode (64 sequences, U[128, 4096]) measured on their own.
 
@@ -54,8 +56,10 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill attention TFLOP/s + paged-decode KV GB/s on 1 MI355X (% of roofline)"
 PEAK_BF16_FLOPS = 2.5e15
 TRAFFIC_PROBE_BYTES = 256 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-DECODE_SRC = os.path.join(ROOT, "transformer_attention_05_amd", "csrc", "decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "mixed_traffic.json")
+# the sources the counted kernel is compiled from
+MIXED_SRCS = [os.path.join(ROOT, "transformer_attention_05_amd", "csrc", f)
+              for f in ("mixed.hip", "prefill_body.h", "decode_body.h", "device_common.h", "kernels.h")]
 PEAK_HBM = 8.0e12
 HQ, HKV, D, BS = 12, 2, 128, 16
 ELT = 2  # bf16 bytes
@@ -104,7 +108,7 @@ def write_bytes(n_tokens):
 # ----------------------------------------------------------------------------- timing helpers
 
 WARM_CALLS, TIMED_CALLS, PER_SAMPLE = 20, 100, 20
-IN_STEP_SAMPLES = 20  # steps timed with events on each stream (one sample each)
+IN_STEP_SAMPLES = 5  # runs of PER_SAMPLE back-to-back steps with events around the mixed launch
 
 
 def timed(torch, fn, warm=None, calls=None, per=PER_SAMPLE, graph=True):
@@ -158,6 +162,9 @@ def fig(t, work=None, unit=None, peak=None, key="frac_of_peak"):
     how = "graph replays of" if t.get("graph") else "eager,"
     d = {"us": round(t["median"] * 1e3, 2), "us_min": round(t["min"] * 1e3, 2), "us_mean": round(t["mean"] * 1e3, 2),
          "iters": f"{t['warm']} warm-up + {t['calls']} timed calls ({how} {t['per_sample']} calls per event pair)"}
+    if t.get("back_to_back"):
+        d["iters"] = (f"{t['warm']} warm-up + {t['calls']} timed launches (eager, events around the launch in each "
+                      f"step of runs of {t['back_to_back']} back-to-back steps)")
     if work is not None:
         rate = work / (t["median"] / 1e3)
         d[unit] = round(rate / (1e12 if unit == "TFLOP/s" else 1e9), 1)
@@ -212,7 +219,7 @@ def main():
     if args.only in (None, "mixed"):
         log("bench: building the mixed step (seed 1004)")
         case = mixed_case(1004)
-        step = MixedStep(case, assign_blocks, dev, scatter=scatter_to_pool)
+        step = MixedStep(case, assign_blocks, dev, scatter=scatter_to_pool, single_launch=True)
         n_new = case.q_new.shape[0]
         F = chunk_flops(case)
         B_dec = decode_bytes(case.dec_lengths)
@@ -230,24 +237,26 @@ def main():
         wall = (time.perf_counter() - t0) / args.steps
         # the step again, event-timed (median and min over samples)
         t_step = timed(torch, lambda i: step.run(), graph=False)
-        # the prefill and the decode inside the step: events on each stream
-        # around each of them (each event adds a few microseconds of idle
-        # time to its stream, so these are slight overestimates)
-        names = ("prefill0", "prefill1", "decode0", "decode1")
-        in_pre, in_dec = [], []
-        for _ in range(WARM_CALLS + IN_STEP_SAMPLES):
-            marks = {n: torch.cuda.Event(enable_timing=True) for n in names}
-            step.run(marks)
+        # the mixed launch inside the step: events around it in each of
+        # PER_SAMPLE back-to-back steps (the queue stays ahead of the GPU, so
+        # no host latency falls between a step's events)
+        in_mix = []
+        for k in range(WARM_CALLS + IN_STEP_SAMPLES):
+            marks = [{n: torch.cuda.Event(enable_timing=True) for n in ("mixed0", "mixed1")} for _ in range(PER_SAMPLE)]
+            for mk in marks:
+                step.run(mk)
             torch.cuda.synchronize()
-            in_pre.append(marks["prefill0"].elapsed_time(marks["prefill1"]))
-            in_dec.append(marks["decode0"].elapsed_time(marks["decode1"]))
-        in_pre, in_dec = in_pre[WARM_CALLS:], in_dec[WARM_CALLS:]
-        in_step = dict(prefill=dict(mean=float(np.mean(in_pre)), median=float(np.median(in_pre)),
-                                    min=float(np.min(in_pre)), warm=WARM_CALLS, calls=len(in_pre), per_sample=1),
-                       decode=dict(mean=float(np.mean(in_dec)), median=float(np.median(in_dec)),
-                                   min=float(np.min(in_dec)), warm=WARM_CALLS, calls=len(in_dec), per_sample=1))
-        # per-stage durations: each stage repeated on its own, back to back,
-        # between HIP events on the stream the kernels are launched on
+            if k >= WARM_CALLS:
+                in_mix += [mk["mixed0"].elapsed_time(mk["mixed1"]) for mk in marks]
+        in_step = dict(mean=float(np.mean(in_mix)), median=float(np.median(in_mix)), min=float(np.min(in_mix)),
+                       warm=WARM_CALLS * PER_SAMPLE, calls=len(in_mix), per_sample=1, back_to_back=PER_SAMPLE)
+        # the step's two launches on their own, back to back, between HIP
+        # events on their stream: the chunk tokens' write and the mixed launch
+        # (chunked prefill + decode with its tokens' write)
+        t_wchunk = timed(torch, lambda i: step.write(0, step.n_prefill))
+        t_mix = timed(torch, lambda i: step.prefill_and_decode())
+        # the stages as separate kernels, for reference: every token's write,
+        # the chunked prefill (default tile) and the decode
         stages = [timed(torch, lambda i, f=fn: f()) for fn in (step.write, step.prefill, step.decode)]
         ms_wr, ms_pre, ms_dec = (t["mean"] for t in stages)
         # the same step captured in a HIP graph, replays back to back
@@ -262,17 +271,33 @@ def main():
                 step.replay()
             torch.cuda.synchronize()
             graph_s = (time.perf_counter() - t0) / args.steps
-        # prefill and decode overlap (two streams), so the step's bound is the
-        # larger of its total HBM bytes and its total matrix-core flops
+        # the former schedule: the prefill and the decode as two launches on
+        # two streams (each stream writing its own tokens first)
+        two_s = None
+        if not args.no_components:
+            two = MixedStep(case, assign_blocks, dev, scatter=scatter_to_pool)
+            for _ in range(args.warmup):
+                two.run()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(args.steps):
+                two.run()
+            torch.cuda.synchronize()
+            two_s = (time.perf_counter() - t0) / args.steps
+            del two
+        # prefill and decode overlap, so the step's bound is the larger of its
+        # total HBM bytes and its total matrix-core flops
         B_pre = prefill_io_bytes(case)
         t_roof = max(F / PEAK_BF16_FLOPS, (B_dec + B_wr + B_pre) / PEAK_HBM)
+        S = len(case.dec_lengths)
+        B_mix = B_dec + B_pre + write_bytes(S)  # the mixed launch: decode, chunked prefill, decode tokens' write
         out["mixed"] = dict(wall_s=wall, ms_write=ms_wr, ms_prefill=ms_pre, ms_decode=ms_dec, stages=stages,
-                            t_step=t_step, in_step=in_step, F=F, B_dec=B_dec,
-                            B_wr=B_wr, B_pre=B_pre, t_roof=t_roof, n_new=n_new, part=step.partition_size,
-                            dec_tokens=int(case.dec_lengths.sum()), pool_blocks=case.num_blocks,
-                            graph_s=graph_s)
-        log(f"bench: mixed step wall {wall * 1e3:.3f} ms | write {ms_wr:.3f} prefill {ms_pre:.3f} "
-            f"decode {ms_dec:.3f} ms")
+                            t_step=t_step, in_step=in_step, t_wchunk=t_wchunk, t_mix=t_mix, F=F, B_dec=B_dec,
+                            B_wr=B_wr, B_pre=B_pre, B_mix=B_mix, B_wchunk=write_bytes(step.n_prefill), t_roof=t_roof,
+                            n_new=n_new, part=step.partition_size, dec_tokens=int(case.dec_lengths.sum()),
+                            pool_blocks=case.num_blocks, graph_s=graph_s, two_s=two_s)
+        log(f"bench: mixed step wall {wall * 1e3:.3f} ms | chunk write {t_wchunk['mean']:.3f} mixed launch "
+            f"{t_mix['mean']:.3f} ms | two streams {two_s * 1e3 if two_s else float('nan'):.3f} ms")
         del step
 
     # ------------------------------------------------------------------ contiguous long prefill
@@ -429,18 +454,26 @@ def cpu_baseline(case, m):
                        "fp64 NumPy, once")
 
 
-def measured_traffic():
-    """HBM bytes per decode launch from the committed counter profile, or
-    None if the decode source changed since the counters were taken."""
+def mixed_src_sha256():
+    """sha256 over the sources of the mixed launch's kernel, in order."""
     import hashlib
+    h = hashlib.sha256()
+    for path in MIXED_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per mixed launch from the committed counter profile, or
+    None if its sources changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        with open(DECODE_SRC, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = mixed_src_sha256()
     except (OSError, ValueError):
         return None
-    if t.get("decode_src_sha256") != sha:
+    if t.get("src_sha256") != sha:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -460,33 +493,38 @@ def emit(args, out, cpu):
                                      "Hq 12 / Hkv 2, D 128, bf16, block 16, fragmented pool, seed 1004",
                          "new_tokens": m["n_new"], "decode_context_tokens": m["dec_tokens"],
                          "pool_blocks": m["pool_blocks"], "decode_partition": m["part"],
-                         "schedule": "chunk tokens' RoPE write then chunked prefill (ATTN_PREFILL_SHARE_CU: one "
-                                     "4-wavefront workgroup per CU) on one stream, beside the decode tokens' RoPE write "
-                                     "then the decode on a second; stage figures run alone, default tiles",
+                         "schedule": "one stream: the chunk tokens' RoPE write, then one launch running the chunked "
+                                     "prefill's and the decode's workgroups together (attn_prefill_decode_paged; the "
+                                     "decode writes its own tokens); stage figures run alone, default tiles",
                          "parallelism": "single GPU"}
-        dec_s = m["ms_decode"] / 1e3
-        gbps = m["B_dec"] / dec_s / 1e9
-        ins = m["in_step"]["decode"]
-        res["roofline"] = {"kernel": "paged decode (decode_planned_kernel: partitions and their merge, one launch)",
+        mix_s = m["t_mix"]["mean"] / 1e3
+        gbps = m["B_mix"] / mix_s / 1e9
+        ins = m["in_step"]
+        res["roofline"] = {"kernel": "mixed_kernel: the chunked prefill's and the paged decode's workgroups (decode "
+                                     "tokens' write, partitions and merge included) in one launch",
                            "bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                            "frac": round(gbps * 1e9 / PEAK_HBM, 4), "traffic": measured_traffic(),
-                           "algorithmic_bytes_per_launch": m["B_dec"], "avg_launch_us": round(m["ms_decode"] * 1e3, 2),
-                           "launches_timed": m["stages"][2]["calls"],
+                           "algorithmic_bytes_per_launch": m["B_mix"],
+                           "flops_per_launch": m["F"],
+                           "frac_of_bf16_peak": round(m["F"] / mix_s / PEAK_BF16_FLOPS, 4),
+                           "avg_launch_us": round(m["t_mix"]["mean"] * 1e3, 2),
+                           "launches_timed": m["t_mix"]["calls"],
                            "in_step": {"avg_launch_us": round(ins["mean"] * 1e3, 2),
                                        "median_launch_us": round(ins["median"] * 1e3, 2),
-                                       "frac": round(m["B_dec"] / (ins["mean"] / 1e3) / PEAK_HBM, 4),
-                                       "note": "the same decode inside the timed step, beside the chunked prefill "
-                                               "(events on its stream)"}}
+                                       "frac": round(m["B_mix"] / (ins["mean"] / 1e3) / PEAK_HBM, 4),
+                                       "note": "the same launch inside back-to-back steps (events around it)"}}
         st_w, st_p, st_d = m["stages"]
         comps["step"] = fig(m["t_step"])
         comps["step"]["frac_of_step_roofline"] = round(m["t_roof"] / (m["t_step"]["median"] / 1e3), 4)
-        comps["step_write"] = fig(st_w, m["B_wr"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
-        comps["step_chunked_prefill"] = fig(st_p, m["F"], "TFLOP/s", PEAK_BF16_FLOPS, "frac_of_bf16_peak")
-        comps["step_decode"] = fig(st_d, m["B_dec"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
-        comps["step_chunked_prefill_in_step"] = fig(m["in_step"]["prefill"], m["F"], "TFLOP/s", PEAK_BF16_FLOPS,
-                                                    "frac_of_bf16_peak")
-        comps["step_decode_in_step"] = fig(m["in_step"]["decode"], m["B_dec"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
+        comps["step_chunk_write"] = fig(m["t_wchunk"], m["B_wchunk"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
+        comps["step_mixed_launch"] = fig(m["t_mix"], m["B_mix"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
+        comps["step_mixed_launch_in_step"] = fig(m["in_step"], m["B_mix"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
+        comps["write_all_4224_tokens"] = fig(st_w, m["B_wr"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
+        comps["chunked_prefill_alone"] = fig(st_p, m["F"], "TFLOP/s", PEAK_BF16_FLOPS, "frac_of_bf16_peak")
+        comps["decode_alone"] = fig(st_d, m["B_dec"], "GB/s", PEAK_HBM, "frac_of_hbm_peak")
         comps["step_roofline_us"] = round(m["t_roof"] * 1e6, 2)
+        if m.get("two_s"):
+            comps["step_two_streams_us"] = round(m["two_s"] * 1e6, 2)
         if m.get("graph_s"):
             comps["step_graph_replay_us"] = round(m["graph_s"] * 1e6, 2)
     if "prefill_c4" in out:
