@@ -749,12 +749,15 @@ extern "C" int attn_decode_paged_rope(void* q_rot_out, const void* q, const void
 // ---------------------------------------------------------------------------
 // Mixed launch: the interleave of prefill and decode workgroups in its grid.
 // Measured on MI355X with 8 chunks of 512 new tokens (384 prefill
-// workgroups) beside a 128-sequence decode (1390 workgroups): groups of 32
-// prefill and 64 decode workgroups 172-177 us per step (RoPE write
-// included), 32 + 32 175-178, 16 + 16 184, all prefill first 177-180,
-// against 189-194 us for the two-launch, two-stream step.
+// workgroups) beside a 128-sequence decode (1390 workgroups), RoPE write
+// included, us per step: groups of 32 prefill and 64 decode workgroups
+// 172-177 against 189-194 for the two-launch, two-stream step; 32 + 32
+// 175-178, 16 + 16 184, all prefill first 177-180.  With the prefill's waves
+// at raised priority (mixed.hip), same box, configurations interleaved:
+// 32 + 72 169.0, 32 + 56 169.4, 32 + 64 171.6, 32 + 80 171.2, 24 + 48 171.2,
+// 24 + 56 174.2; spreading the prefill thinner (16 + 64, 32 + 128) 199.
 constexpr int32_t kMixedPrefillPerGroup = 32;
-constexpr int32_t kMixedDecodePerGroup = 64;
+constexpr int32_t kMixedDecodePerGroup = 72;
 
 extern "C" int attn_prefill_decode_paged(const attn_paged_prefill_part* prefill, const attn_paged_decode_part* decode,
                                          void* k_cache, void* v_cache, int32_t num_q_heads,
