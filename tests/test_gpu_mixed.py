@@ -12,7 +12,7 @@ import oracle
 import transformer_attention_05_amd as mi
 from tests.gpu_util import DEV, check, f64, say
 from transformer_attention_05_amd.step import MixedStep
-from workloads import assign_blocks, mixed_case, scatter_to_pool, to_f64
+from workloads import BLOCK_SIZE, assign_blocks, mixed_case, normal, rng, scatter_to_pool, to_f64
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -127,3 +127,65 @@ def test_rejects_before_launch():
     with pytest.raises(mi.AttnError):
         mi.attn_prefill_decode_paged(st.k_cache, st.v_cache, decode=dict(dec, q_rot_out=st.q_dec_rot[:3]))
     assert "attn_prefill_decode_paged" in mi.attn_last_error()
+
+
+def ragged_pool(seed, pre_cached, pre_new, dec_ctx, hq=12, hkv=2, d=128, dtype=torch.bfloat16):
+    """One NaN-filled pool holding the chunked sequences (cached + new
+    tokens) and the decode sequences, blocks scattered at random."""
+    g = rng(seed)
+    totals = [int(c) + int(n) for c, n in zip(pre_cached, pre_new)] + [int(c) for c in dec_ctx]
+    nblk = [(t + BLOCK_SIZE - 1) // BLOCK_SIZE for t in totals]
+    nb = sum(nblk) + 8
+    perm = g.permutation(nb)
+    bt = np.zeros((len(totals), max(nblk)), dtype=np.int32)
+    p = 0
+    for s, n in enumerate(nblk):
+        bt[s, :n] = perm[p:p + n]
+        p += n
+    ks = [normal(g, (t, hkv, d), dtype) for t in totals]
+    vs = [normal(g, (t, hkv, d), dtype) for t in totals]
+    kc = torch.full((nb, hkv, BLOCK_SIZE, d), float("nan"), dtype=dtype, device=DEV)
+    vc = torch.full((nb, hkv, d, BLOCK_SIZE), float("nan"), dtype=dtype, device=DEV)
+    for s in range(len(totals)):
+        scatter_to_pool(kc, vc, bt[s], ks[s], vs[s])
+    q_pre = [normal(g, (int(n), hq, d), dtype) for n in pre_new]
+    q_dec = normal(g, (len(dec_ctx), hq, d), dtype)
+    return q_pre, q_dec, ks, vs, bt, kc, vc, np.array(totals, dtype=np.int32)
+
+
+@pytest.mark.parametrize("part,plan", [(0, True), (64, True), (64, False)])
+def test_ragged_chunks_and_short_contexts(part, plan):
+    """Ragged chunks (1 to 512 new tokens on 0 to 2048 cached, unaligned to
+    blocks and tiles) beside decodes of 1, 16, 17, 1024, 1025 and 3000
+    tokens, over one NaN-filled pool: bit-identical to the separate calls,
+    and the oracle."""
+    say(f"case: ragged mixed launch, partition {part}, plan {plan}")
+    cached, new = [0, 17, 2048, 5], [1, 129, 512, 64]
+    dec_ctx = [1, 16, 17, 1024, 1025, 3000]
+    q_pre, q_dec, ks, vs, bt, kc, vc, totals = ragged_pool(85 + part, cached, new, dec_ctx)
+    R, S = len(cached), len(dec_ctx)
+    q = torch.cat(q_pre).to(DEV)
+    qd = q_dec.to(DEV)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(new)]).astype(np.int32)).to(DEV)
+    tables = torch.from_numpy(bt).to(DEV)
+    lens = torch.from_numpy(totals).to(DEV)
+    mx = int(max(dec_ctx))
+    part_eff = part if part else mi.attn_decode_paged_partition_for(np.array(dec_ctx, np.int32), 12, 2, 128)
+    ws = torch.zeros(max(256, mi.attn_decode_paged_workspace_size(S, 12, 2, 128, mx, part_eff)), dtype=torch.uint8,
+                     device=DEV)
+    pl = torch.from_numpy(mi.attn_decode_paged_plan(np.array(dec_ctx, np.int32), 2, mx, part_eff)).to(DEV) if plan else None
+    pre = dict(q=q, block_table=tables[:R], cu_seqlens_q=cu, context_lens=lens[:R], max_seqlen_q=max(new), causal=True)
+    dec = dict(q=qd, block_table=tables[R:], context_lens=lens[R:], max_context_len=mx, partition_size=part_eff,
+               workspace=ws, plan=pl)
+    o_pre, o_dec = mi.attn_prefill_decode_paged(kc, vc, prefill=pre, decode=dec)
+    ref_pre = mi.attn_prefill_paged(q, kc, vc, tables[:R], cu, lens[:R], max(new), causal=True, workspace=False)
+    ref_dec = mi.attn_decode_paged(qd, kc, vc, tables[R:], lens[R:], mx, partition_size=part_eff, workspace=ws,
+                                   plan=pl)
+    torch.cuda.synchronize()
+    same(o_pre, ref_pre, "prefill")
+    same(o_dec, ref_dec, "decode")
+    exp_pre = oracle.chunked_prefill([to_f64(x) for x in q_pre], [to_f64(k) for k in ks[:R]],
+                                     [to_f64(v) for v in vs[:R]])
+    check(f64(o_pre), np.concatenate(exp_pre), torch.bfloat16, "prefill vs oracle")
+    exp_dec, _ = oracle.decode(to_f64(q_dec), [to_f64(k) for k in ks[R:]], [to_f64(v) for v in vs[R:]])
+    check(f64(o_dec), exp_dec, torch.bfloat16, "decode vs oracle")
