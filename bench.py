@@ -43,6 +43,7 @@ uniform-context decode (64 sequences, U[128, 4096]) measured on their own.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -207,6 +208,11 @@ def main():
     mi.load()
     dev = "cuda"
     out = {}
+    # no cyclic garbage collection while timing (reference counting still
+    # frees everything): a collection pass inside a timed window stalled the
+    # host for tens of milliseconds; the cpu_baseline leg runs with it on
+    gc.collect()
+    gc.disable()
     if args.traffic_probe:
         src = torch.empty(TRAFFIC_PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -406,6 +412,7 @@ def main():
 
     # ------------------------------------------------------------------ CPU baseline (oracle)
     cpu = None
+    gc.enable()
     if not args.no_cpu_baseline and "mixed" in out:
         cpu = cpu_baseline(case, out["mixed"])
 
