@@ -262,13 +262,20 @@ ATTN_API int attn_prefill_paged_masked(const void* q, const void* k_cache, const
  *                unset.
  *   workspace    device scratch (256-byte aligned) of at least
  *                attn_decode_paged_workspace_size(...) bytes (same arguments),
- *                needed when that size is non-zero.  It begins with arrival
- *                counters that must be ZERO before the first call that uses
- *                the workspace (fill it with zeros once after allocating);
- *                every completed call leaves them zero again, so the same
- *                workspace serves later calls of any shape that fits.  Calls
- *                that overlap on one workspace race; a plan that lists a
- *                partition twice corrupts the counters.
+ *                needed when that size is non-zero.  It begins with a block
+ *                of arrival counters, one int32 for each (sequence, kv head
+ *                slice) pair that a call with these numbers of query and kv
+ *                heads may have (65535 sequences x kv heads x
+ *                ceil(query heads per kv head / 16); 512 KiB at 2 kv heads),
+ *                that must be ZERO before the first call that uses the
+ *                workspace (fill it with zeros once after allocating); every
+ *                completed call leaves them zero again, so the same
+ *                workspace serves later calls with the same numbers of
+ *                query and kv heads and any sequence count, contexts and
+ *                partition size that fit.  (A call with other head numbers
+ *                has a counter block of another size: zero the workspace
+ *                again first.)  Calls that overlap on one workspace race; a
+ *                plan that lists a partition twice corrupts the counters.
  * ---------------------------------------------------------------------- */
 ATTN_API size_t attn_decode_paged_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t max_context_len,
@@ -286,16 +293,19 @@ ATTN_API int attn_decode_paged(const void* q, const void* k_cache, const void* v
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid allocation): the same arguments without a
  * workspace, the same kernels and results bit for bit.  The split-KV
- * scratch (arrival counters, partial outputs and (m, l) pairs, in
- * attn_decode_paged's workspace layout) is a fixed 32 MiB device array of
+ * scratch (arrival counters, partial outputs and (m, l) pairs, laid out
+ * like attn_decode_paged's workspace but with a 4 MiB counter block, room
+ * for 65535 sequences x 16 kv head slices whatever the call's head
+ * numbers) is a fixed 32 MiB device array of
  * the library's own, which every GPU the library runs on holds until the
  * process ends; the first call on a device finds its address there and
  * zero-fills it with a kernel on `stream`.  Nothing is allocated or freed.
- *   - A call whose attn_decode_paged_workspace_size(...) exceeds 32 MiB
- *     returns ATTN_E_NOMEM (launching nothing): about 160 sequences of
- *     12 query heads at 32768 tokens with 1024-token partitions fit.
+ *   - A call whose partials and (m, l) pairs exceed the 28 MiB after the
+ *     counter block, or whose kv head slices exceed 16, returns
+ *     ATTN_E_NOMEM (launching nothing): about 140 sequences of 12 query
+ *     heads at 32768 tokens with 1024-token partitions fit.
  *   - Every call on one GPU shares that GPU's array, and a completed call
- *     leaves its counters zero for the next; calls that overlap on one GPU
+ *     leaves its counters zero for the next, of any shape; calls that overlap on one GPU
  *     (other streams, other threads) race and corrupt each other's results.
  *     Serialise them on one stream.
  * ---------------------------------------------------------------------- */

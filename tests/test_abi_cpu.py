@@ -326,15 +326,20 @@ def test_residual_rms_norm_rejects(lib, kw, status):
 
 def test_decode_workspace_size(lib):
     # one partition: no workspace; several: an arrival counter per (seq, kv
-    # head slice), then (D + 2) floats per (seq, head, partition)
+    # head slice) for the most sequences a call may have (65535), whatever
+    # this call's count, then (D + 2) floats per (seq, head, partition)
     assert lib.attn_decode_paged_workspace_size(4, 12, 2, 128, 128, 128) == 0
     n = lib.attn_decode_paged_workspace_size(4, 12, 2, 128, 1024, 128)
     rows = 4 * 12 * 8
-    assert n == 256 + ((rows * 128 * 4 + 255) // 256) * 256 + rows * 8
+    cnt = ((65535 * 2 * 4 + 255) // 256) * 256
+    assert n == cnt + ((rows * 128 * 4 + 255) // 256) * 256 + rows * 8
+    # the counter block is the same for 4 and for 1000 sequences of the same heads
+    n2 = lib.attn_decode_paged_workspace_size(1000, 12, 2, 128, 1024, 128)
+    assert n2 == cnt + ((1000 * 12 * 8 * 128 * 4 + 255) // 256) * 256 + 1000 * 12 * 8 * 8
     # 40 query heads on 2 kv heads (groups of 20): two slices (16 + 4 heads) per kv head
     n = lib.attn_decode_paged_workspace_size(100, 40, 2, 64, 1024, 128)
     rows = 100 * 40 * 8
-    assert n == ((100 * 2 * 2 * 4 + 255) // 256) * 256 + ((rows * 64 * 4 + 255) // 256) * 256 + rows * 8
+    assert n == ((65535 * 2 * 2 * 4 + 255) // 256) * 256 + ((rows * 64 * 4 + 255) // 256) * 256 + rows * 8
     p = lib.attn_decode_paged_auto_partition(64, 2, 4096)
     assert p % 128 == 0 and 128 <= p <= 1024
 

@@ -84,6 +84,32 @@ def test_workspace_counters_reset_and_reuse():
     assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
 
 
+def test_workspace_reuse_with_more_sequences():
+    """A call with few sequences and many partitions, then one with more
+    sequences on the same workspace.  The counter block is sized for the
+    most sequences a call may have, so the second call's counters lie where
+    only counters ever were (not where the first call left partials): every
+    call finds them zero, leaves them zero, and equals the oracle."""
+    say("case: decode workspace reuse, 7 then 100 sequences")
+    few = decode_case(43, 7, 1000, 3000)
+    many = decode_case(44, 100, 1, 3000)
+    part = 128
+    need = max(mi.attn_decode_paged_workspace_size(len(c.lengths), 12, 2, 128, int(c.lengths.max()), part)
+               for c in (few, many))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    for case in (few, many, few):
+        kc, vc = build_decode_pool(case, DEV)
+        q = case.q.to(DEV)
+        bt = torch.from_numpy(case.block_tables).to(DEV)
+        cl = torch.from_numpy(case.lengths.astype(np.int32)).to(DEV)
+        mx = int(case.lengths.max())
+        o = mi.attn_decode_paged(q, kc, vc, bt, cl, mx, partition_size=part, workspace=ws)
+        torch.cuda.synchronize()
+        check(f64(o.cpu()), oracle_decode(case), torch.bfloat16, f"reuse {len(case.lengths)} seqs")
+        cnt = (65535 * 2 * 4 + 255) // 256 * 256
+        assert int((ws[:cnt] != 0).sum().item()) == 0, "counter block not left zero"
+
+
 @pytest.mark.parametrize("part", [0, 128])
 def test_planned_grid_equals_padded(part):
     """The planned launch (only the real partitions, longest sequences first)

@@ -1,7 +1,10 @@
 """attn_decode_paged_noalloc, the decode for callers that cannot allocate:
 through the C ABI against attn_decode_paged (same kernels, so bit for bit)
-and the oracle, on two calls in a row (the second smaller), then a call too
-large for the fixed scratch, refused without a launch."""
+and the oracle, on two calls in a row (the second smaller), on calls that
+grow in sequence count and change head numbers (the shared scratch's
+counter block is fixed, so no call finds an earlier call's partials where
+its counters are), then a call too large for the fixed scratch, refused
+without a launch."""
 
 import numpy as np
 import pytest
@@ -17,6 +20,7 @@ pytestmark = [pytest.mark.gpu,
 
 
 def run_both(case, partition_size):
+    """The no-allocation decode and attn_decode_paged (a fresh workspace)."""
     kc, vc = build_decode_pool(case, DEV)
     q = case.q.to(DEV)
     bt = torch.from_numpy(case.block_tables).to(DEV)
@@ -45,6 +49,17 @@ def test_noalloc_decode_two_calls(first, second):
         o_na, o_ws = run_both(case, part)
         assert torch.equal(o_na.view(torch.int16), o_ws.view(torch.int16)), f"call {i + 1}: differs from attn_decode_paged"
         check(f64(o_na), reference(case), torch.bfloat16, f"call {i + 1} vs oracle")
+
+
+def test_noalloc_decode_growing_calls():
+    calls = [(9, 1000, 3000, 128, 12, 2, 128), (100, 1, 3000, 128, 12, 2, 128), (30, 500, 2000, 64, 40, 2, 64),
+             (120, 1, 3000, 128, 12, 2, 128)]
+    for i, (n, lo, hi, part, hq, hkv, d) in enumerate(calls):
+        say(f"case: no-allocation decode, growing call {i + 1}: {n} seqs ctx U[{lo}, {hi}], {hq}/{hkv} heads, D {d}")
+        case = decode_case(3200 + i, n, lo, hi, hq=hq, hkv=hkv, d=d)
+        o_na, o_ws = run_both(case, part)
+        assert torch.equal(o_na.view(torch.int16), o_ws.view(torch.int16)), f"call {i + 1}: differs from attn_decode_paged"
+        check(f64(o_na), reference(case), torch.bfloat16, f"growing call {i + 1} vs oracle")
 
 
 def test_noalloc_decode_refuses_above_the_fixed_scratch():

@@ -506,7 +506,15 @@ namespace {
 constexpr int32_t kMaxF32Partition = 65536;
 // Decode workspace, used only when a context can span several partitions:
 // the arrival counters (one int32 per sequence and kv head slice, zero
-// between calls), then the partial outputs, then the (m, l) pairs.
+// between calls), then the partial outputs, then the (m, l) pairs.  The
+// counter block has room for the most sequences a call may have (65535)
+// with the call's head geometry, so where it ends does not depend on the
+// sequence count: a later call with more sequences finds its counters where
+// only counters ever were, not where an earlier, smaller call left partials.
+// The fixed scratch of attn_decode_paged_noalloc, shared by calls of every
+// geometry, begins with a block of its own for up to 16 slices.
+constexpr int64_t kMaxDecodeSeqs = 65535;
+constexpr size_t kScratchCounterBytes = size_t(kMaxDecodeSeqs) * 16 * sizeof(int32_t) / 256 * 256 + 256;
 struct DecodeGeom {
   int32_t part, max_parts;
   size_t cnt_bytes, o_bytes, ml_bytes;
@@ -519,7 +527,7 @@ DecodeGeom decode_geom(int32_t num_seqs, int32_t hq, int32_t hkv, int32_t d, int
   gm.max_parts = ceil_div(max_ctx, gm.part);
   if (gm.max_parts > 1) {
     const size_t slices = (size_t)hkv * ceil_div(hq / hkv, 16);
-    gm.cnt_bytes = ((size_t)num_seqs * slices * sizeof(int32_t) + 255) / 256 * 256;
+    gm.cnt_bytes = ((size_t)kMaxDecodeSeqs * slices * sizeof(int32_t) + 255) / 256 * 256;
     const size_t rows = (size_t)num_seqs * hq * gm.max_parts;
     gm.o_bytes = (rows * d * sizeof(float) + 255) / 256 * 256;
     gm.ml_bytes = rows * 2 * sizeof(float);
@@ -648,6 +656,12 @@ int decode_common(const char* fn, const DecodeWrite* w, const void* q, const voi
   DecodeGeom gm = decode_geom(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, partition_size);
   if (plan != nullptr && (int64_t)plan_items > (int64_t)num_seqs * gm.max_parts)
     return fail(ATTN_E_INVALID, "%s: plan_items %d exceeds num_seqs x partitions", fn, plan_items);
+  if (use_scratch && gm.max_parts > 1) {
+    if ((size_t)num_kv_heads * ceil_div(num_q_heads / num_kv_heads, 16) > 16)
+      return fail(ATTN_E_NOMEM, "%s: the fixed scratch holds arrival counters for at most 16 kv head slices "
+                  "(kv heads x ceil(query heads per kv head / 16))", fn);
+    gm.cnt_bytes = kScratchCounterBytes;
+  }
   const size_t need = gm.total();
   if (use_scratch) {
     if (need > kDecodeScratchBytes)
@@ -661,7 +675,7 @@ int decode_common(const char* fn, const DecodeWrite* w, const void* q, const voi
   }
   if ((int64_t)plan_items * num_kv_heads * ceil_div(num_q_heads / num_kv_heads, 16) > INT32_MAX)
     return fail(ATTN_E_UNSUPPORTED, "%s: plan too large for one launch", fn);
-  if ((int64_t)num_kv_heads * ceil_div(num_q_heads / num_kv_heads, 16) > 65535 || num_seqs > 65535)
+  if ((int64_t)num_kv_heads * ceil_div(num_q_heads / num_kv_heads, 16) > 65535 || num_seqs > kMaxDecodeSeqs)
     return fail(ATTN_E_UNSUPPORTED, "%s: at most 65535 sequences (and kv head slices) per call", fn);
   if (num_seqs == 0) return ok();
   if (use_scratch && need > 0) {
