@@ -421,6 +421,10 @@ def test_decode_noalloc_rejects_before_any_hip_call(lib):
     assert need > (32 << 20)
     assert na(s=4096, mb=2048, mctx=32768, part=1024) == ATTN_E_NOMEM
     assert "32" in mi.attn_last_error() or "scratch" in mi.attn_last_error()
+    # the scratch's fixed counter block holds 16 kv head slices: 17 kv heads
+    # (one slice each) are refused, 16 fit (small partials)
+    assert na(s=4, hq=17, hkv=17, mctx=2048, part=1024) == ATTN_E_NOMEM
+    assert "16" in mi.attn_last_error()
 
 
 def test_paged_masked_rejects(lib):
