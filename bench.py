@@ -11,7 +11,7 @@ timed both ways: RoPE write then decode, and the decode launch that writes
 its own tokens.
 Inputs are synthetic and already resident in HBM when timing starts.
 
-Timing: the headline times --steps steps after --warmup untimed ones,
+Timing: the headline times --steps steps (200) after --warmup untimed ones (20),
 between two device synchronisations (eager launches).  Every component
 figure takes 20 untimed calls and then 100 timed calls in samples of 20
 back-to-back calls between a pair of HIP events on the launching stream,
@@ -37,7 +37,7 @@ also carries the roofline of that dominant launch, the oracle timed on the host 
 and the per-stage figures, plus the contiguous long prefill (T 16384) and the
 uniform-context decode (64 sequences, U[128, 4096]) measured on their own.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
@@ -178,8 +178,11 @@ def main():
     global WARM_CALLS, TIMED_CALLS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # 200 steps (about 35 ms of GPU time): the window's own start and end
+    # (the first launch's latency, the final synchronisation) then cost
+    # under 1 % of a step; over 20 steps they added ~5-9 us to each
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--only", choices=["mixed", "prefill", "decode"], default=None,
