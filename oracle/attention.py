@@ -12,7 +12,7 @@ on purpose: this is the plain definition, not the tiled method.
 Source: the tutorial "Fast Attention Kernels and Operator Fusion"
 (Machine Learning Mastery).  Citations below name its sections.
 
-Readings of points the page leaves open (each is listed again in the design doc):
+Readings of points the page leaves open:
   * d in 1/sqrt(d) is the head dimension.
   * The mask M is additive with entries 0 or -inf; "causal" keeps key j
     visible to query i iff j <= i + (Tk - Tq) (bottom-right alignment, the

@@ -11,7 +11,7 @@ square of the sum (eps under the root, default 1e-6) and scaled elementwise
 by a weight vector; the function returns the normalised rows and the updated
 residual (the sum).
 
-Readings (each listed again in the design doc):
+Readings:
   * The updated residual is stored in the input dtype, so it is the sum
     rounded once to that dtype; the sum itself is taken in float32 before
     that rounding, as the example's elementwise add of two bf16 tensors
