@@ -392,9 +392,10 @@ ATTN_API int32_t attn_decode_paged_partition_for(const int32_t* context_lens, in
  * Kernels).  The two only read the cache (apart from the decode's own new
  * tokens) and write disjoint outputs, so one grid holds the workgroups of
  * both: no second stream, no join, and the CUs are shared in an order the
- * library chooses.  The results are those of attn_prefill_paged (prefill
- * part) and attn_decode_paged, or attn_decode_paged_rope when the decode part
- * carries the new tokens, bit for bit.
+ * library chooses.  The results are those of attn_prefill_paged without a
+ * workspace (prefill part, one pass per query tile) and attn_decode_paged,
+ * or attn_decode_paged_rope when the decode part carries the new tokens,
+ * bit for bit.
  *
  *   prefill   the chunked prefill: the arguments of attn_prefill_paged
  *             (num_seqs 0: no prefill part).  It runs on the default tile in
