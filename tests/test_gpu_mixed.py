@@ -189,3 +189,32 @@ def test_ragged_chunks_and_short_contexts(part, plan):
     check(f64(o_pre), np.concatenate(exp_pre), torch.bfloat16, "prefill vs oracle")
     exp_dec, _ = oracle.decode(to_f64(q_dec), [to_f64(k) for k in ks[R:]], [to_f64(v) for v in vs[R:]])
     check(f64(o_dec), exp_dec, torch.bfloat16, "decode vs oracle")
+
+
+def test_workspace_reused_by_growing_launches():
+    """Two single launches in a row on one decode workspace, the second with
+    more decode sequences than the first (its arrival counters reach past
+    the first's): both equal the separate calls bit for bit, and the
+    counter block is zero after each."""
+    say("case: mixed launches on one workspace, 9 then 60 decode sequences")
+    small = mixed_case(86, num_req=2, chunk=100, cached_max=300, num_dec=9, dec_lo=1000, dec_hi=3000)
+    big = mixed_case(87, num_req=2, chunk=100, cached_max=300, num_dec=60, dec_lo=1, dec_hi=3000)
+    need = 0
+    for case in (small, big):
+        mx = int(case.dec_lengths.max())
+        need = max(need, mi.attn_decode_paged_workspace_size(len(case.dec_lengths), 12, 2, 128, mx, 128))
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    cnt = (65535 * 2 * 4 + 255) // 256 * 256
+    for case in (small, big, small):
+        st = MixedStep(case, assign_blocks, DEV, partition_size=128, scatter=scatter_to_pool)
+        st.write()
+        torch.cuda.synchronize()
+        st.workspace = ws
+        ref_pre, ref_dec = separate(st)
+        assert int((ws[:cnt] != 0).sum().item()) == 0
+        pre, dec = parts(st)
+        o_pre, o_dec = mi.attn_prefill_decode_paged(st.k_cache, st.v_cache, prefill=pre, decode=dec)
+        torch.cuda.synchronize()
+        same(o_pre, ref_pre, "prefill")
+        same(o_dec, ref_dec, f"decode, {len(case.dec_lengths)} sequences")
+        assert int((ws[:cnt] != 0).sum().item()) == 0, "counter block not left zero"
